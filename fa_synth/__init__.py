@@ -1,0 +1,102 @@
+"""Seeded synthetic inputs shared by the HIP path's tests/bench and the oracle.
+
+This module holds no attention arithmetic.  It only draws i.i.d. normal
+values and rounds them to bfloat16 bit patterns, so that the GPU path and the
+CPU oracle see exactly the same input bits.
+
+Recipe (the same for every workload): numpy ``Generator(PCG64(seed))``
+standard normals drawn in float32, multiplied by ``sigma``, rounded to
+bfloat16 with round-to-nearest-even on the bit pattern.  Tensors are
+contiguous ``[B, H, L, D]`` with D innermost.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_from_f32",
+    "normal_bf16_bits",
+    "AttnShape",
+    "WORKLOADS",
+    "make_inputs",
+]
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round-to-nearest-even); return uint16 bits.
+
+    Inputs are finite (normal draws), so no NaN special case is needed.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def normal_bf16_bits(shape, seed: int, sigma: float = 1.0) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        x = x * np.float32(sigma)
+    return bf16_bits_from_f32(x)
+
+
+@dataclass(frozen=True)
+class AttnShape:
+    """One attention problem: sizes, softmax scale, masking and input recipe."""
+
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Lq: int
+    Lk: int
+    D: int
+    causal: bool
+    sigma: float = 1.0
+    seed: int = 0
+    scale: float | None = None  # None -> float32(1/sqrt(D))
+    backward: bool = True
+    q_sigma_mult: float = 1.0  # extra factor on Q only (peaked-softmax variant)
+
+    @property
+    def softmax_scale(self) -> float:
+        s = self.scale if self.scale is not None else 1.0 / math.sqrt(self.D)
+        return float(np.float32(s))
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+
+# The workloads the library is measured and checked on.  Seeds follow
+# seed = 1000*workload + 100*sub-run; tensor t in (q, k, v, dO) adds t.
+WORKLOADS = {
+    "tiny": AttnShape("tiny", 1, 2, 1, 128, 128, 64, True, seed=1000),
+    "train8k": AttnShape("train8k", 1, 32, 8, 8192, 8192, 128, True, seed=2000),
+    "dense4k_d64": AttnShape("dense4k_d64", 2, 16, 16, 4096, 4096, 64, False, sigma=0.5, seed=3000),
+    "dense4k_d96": AttnShape("dense4k_d96", 2, 16, 16, 4096, 4096, 96, False, sigma=0.5, seed=3100),
+    "d256_8192": AttnShape("d256_8192", 1, 16, 2, 8192, 8192, 256, True, seed=4000, scale=1.0 / 16, backward=False),
+    "d256_4064x4096": AttnShape("d256_4064x4096", 1, 16, 2, 4064, 4096, 256, True, seed=4100, scale=1.0 / 16, backward=False),
+    "d256_8200": AttnShape("d256_8200", 1, 16, 2, 8200, 8200, 256, True, seed=4200, scale=1.0 / 16, backward=False),
+    "long23k": AttnShape("long23k", 1, 32, 8, 23040, 23040, 128, True, seed=5000),
+}
+
+
+def make_inputs(shape: AttnShape, with_grad: bool | None = None) -> dict:
+    """Return uint16 bf16 bit arrays q, k, v (and dO when a backward is wanted)."""
+    if with_grad is None:
+        with_grad = shape.backward
+    s = shape.seed
+    out = {
+        "q": normal_bf16_bits((shape.B, shape.Hq, shape.Lq, shape.D), s + 0, shape.sigma * shape.q_sigma_mult),
+        "k": normal_bf16_bits((shape.B, shape.Hkv, shape.Lk, shape.D), s + 1, shape.sigma),
+        "v": normal_bf16_bits((shape.B, shape.Hkv, shape.Lk, shape.D), s + 2, shape.sigma),
+    }
+    if with_grad:
+        out["do"] = normal_bf16_bits((shape.B, shape.Hq, shape.Lq, shape.D), s + 3, shape.sigma)
+    return out

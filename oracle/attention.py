@@ -1,0 +1,198 @@
+"""Plain fp64 attention forward/backward (test infrastructure only).
+
+Every contraction is a numpy float64 matmul; the score matrix S, the
+probabilities P, dP and dS are materialised explicitly for a block of query
+rows, so the code reads as the definition.  See ``oracle/__init__.py`` for
+the page passages each step follows.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_NEG_INF = -np.inf
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns (uint16/int16) to float64."""
+    b = np.ascontiguousarray(bits).view(np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def visible_mask(Lq: int, Lk: int, causal: bool, rows=None) -> np.ndarray:
+    """Boolean [len(rows), Lk]: may query row i attend to key j?
+
+    Causal masking is bottom-right aligned: j <= i + (Lk - Lq)
+    ("Add a fused full-attention path for head_dim 256 on NAX devices",
+    Design, ragged causal inputs).  Without a causal mask every key is seen.
+    """
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    if not causal:
+        return np.ones((rows.shape[0], Lk), dtype=bool)
+    off = Lk - Lq
+    return np.arange(Lk)[None, :] <= (rows[:, None] + off)
+
+
+def _scores(qb: np.ndarray, kh: np.ndarray, scale: float, vis: np.ndarray) -> np.ndarray:
+    """S = scale * Q K^T, with -inf where the mask hides a key."""
+    s = scale * (qb @ kh.T)
+    return np.where(vis, s, _NEG_INF)
+
+
+def _lse(s: np.ndarray) -> np.ndarray:
+    """Natural-log log-sum-exp of each row: m + log(sum exp(s - m))."""
+    m = s.max(axis=1)
+    if not np.all(np.isfinite(m)):
+        raise ValueError("a query row sees no key; its softmax is undefined")
+    return m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+
+
+def _row_blocks(rows: np.ndarray, block: int):
+    for i in range(0, rows.shape[0], block):
+        yield rows[i:i + block]
+
+
+def head_forward(qh, kh, vh, scale, causal, rows=None, block=256):
+    """One head: O and LSE for the given query rows (default: all rows).
+
+    qh [Lq, D], kh/vh [Lk, D] float64.  Returns (o [n, D], lse [n]).
+    """
+    Lq, Lk = qh.shape[0], kh.shape[0]
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    o = np.empty((rows.shape[0], vh.shape[1]))
+    lse = np.empty(rows.shape[0])
+    pos = 0
+    for rb in _row_blocks(rows, block):
+        s = _scores(qh[rb], kh, scale, visible_mask(Lq, Lk, causal, rb))
+        l = _lse(s)
+        p = np.exp(s - l[:, None])          # softmax rows, 0 where masked
+        o[pos:pos + rb.shape[0]] = p @ vh   # O = P V
+        lse[pos:pos + rb.shape[0]] = l
+        pos += rb.shape[0]
+    return o, lse
+
+
+def head_forward_online(qh, kh, vh, scale, causal, block_n=32):
+    """Forward by the tiled online-softmax recurrence (all rows of one head).
+
+    Follows section 3 of "When the Bottleneck Moved": per key block keep a
+    running row maximum m, denominator l and unnormalised accumulator acc;
+    m_new = max(m_old, rowmax(S_blk)), alpha = exp(m_old - m_new),
+    p = exp(S_blk - m_new), l = alpha*l + rowsum(p), acc = alpha*acc + p V_blk;
+    finally O = acc / l and L = m + log(l).  It is an independent route to
+    the same numbers as ``head_forward`` and pins the schedule the GPU uses.
+    """
+    Lq, Lk = qh.shape[0], kh.shape[0]
+    D = vh.shape[1]
+    vis = visible_mask(Lq, Lk, causal)
+    m = np.full(Lq, _NEG_INF)
+    l = np.zeros(Lq)
+    acc = np.zeros((Lq, D))
+    for j0 in range(0, Lk, block_n):
+        j1 = min(Lk, j0 + block_n)
+        s = np.where(vis[:, j0:j1], scale * (qh @ kh[j0:j1].T), _NEG_INF)
+        m_new = np.maximum(m, s.max(axis=1))
+        # rows that have seen nothing yet keep m = -inf; their alpha and p are 0
+        safe = np.where(np.isfinite(m_new), m_new, 0.0)
+        alpha = np.where(np.isfinite(m), np.exp(m - safe), 0.0)
+        p = np.exp(s - safe[:, None])
+        l = alpha * l + p.sum(axis=1)
+        acc = alpha[:, None] * acc + p @ vh[j0:j1]
+        m = m_new
+    return acc / l[:, None], m + np.log(l)
+
+
+def head_backward(qh, kh, vh, doh, scale, causal, rows=None, key_rows=None, block=256):
+    """One query head's backward by explicit recomputation.
+
+    Per block of query rows: S, P from the row's own log-sum-exp, O = P V,
+    delta_i = sum_d dO_id O_id, dP = dO V^T, dS = P * (dP - delta),
+    dQ = scale * dS K, and this head's contributions
+    dK += scale * dS^T Q, dV += P^T dO.
+
+    ``rows`` limits the query rows (dK/dV are then partial sums over those
+    rows only).  ``key_rows`` limits which key rows get dK/dV (dQ is then
+    not computed).  Returns a dict with o, lse, delta, dq (rows) and dk, dv
+    ([len(key_rows) or Lk, D]).
+    """
+    Lq, Lk = qh.shape[0], kh.shape[0]
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    kcols = np.arange(Lk) if key_rows is None else np.asarray(key_rows)
+    full_keys = key_rows is None
+    n = rows.shape[0]
+    D = qh.shape[1]
+    out = {
+        "o": np.empty((n, D)),
+        "lse": np.empty(n),
+        "delta": np.empty(n),
+        "dq": np.empty((n, D)) if full_keys else None,
+        "dk": np.zeros((kcols.shape[0], D)),
+        "dv": np.zeros((kcols.shape[0], D)),
+    }
+    pos = 0
+    for rb in _row_blocks(rows, block):
+        nb = rb.shape[0]
+        qb, dob = qh[rb], doh[rb]
+        s = _scores(qb, kh, scale, visible_mask(Lq, Lk, causal, rb))
+        l = _lse(s)
+        p = np.exp(s - l[:, None])
+        o = p @ vh
+        dl = (dob * o).sum(axis=1)                      # delta = rowsum(dO * O)
+        pk = p[:, kcols]
+        dp = dob @ vh[kcols].T                          # dP = dO V^T
+        ds = pk * (dp - dl[:, None])                    # dS (scale applied below)
+        if full_keys:
+            out["dq"][pos:pos + nb] = scale * (ds @ kh)  # dQ = scale * dS K
+        out["dk"] += scale * (ds.T @ qb)                # dK += scale * dS^T Q
+        out["dv"] += pk.T @ dob                         # dV += P^T dO
+        out["o"][pos:pos + nb] = o
+        out["lse"][pos:pos + nb] = l
+        out["delta"][pos:pos + nb] = dl
+        pos += nb
+    return out
+
+
+def _check(q, k, v):
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, Lk, Dk = k.shape
+    if (Bk, Dk) != (B, D) or v.shape != k.shape or Hq % Hkv:
+        raise ValueError("shape mismatch")
+    return B, Hq, Hkv, Lq, Lk, D, Hq // Hkv
+
+
+def forward(q, k, v, scale, causal, block=256):
+    """Full forward over [B, Hq, Lq, D] / [B, Hkv, Lk, D] float64 arrays."""
+    B, Hq, Hkv, Lq, Lk, D, G = _check(q, k, v)
+    o = np.empty((B, Hq, Lq, D))
+    lse = np.empty((B, Hq, Lq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            o[b, h], lse[b, h] = head_forward(q[b, h], k[b, g], v[b, g], scale, causal, block=block)
+    return o, lse
+
+
+def backward(q, k, v, do, scale, causal, block=256):
+    """Full backward; dK/dV of a key/value head sum over its query heads."""
+    B, Hq, Hkv, Lq, Lk, D, G = _check(q, k, v)
+    res = {
+        "o": np.empty((B, Hq, Lq, D)),
+        "lse": np.empty((B, Hq, Lq)),
+        "delta": np.empty((B, Hq, Lq)),
+        "dq": np.empty((B, Hq, Lq, D)),
+        "dk": np.zeros((B, Hkv, Lk, D)),
+        "dv": np.zeros((B, Hkv, Lk, D)),
+    }
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            r = head_backward(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal, block=block)
+            for name in ("o", "lse", "delta", "dq"):
+                res[name][b, h] = r[name]
+            res["dk"][b, g] += r["dk"]
+            res["dv"][b, g] += r["dv"]
+    return res
+
+
+def delta(o, do):
+    """delta[..., i] = sum_d dO[..., i, d] * O[..., i, d] in float64."""
+    return (np.asarray(do, dtype=np.float64) * np.asarray(o, dtype=np.float64)).sum(axis=-1)
