@@ -1,0 +1,18 @@
+"""Causal grouped-query FlashAttention (forward + fused backward) for AMD MI355X.
+
+The computation lives in hand-written HIP kernels for gfx950 inside
+``libcgqa_fa.so`` (C ABI in ``include/fa.h``); this package only loads that
+library and marshals torch tensors into it.
+"""
+from .binding import (  # noqa: F401
+    FAError,
+    fa_bwd,
+    fa_bwd_delta,
+    fa_fwd,
+    lib_path,
+    load_library,
+    status_str,
+    version,
+)
+
+__all__ = ["FAError", "fa_fwd", "fa_bwd_delta", "fa_bwd", "lib_path", "load_library", "status_str", "version"]

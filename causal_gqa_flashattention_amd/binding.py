@@ -1,0 +1,170 @@
+"""ctypes binding of libcgqa_fa.so (argument marshalling only).
+
+The names match the C ABI in ``include/fa.h``: ``fa_fwd``, ``fa_bwd_delta``,
+``fa_bwd``.  Each takes torch tensors that live on the GPU (torch is used
+for device memory and streams only), checks dtype/contiguity/device, derives
+the sizes from the shapes and calls the library on the current stream.  Every
+step of the computation runs in the HIP kernels; there is no other path.  If
+the library is missing or a call returns a non-zero status, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_NAME, PKG_DIR
+
+FA_OK = 0
+STATUS_NAMES = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_ALIGN", 3: "FA_ERR_SHAPE",
+    4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_GQA", 6: "FA_ERR_CAUSAL_LQ_GT_LK",
+    7: "FA_ERR_SCALE", 8: "FA_ERR_LAUNCH",
+}
+
+_c_int, _c_float, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+
+_SIGS = {
+    "fa_fwd": [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6 + [_c_float, _c_int, _vp],
+    "fa_bwd_delta": [_vp, _vp, _vp] + [_c_int] * 4 + [_vp],
+    "fa_bwd": [_vp] * 10 + [_c_int] * 6 + [_c_float, _c_int, _vp],
+    "fa_status_str": [_c_int],
+    "fa_version": [],
+}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call} failed: {STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+def lib_path() -> str:
+    return os.path.join(PKG_DIR, LIB_NAME)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        p = lib_path()
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(p)
+        for name, argtypes in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = argtypes
+            fn.restype = ctypes.c_char_p if name in ("fa_status_str", "fa_version") else ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return load_library().fa_status_str(status).decode()
+
+
+def version() -> str:
+    return load_library().fa_version().decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != FA_OK:
+        raise FAError(status, call)
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _require(t, name, dtype, ndim):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fa_fwd(q, k, v, o=None, lse=None, *, scale: float, causal: bool, stream=None):
+    """O, LSE = attention(q, k, v).  q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] bf16."""
+    _require(q, "q", torch.bfloat16, 4)
+    _require(k, "k", torch.bfloat16, 4)
+    _require(v, "v", torch.bfloat16, 4)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k/v shapes do not match q")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    _require(o, "o", torch.bfloat16, 4)
+    _require(lse, "lse", torch.float32, 3)
+    if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Lq):
+        raise ValueError("output shapes do not match q")
+    st = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                               B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)),
+                               _stream_ptr(stream))
+    _check(st, "fa_fwd")
+    return o, lse
+
+
+def fa_bwd_delta(o, do, delta=None, *, stream=None):
+    """delta[b,h,i] = sum_d dO*O in fp32.  o, do [B,H,Lq,D] bf16."""
+    _require(o, "o", torch.bfloat16, 4)
+    _require(do, "do", torch.bfloat16, 4)
+    if tuple(do.shape) != tuple(o.shape):
+        raise ValueError("do must have the shape of o")
+    B, H, Lq, D = o.shape
+    if delta is None:
+        delta = torch.empty((B, H, Lq), dtype=torch.float32, device=o.device)
+    _require(delta, "delta", torch.float32, 3)
+    if tuple(delta.shape) != (B, H, Lq):
+        raise ValueError("delta must be [B, H, Lq]")
+    st = load_library().fa_bwd_delta(_ptr(o), _ptr(do), _ptr(delta), B, H, Lq, D, _stream_ptr(stream))
+    _check(st, "fa_bwd_delta")
+    return delta
+
+
+def fa_bwd(q, k, v, o, lse, delta, do, dq=None, dk=None, dv=None, *, scale: float, causal: bool,
+           stream=None):
+    """dQ, dK, dV of attention given the saved lse, the precomputed delta and dO."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (do, "do")):
+        _require(t, n, torch.bfloat16, 4)
+    _require(lse, "lse", torch.float32, 3)
+    _require(delta, "delta", torch.float32, 3)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or tuple(do.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch")
+    if tuple(lse.shape) != (B, Hq, Lq) or tuple(delta.shape) != (B, Hq, Lq):
+        raise ValueError("lse/delta must be [B, Hq, Lq]")
+    if o is not None:
+        _require(o, "o", torch.bfloat16, 4)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, ref, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _require(t, n, torch.bfloat16, 4)
+        if tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"{n} has the wrong shape")
+    st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(delta), _ptr(do),
+                               _ptr(dq), _ptr(dk), _ptr(dv),
+                               B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)),
+                               _stream_ptr(stream))
+    _check(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,51 @@
+// Kernel argument blocks and host-side launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cgqa {
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int B, Hq, Hkv, Lq, Lk, G;
+  int off;          // Lk - Lq: causal diagonal offset
+  int nqt;          // number of query tiles
+  float scale_log2; // scale * log2(e)
+};
+
+struct DeltaArgs {
+  const uint16_t* o;
+  const uint16_t* dO;
+  float* delta;
+  int64_t rows;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* lse;
+  const float* delta;
+  const uint16_t* dO;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int B, Hq, Hkv, Lq, Lk, G;
+  int off;
+  int nqt;          // query tiles (dQ kernel)
+  int nkt;          // key tiles (dK/dV kernel)
+  float scale;
+  float scale_log2;
+};
+
+// Each launcher enqueues on `stream` and returns hipGetLastError().
+hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, hipStream_t stream);
+hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, hipStream_t stream);
+
+}  // namespace cgqa

@@ -1,0 +1,114 @@
+/*
+ * fa.h — C ABI of the causal grouped-query FlashAttention library for
+ * AMD Instinct MI355X (gfx950).  Built as libcgqa_fa.so.
+ *
+ * The three compute calls follow the statement of the problem on the pages:
+ *   - forward: scores S = scale * Q K^T with a causal mask, P = softmax(S),
+ *     O = P V, saving only O and one log-sum-exp per query row
+ *     (page "When the Bottleneck Moved: From Fused Cross-Entropy to
+ *     FlashAttention on MLX", section 3; page "feat(attention): complete
+ *     Flash Attention VJP implementation", Background);
+ *   - delta precompute: delta_i = sum_d dO_id * O_id in fp32, once, outside
+ *     the gradient kernels (VJP page, "Reference implementation" section and
+ *     Architecture / Two-Kernel Design);
+ *   - backward: a dQ kernel over query blocks and a dK/dV kernel over key
+ *     blocks and key/value heads (looping over the query heads of the group,
+ *     then over query blocks), both recomputing P from the saved log-sum-exp,
+ *     no atomics (VJP page, Architecture / Two-Kernel Design).
+ *
+ * Tensor layout (all calls): contiguous [B, H, L, D], D innermost.
+ *   q, o, dO, dq : [B, Hq,  Lq, D]   bfloat16 (passed as raw 16-bit words)
+ *   k, v, dk, dv : [B, Hkv, Lk, D]   bfloat16
+ *   lse, delta   : [B, Hq,  Lq]      float32
+ * The value head dimension equals the query/key head dimension.
+ * Query head h reads key/value head h / (Hq / Hkv) (contiguous groups).
+ *
+ * Causal masking is bottom-right aligned: key j is visible to query i iff
+ * j <= i + (Lk - Lq) (page "Add a fused full-attention path for head_dim 256
+ * on NAX devices", Design, ragged causal inputs).  With causal = 0 every key
+ * is visible.  Masked keys receive exactly zero probability.
+ *
+ * lse is the natural-log log-sum-exp of each query row's scaled scores:
+ * lse_i = log(sum_j exp(scale * q_i . k_j)) over the visible j.
+ *
+ * Ownership and execution: every pointer is a DEVICE pointer owned by the
+ * caller; the library allocates no memory and keeps no per-call state.
+ * Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ * void*; NULL means the null stream) and nothing synchronises.  Every output
+ * element is written exactly once, so outputs need no initialisation.  Calls
+ * are thread-safe.  Results are bitwise reproducible run to run.
+ *
+ * Errors: all arguments are checked on the host before anything is
+ * launched; a failed check returns a non-zero fa_status and launches
+ * nothing.  There is no fallback path.  A kernel launch failure returns
+ * FA_ERR_LAUNCH.  Sizes:
+ *   B, Hq, Hkv, Lq, Lk >= 0 and < 2^31; B*H*L*D element counts must fit
+ *   in int64; Hq % Hkv == 0 (Hkv >= 1 when Hq >= 1);
+ *   D in {64, 96, 128, 256} for fa_fwd and fa_bwd_delta,
+ *   D in {64, 96, 128} for fa_bwd;
+ *   causal requires Lq <= Lk (otherwise the first rows see no key);
+ *   Lk == 0 with Lq > 0 is rejected (softmax over no keys).
+ * Empty problems (B == 0, Hq == 0, or Lq == 0) are valid no-ops, except that
+ * fa_bwd with Lq == 0 and Lk > 0 writes zeros to dk and dv.
+ * Pointers to non-empty tensors must be non-NULL and 16-byte aligned.
+ */
+#ifndef CGQA_FA_H
+#define CGQA_FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,              /* a required pointer is NULL                 */
+  FA_ERR_ALIGN = 2,             /* a pointer is not 16-byte aligned           */
+  FA_ERR_SHAPE = 3,             /* negative size, Lk == 0 < Lq, or overflow   */
+  FA_ERR_HEAD_DIM = 4,          /* D not supported by this call               */
+  FA_ERR_GQA = 5,               /* Hq not a multiple of Hkv                   */
+  FA_ERR_CAUSAL_LQ_GT_LK = 6,   /* causal with Lq > Lk                        */
+  FA_ERR_SCALE = 7,             /* scale not finite or not positive           */
+  FA_ERR_LAUNCH = 8             /* the HIP runtime refused a kernel launch    */
+} fa_status;
+
+/*
+ * Forward attention.  Writes o [B,Hq,Lq,D] (bf16) and lse [B,Hq,Lq] (fp32,
+ * natural log).  `scale` multiplies q.k before the softmax (usually
+ * 1/sqrt(D)); it must be finite and > 0.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                 int causal, void* stream);
+
+/*
+ * Delta precompute for the backward: delta[b,h,i] = sum_d f32(dO[b,h,i,d]) *
+ * f32(O[b,h,i,d]), accumulated in fp32.  `H` is the number of query heads.
+ */
+fa_status fa_bwd_delta(const void* o, const void* dO, float* delta,
+                       int B, int H, int Lq, int D, void* stream);
+
+/*
+ * Backward attention.  Given q, k, v, the saved lse (from fa_fwd) and delta
+ * (from fa_bwd_delta), and the output gradient dO, writes
+ *   dq [B,Hq,Lq,D], dk and dv [B,Hkv,Lk,D] (bf16).
+ * dk/dv of a key/value head sum the contributions of all Hq/Hkv query heads
+ * of its group.  `o` is accepted for the problem's signature; the kernels
+ * read O only through delta and `o` may be NULL.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const float* delta, const void* dO,
+                 void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                 int causal, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_str(fa_status s);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CGQA_FA_H */

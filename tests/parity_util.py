@@ -1,0 +1,75 @@
+"""Helpers shared by the GPU parity tests: move seeded bf16 bits to the GPU,
+run the library's three calls, and compare against the fp64 oracle with the
+stated tolerances.
+
+Tolerances (per output tensor):
+  LSE            max |gpu - ref| <= 1e-3 (absolute, natural-log units)
+  O              max |gpu - ref| <= 1e-2 * max |ref|
+  dQ, dK, dV     max |gpu - ref| <= 2e-2 * max |ref|
+The median elementwise relative error (over |ref| >= 1e-3 * max |ref|) and the
+relative L2 error are reported alongside.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL = {"lse": ("abs", 1e-3), "o": ("rel_max", 1e-2), "dq": ("rel_max", 2e-2),
+       "dk": ("rel_max", 2e-2), "dv": ("rel_max", 2e-2), "delta": ("rel_max", 1e-2)}
+
+
+def to_gpu(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run_library(q, k, v, do, scale, causal, backward=True):
+    """Run fa_fwd (+ fa_bwd_delta + fa_bwd) on GPU tensors; return GPU tensors."""
+    import causal_gqa_flashattention_amd as fa
+    o, lse = fa.fa_fwd(q, k, v, scale=scale, causal=causal)
+    out = {"o": o, "lse": lse}
+    if backward:
+        delta = fa.fa_bwd_delta(o, do)
+        dq, dk, dv = fa.fa_bwd(q, k, v, o, lse, delta, do, scale=scale, causal=causal)
+        out.update(delta=delta, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return out
+
+
+def stats(got: np.ndarray, ref: np.ndarray) -> dict:
+    err = np.abs(got - ref)
+    amax = float(np.abs(ref).max()) if ref.size else 0.0
+    sel = (np.abs(ref) >= 1e-3 * amax) & (np.abs(ref) > 0)
+    med = float(np.median(err[sel] / np.abs(ref[sel]))) if sel.any() else 0.0
+    l2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    return {"max_abs": float(err.max()) if err.size else 0.0, "max_ref": amax, "median_rel": med, "rel_l2": l2}
+
+
+def check(name: str, got: np.ndarray, ref: np.ndarray, label: str = "", atol: float = 0.0) -> dict:
+    """Assert the tolerance for `name`; `atol` is an absolute floor used only
+    where the exact result is identically zero (degenerate cases)."""
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{label} {name}: non-finite values"
+    st = stats(got, ref)
+    kind, tol = TOL[name]
+    bound = tol if kind == "abs" else max(tol * st["max_ref"], atol)
+    print(f"[parity] {label} {name}: max_abs={st['max_abs']:.3e} bound={bound:.3e} "
+          f"median_rel={st['median_rel']:.2e} rel_l2={st['rel_l2']:.2e}", flush=True)
+    assert st["max_abs"] <= bound, f"{label} {name}: {st['max_abs']:.4e} > {bound:.4e}"
+    return st
+
+
+def oracle_full(bits: dict, scale: float, causal: bool, backward=True) -> dict:
+    q = oracle.bf16_bits_to_f64(bits["q"])
+    k = oracle.bf16_bits_to_f64(bits["k"])
+    v = oracle.bf16_bits_to_f64(bits["v"])
+    if not backward:
+        o, lse = oracle.forward(q, k, v, scale, causal)
+        return {"o": o, "lse": lse}
+    do = oracle.bf16_bits_to_f64(bits["do"])
+    return oracle.backward(q, k, v, do, scale, causal)

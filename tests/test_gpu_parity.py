@@ -1,0 +1,211 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded
+bf16 inputs, element by element, at sizes the oracle finishes in seconds
+(several tiles, ragged tails, bottom-right causal rectangles, every head
+dimension), plus structural checks: bitwise run-to-run repeatability, guard
+bands around every output, empty problems and typed errors.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from fa_synth import normal_bf16_bits
+from parity_util import check, oracle_full, run_library, to_f64, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def make_bits(B, Hq, Hkv, Lq, Lk, D, seed, sigma=1.0, q_mult=1.0):
+    return {
+        "q": normal_bf16_bits((B, Hq, Lq, D), seed + 0, sigma * q_mult),
+        "k": normal_bf16_bits((B, Hkv, Lk, D), seed + 1, sigma),
+        "v": normal_bf16_bits((B, Hkv, Lk, D), seed + 2, sigma),
+        "do": normal_bf16_bits((B, Hq, Lq, D), seed + 3, sigma),
+    }
+
+
+def run_case(B, Hq, Hkv, Lq, Lk, D, causal, seed, sigma=1.0, q_mult=1.0, backward=True, atol=None):
+    label = f"B{B} Hq{Hq} Hkv{Hkv} Lq{Lq} Lk{Lk} D{D} causal={causal} seed={seed}"
+    print(f"[case] {label}", flush=True)
+    bits = make_bits(B, Hq, Hkv, Lq, Lk, D, seed, sigma, q_mult)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    g = {n: to_gpu(b) for n, b in bits.items()}
+    out = run_library(g["q"], g["k"], g["v"], g["do"], scale, causal, backward=backward)
+    ref = oracle_full(bits, scale, causal, backward=backward)
+    names = ["o", "lse"] + (["dq", "dk", "dv"] if backward else [])
+    for n in names:
+        check(n, to_f64(out[n]), ref[n], label, atol=(atol or {}).get(n, 0.0))
+    if backward:
+        # stage check: the delta kernel against the oracle's delta of the
+        # GPU's own O (the only place a GPU value feeds a comparison)
+        import oracle
+        d_ref = oracle.delta(to_f64(out["o"]), oracle.bf16_bits_to_f64(bits["do"]))
+        got = to_f64(out["delta"])
+        assert np.abs(got - d_ref).max() <= 1e-5 * max(1.0, np.abs(d_ref).max()), label
+    return out
+
+
+# --------------------------------------------------------------- tiny workload
+
+def test_tiny_workload_full():
+    # B=1, Hq=2, Hkv=1, Lq=Lk=128, D=64, causal; seeds of the tiny workload
+    from fa_synth import WORKLOADS, make_inputs
+    w = WORKLOADS["tiny"]
+    bits = make_inputs(w)
+    g = {n: to_gpu(b) for n, b in bits.items()}
+    out = run_library(g["q"], g["k"], g["v"], g["do"], w.softmax_scale, w.causal)
+    ref = oracle_full(bits, w.softmax_scale, w.causal)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        check(n, to_f64(out[n]), ref[n], "tiny")
+
+
+# ------------------------------------------------ small grid (lengths 61/64/257)
+
+@pytest.mark.parametrize("L", [61, 64, 257])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B", [1, 2])
+@pytest.mark.parametrize("heads", [(2, 2), (4, 1)])
+def test_small_grid(L, D, B, heads):
+    run_case(B, heads[0], heads[1], L, L, D, True, seed=7000 + L + D + B)
+
+
+def test_gqa_32_8_at_64():
+    run_case(1, 32, 8, 64, 64, 128, True, seed=7100)
+
+
+# ----------------------------------------------- several tiles and ragged tails
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_multi_tile_ragged(D, causal):
+    run_case(2, 4, 2, 1000, 1000, D, causal, seed=7200 + D + int(causal))
+
+
+@pytest.mark.parametrize("Lq,Lk", [(300, 1000), (1, 777), (129, 130), (1031, 2049)])
+def test_bottom_right_causal_rectangles(Lq, Lk):
+    run_case(1, 4, 1, Lq, Lk, 128, True, seed=7300 + Lq)
+
+
+@pytest.mark.parametrize("Lq,Lk", [(1000, 300), (64, 200)])
+def test_dense_rectangles(Lq, Lk):
+    run_case(1, 2, 1, Lq, Lk, 64, False, seed=7400 + Lq, sigma=0.5)
+
+
+def test_single_key_gradient_is_zero():
+    # With one key, P = 1 and dS = dP - delta = 0 exactly, so dQ = 0 and
+    # dK = 0.  The GPU's dP (MFMA, fp32) and delta (fp32 dot product of the
+    # bf16-rounded O, which here equals V exactly) differ only by fp32
+    # summation order: |dP - delta| <= 2 * D * 2^-24 * sum|dO||V| ~ 1e-5,
+    # times scale * |K| <= 4 gives the 1e-4 absolute floor.
+    run_case(1, 2, 1, 5, 1, 64, False, seed=7405, sigma=0.5, atol={"dq": 1e-4, "dk": 1e-4})
+
+
+def test_single_row_single_key():
+    run_case(1, 1, 1, 1, 1, 64, True, seed=7500)
+
+
+def test_peaked_softmax():
+    # queries 4x larger: sharper softmax rows than i.i.d. N(0, 1)
+    run_case(1, 4, 2, 513, 513, 128, True, seed=7600, q_mult=4.0)
+
+
+# ------------------------------------------------------------ head dim 256 fwd
+
+@pytest.mark.parametrize("Lq,Lk,causal", [(300, 300, True), (200, 520, True), (257, 100, False)])
+def test_head_dim_256_forward(Lq, Lk, causal):
+    run_case(1, 4, 2, Lq, Lk, 256, causal, seed=7700 + Lq, backward=False)
+
+
+# ---------------------------------------------------------------- structure
+
+def test_bitwise_repeatable():
+    bits = make_bits(1, 8, 2, 700, 700, 128, seed=7800)
+    g = {n: to_gpu(b) for n, b in bits.items()}
+    scale = float(np.float32(1 / math.sqrt(128)))
+    a = run_library(g["q"], g["k"], g["v"], g["do"], scale, True)
+    b = run_library(g["q"], g["k"], g["v"], g["do"], scale, True)
+    for n in ("o", "lse", "delta", "dq", "dk", "dv"):
+        assert torch.equal(a[n].view(torch.int16) if a[n].dtype == torch.bfloat16 else a[n],
+                           b[n].view(torch.int16) if b[n].dtype == torch.bfloat16 else b[n]), n
+
+
+def _guarded(shape, dtype, fill):
+    """A tensor living inside a larger buffer whose guard bands hold `fill`."""
+    n = int(np.prod(shape))
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), fill, dtype=dtype, device="cuda")
+    return buf, buf[pad:pad + n].view(shape), pad
+
+
+@pytest.mark.parametrize("D,backward", [(64, True), (128, True), (96, True), (256, False)])
+def test_guard_bands_and_nan_poison(D, backward):
+    """Inputs sit between NaN guard bands (an out-of-bounds read would make
+    NaN appear in the outputs); outputs sit between sentinel guard bands that
+    must be untouched, and start as NaN so any unwritten element shows."""
+    import causal_gqa_flashattention_amd as fa
+    B, Hq, Hkv, Lq, Lk = 1, 4, 2, 203, 331
+    bits = make_bits(B, Hq, Hkv, Lq, Lk, D, seed=7900 + D)
+    nan = float("nan")
+    ins = {}
+    for n, b in bits.items():
+        buf, t, _ = _guarded(b.shape, torch.bfloat16, nan)
+        t.copy_(to_gpu(b))
+        ins[n] = (buf, t)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    sentinel = 12288.0  # exactly representable in bf16 and fp32
+    o_buf, o, pad = _guarded((B, Hq, Lq, D), torch.bfloat16, sentinel)
+    l_buf, lse, _ = _guarded((B, Hq, Lq), torch.float32, sentinel)
+    o.fill_(nan)
+    lse.fill_(nan)
+    fa.fa_fwd(ins["q"][1], ins["k"][1], ins["v"][1], o, lse, scale=scale, causal=True)
+    outs = [(o_buf, o), (l_buf, lse)]
+    if backward:
+        d_buf, delta, _ = _guarded((B, Hq, Lq), torch.float32, sentinel)
+        delta.fill_(nan)
+        fa.fa_bwd_delta(o, ins["do"][1], delta)
+        grads = {}
+        for n, shp in (("dq", (B, Hq, Lq, D)), ("dk", (B, Hkv, Lk, D)), ("dv", (B, Hkv, Lk, D))):
+            gb, gt, _ = _guarded(shp, torch.bfloat16, sentinel)
+            gt.fill_(nan)
+            grads[n] = (gb, gt)
+        fa.fa_bwd(ins["q"][1], ins["k"][1], ins["v"][1], o, lse, delta, ins["do"][1],
+                  grads["dq"][1], grads["dk"][1], grads["dv"][1], scale=scale, causal=True)
+        outs += [(d_buf, delta)] + list(grads.values())
+    torch.cuda.synchronize()
+    for buf, t in outs:
+        assert torch.isfinite(t.float()).all(), "unwritten or poisoned output element"
+        guard = torch.cat([buf[:pad], buf[pad + t.numel():]]).float()
+        assert (guard == sentinel).all(), "write outside the output tensor"
+
+
+def test_empty_problems():
+    import causal_gqa_flashattention_amd as fa
+    dev = "cuda"
+    q = torch.empty((0, 4, 16, 64), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((0, 2, 16, 64), dtype=torch.bfloat16, device=dev)
+    o, lse = fa.fa_fwd(q, k, k, scale=0.125, causal=True)
+    assert o.numel() == 0
+    # no query rows but some keys: dK and dV must come back exactly zero
+    q = torch.empty((1, 4, 0, 64), dtype=torch.bfloat16, device=dev)
+    k = to_gpu(normal_bf16_bits((1, 2, 77, 64), 8000))
+    lse = torch.empty((1, 4, 0), dtype=torch.float32, device=dev)
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(k, float("nan"))
+    fa.fa_bwd(q, k, k, None, lse, lse, q, torch.empty_like(q), dk, dv, scale=0.125, causal=True)
+    torch.cuda.synchronize()
+    assert (dk.float() == 0).all() and (dv.float() == 0).all()
+
+
+def test_typed_errors_on_device():
+    import causal_gqa_flashattention_amd as fa
+    q = to_gpu(normal_bf16_bits((1, 2, 8, 256), 1))
+    o, lse = fa.fa_fwd(q, q[:, :1].contiguous(), q[:, :1].contiguous(), scale=0.0625, causal=True)
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_bwd(q, q[:, :1].contiguous(), q[:, :1].contiguous(), o, lse, lse, q, scale=0.0625, causal=True)
+    assert e.value.status == 4  # FA_ERR_HEAD_DIM: the backward stops at D = 128
+    q = to_gpu(normal_bf16_bits((1, 2, 9, 64), 1))
+    k = to_gpu(normal_bf16_bits((1, 1, 8, 64), 2))
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_fwd(q, k, k, scale=0.125, causal=True)
+    assert e.value.status == 6  # causal needs Lq <= Lk
