@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal GQA attention hot path on one MI355X.
+
+One step = fa_fwd + fa_bwd_delta + fa_bwd (dQ kernel, then dK/dV kernel) over
+one batch of resident synthetic bf16 inputs of the 8192-token training shape
+(B=1, 32 query heads, 8 key/value heads, head dim 128, causal).  Prints one
+JSON line with the throughput under the FLOP model of the pages (forward
+4*B*Hq*Lq*Lk*D, backward 2.5x that, both halved for causal), the roofline
+position of the dominant kernel (timed with HIP events on the stream the
+kernels run on), peak device memory, and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd TFLOP/s, causal GQA bf16 attention D=128 L=8192; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU * 4096 FLOP/clk * 2.4 GHz
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+# ------------------------------------------------------------ FLOP accounting
+
+def model_flops(B, Hq, Lq, Lk, D, causal, backward=True):
+    """The pages' model: forward 4*B*Hq*Lq*Lk*D, backward 2.5x the forward,
+    both halved under a causal mask (VJP page, Background)."""
+    fwd = 4.0 * B * Hq * Lq * Lk * D
+    if causal:
+        fwd /= 2.0
+    return fwd * (3.5 if backward else 1.0), fwd
+
+
+def visible_pairs(Lq, Lk, causal):
+    """Exact number of (query, key) pairs inside the mask of one head."""
+    if not causal:
+        return Lq * Lk
+    # causal needs Lq <= Lk; row i sees keys 0 .. i + (Lk - Lq), never past Lk - 1
+    off = Lk - Lq
+    return Lq * (off + 1) + Lq * (Lq - 1) // 2
+
+
+def unfused_score_bytes(H, L, bytes_per=2):
+    """Bytes of one materialised [H, L, L] score matrix (the unfused backward's
+    dominant buffer; VJP page, Memory table, "Attn Matrix Size")."""
+    return H * L * L * bytes_per
+
+
+# per-kernel algorithmic work: MFMA FLOP per visible pair (S, P V | S, dP, dQ |
+# S, dP, dV, dK) and HBM bytes for the delta pass
+KERNEL_FLOP_PER_PAIR = {"fwd": 4, "dq": 6, "dkv": 8}
+
+
+def kernel_work(w, pairs):
+    bh = w.B * w.Hq
+    work = {k: c * w.D * pairs * bh for k, c in KERNEL_FLOP_PER_PAIR.items()}
+    work["delta"] = 2 * bh * w.Lq * w.D * 2 + bh * w.Lq * 4  # read O, dO; write delta
+    return work
+
+
+# ------------------------------------------------------------ traffic record
+
+def source_digest():
+    import glob
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "causal_gqa_flashattention_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernels changed after the counters were taken."""
+    p = os.path.join(PROFILE_DIR, f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes")
+
+
+# ------------------------------------------------------------ CPU oracle leg
+
+def cpu_baseline(w, bits, budget_s=30.0):
+    """Time the fp64 oracle on one whole GQA group (its query heads, all rows,
+    forward + backward) of the same inputs; report model TFLOP/s of that
+    sample.  The group is 1/(B*Hkv) of the workload's model FLOPs."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    G = w.Hq // w.Hkv
+    k = oracle.bf16_bits_to_f64(bits["k"][0, 0])
+    v = oracle.bf16_bits_to_f64(bits["v"][0, 0])
+    t0 = time.perf_counter()
+    heads_done = 0
+    for h in range(G):
+        q = oracle.bf16_bits_to_f64(bits["q"][0, h])
+        do = oracle.bf16_bits_to_f64(bits["do"][0, h])
+        oracle.head_backward(q, k, v, do, w.softmax_scale, w.causal)
+        heads_done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    total, _ = model_flops(1, heads_done, w.Lq, w.Lk, w.D, w.causal)
+    del np
+    return {"value": total / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads_done} query heads of key/value head 0 (one GQA group), all {w.Lq} rows, "
+                      f"fp64 forward+backward, {dt:.2f} s"}
+
+
+# ------------------------------------------------------------ main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="one copy kernel of known size plus one step, for counter runs")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by GQA group with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import causal_gqa_flashattention_amd as fa
+    from fa_synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fa.load_library()
+    bits = make_inputs(w, with_grad=True)
+    g = {n: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for n, b in bits.items()}
+    q, k, v, do = g["q"], g["k"], g["v"], g["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    sc, causal = w.softmax_scale, w.causal
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(q, k, v, o, lse, scale=sc, causal=causal, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fa_bwd_delta(o, do, delta, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fa.fa_bwd_dq(q, k, v, lse, delta, do, dq, scale=sc, causal=causal, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        fa.fa_bwd_dkv(q, k, v, lse, delta, do, dk, dv, scale=sc, causal=causal, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    if args.profile_pass:
+        # a plain copy of known size (calibrates the byte counters), then one step
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "copy_bytes": src.numel(), "workload": w.name}))
+        return 0
+
+    resident = torch.cuda.memory_allocated()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    peak = torch.cuda.max_memory_allocated()
+
+    names = ["fwd", "delta", "dq", "dkv"]
+    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    ms_step = wall * 1e3 / args.steps
+    total_flops, fwd_flops = model_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal)
+    value = total_flops / (ms_step * 1e-3) / 1e12
+
+    pairs = visible_pairs(w.Lq, w.Lk, w.causal)
+    work = kernel_work(w, pairs)
+    kernels = {}
+    for n in names:
+        if n == "delta":
+            kernels[n] = {"ms": per[n], "GB/s": work[n] / (per[n] * 1e-3) / 1e9}
+        else:
+            kernels[n] = {"ms": per[n], "TFLOP/s": work[n] / (per[n] * 1e-3) / 1e12}
+    dom = max(("fwd", "dq", "dkv"), key=lambda n: per[n])
+    achieved = work[dom] / (per[dom] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic(dom, w.name),
+                "flop_per_launch": work[dom], "avg_launch_ms": round(per[dom], 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: causal GQA fwd+bwd, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
+                               f"Lq={w.Lq} Lk={w.Lk} D={w.D}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Lq": w.Lq, "Lk": w.Lk, "D": w.D, "causal": w.causal},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "model_tflop_per_step": round(total_flops / 1e12, 4),
+        "kernels": {n: {kk: round(vv, 4) for kk, vv in d.items()} for n, d in kernels.items()},
+        "roofline": roofline,
+        "memory": {"resident_bytes": int(resident), "peak_bytes": int(peak),
+                   "extra_over_resident": int(peak - resident),
+                   "unfused_fp32_score_bytes": unfused_score_bytes(w.B * w.Hq, w.Lq, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, bits)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -8,6 +8,8 @@ from .binding import (  # noqa: F401
     FAError,
     fa_bwd,
     fa_bwd_delta,
+    fa_bwd_dkv,
+    fa_bwd_dq,
     fa_fwd,
     lib_path,
     load_library,
@@ -15,4 +17,4 @@ from .binding import (  # noqa: F401
     version,
 )
 
-__all__ = ["FAError", "fa_fwd", "fa_bwd_delta", "fa_bwd", "lib_path", "load_library", "status_str", "version"]
+__all__ = ["FAError", "fa_fwd", "fa_bwd_delta", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkv", "lib_path", "load_library", "status_str", "version"]

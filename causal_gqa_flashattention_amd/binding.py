@@ -30,6 +30,8 @@ _SIGS = {
     "fa_fwd": [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6 + [_c_float, _c_int, _vp],
     "fa_bwd_delta": [_vp, _vp, _vp] + [_c_int] * 4 + [_vp],
     "fa_bwd": [_vp] * 10 + [_c_int] * 6 + [_c_float, _c_int, _vp],
+    "fa_bwd_dq": [_vp] * 7 + [_c_int] * 6 + [_c_float, _c_int, _vp],
+    "fa_bwd_dkv": [_vp] * 8 + [_c_int] * 6 + [_c_float, _c_int, _vp],
     "fa_status_str": [_c_int],
     "fa_version": [],
 }
@@ -168,3 +170,47 @@ def fa_bwd(q, k, v, o, lse, delta, do, dq=None, dk=None, dv=None, *, scale: floa
                                _stream_ptr(stream))
     _check(st, "fa_bwd")
     return dq, dk, dv
+
+
+def _bwd_half(which, q, k, v, lse, delta, do, outs, scale, causal, stream):
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (do, "do")):
+        _require(t, n, torch.bfloat16, 4)
+    _require(lse, "lse", torch.float32, 3)
+    _require(delta, "delta", torch.float32, 3)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or tuple(do.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch")
+    if tuple(lse.shape) != (B, Hq, Lq) or tuple(delta.shape) != (B, Hq, Lq):
+        raise ValueError("lse/delta must be [B, Hq, Lq]")
+    lib = load_library()
+    tail = (B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)), _stream_ptr(stream))
+    if which == "dq":
+        (dq,) = outs
+        _require(dq, "dq", torch.bfloat16, 4)
+        if tuple(dq.shape) != tuple(q.shape):
+            raise ValueError("dq has the wrong shape")
+        st = lib.fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(delta), _ptr(do), _ptr(dq), *tail)
+    else:
+        dk, dv = outs
+        for t, n in ((dk, "dk"), (dv, "dv")):
+            _require(t, n, torch.bfloat16, 4)
+            if tuple(t.shape) != tuple(k.shape):
+                raise ValueError(f"{n} has the wrong shape")
+        st = lib.fa_bwd_dkv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(delta), _ptr(do),
+                            _ptr(dk), _ptr(dv), *tail)
+    _check(st, "fa_bwd_" + which)
+    return outs
+
+
+def fa_bwd_dq(q, k, v, lse, delta, do, dq=None, *, scale: float, causal: bool, stream=None):
+    """dQ only (the query-block kernel of fa_bwd)."""
+    dq = torch.empty_like(q) if dq is None else dq
+    return _bwd_half("dq", q, k, v, lse, delta, do, (dq,), scale, causal, stream)[0]
+
+
+def fa_bwd_dkv(q, k, v, lse, delta, do, dk=None, dv=None, *, scale: float, causal: bool, stream=None):
+    """dK and dV only (the key-block kernel of fa_bwd)."""
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    return _bwd_half("dkv", q, k, v, lse, delta, do, (dk, dv), scale, causal, stream)

@@ -131,25 +131,33 @@ fa_status fa_bwd_delta(const void* o, const void* dO, float* delta,
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
-                 const float* lse, const float* delta, const void* dO,
-                 void* dq, void* dk, void* dv,
-                 int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
-                 int causal, void* stream) {
-  (void)o;  // O enters the backward only through delta
+}  // extern "C"
+
+namespace {
+
+// Shared body of fa_bwd / fa_bwd_dq / fa_bwd_dkv.  which: 1 = dQ, 2 = dK/dV.
+fa_status bwd_common(const void* q, const void* k, const void* v, const float* lse,
+                     const float* delta, const void* dO, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                     int which, void* stream) {
   if (!bwd_head_dim_ok(D)) return FA_ERR_HEAD_DIM;
   FA_TRY(check_sizes(B, Hq, Hkv, Lq, Lk, D, causal != 0));
   FA_TRY(check_scale(scale));
   if (B == 0 || Hq == 0) return FA_OK;
-  if (Lq == 0 && Lk == 0) return FA_OK;
-  // dk/dv are written whenever keys exist (zeros when there is no query);
-  // everything else only when there are query rows.
+  // dk/dv are written whenever keys exist (zeros when there is no query row);
+  // dq only when there are query rows.
+  if (Lq == 0) which &= 2;
+  if (Lk == 0) which &= 1;
+  if (which == 0) return FA_OK;
   FA_TRY(check_ptr(k));
   FA_TRY(check_ptr(v));
-  FA_TRY(check_ptr(dk));
-  FA_TRY(check_ptr(dv));
   if (Lq > 0)
-    for (const void* p : {q, (const void*)lse, (const void*)delta, dO, (const void*)dq}) FA_TRY(check_ptr(p));
+    for (const void* p : {q, (const void*)lse, (const void*)delta, dO}) FA_TRY(check_ptr(p));
+  if (which & 1) FA_TRY(check_ptr(dq));
+  if (which & 2) {
+    FA_TRY(check_ptr(dk));
+    FA_TRY(check_ptr(dv));
+  }
 
   cgqa::BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -167,8 +175,39 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
   a.nkt = (Lk + kDkvBN - 1) / kDkvBN;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  const hipError_t e = cgqa::launch_bwd(a, D, causal != 0, static_cast<hipStream_t>(stream));
+  const hipError_t e = cgqa::launch_bwd(a, D, causal != 0, which, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const float* delta, const void* dO,
+                 void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                 int causal, void* stream) {
+  (void)o;  // O enters the backward only through delta
+  return bwd_common(q, k, v, lse, delta, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal, 3,
+                    stream);
+}
+
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
+                    const float* lse, const float* delta, const void* dO, void* dq,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                    int causal, void* stream) {
+  return bwd_common(q, k, v, lse, delta, dO, dq, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, D, scale,
+                    causal, 1, stream);
+}
+
+fa_status fa_bwd_dkv(const void* q, const void* k, const void* v,
+                     const float* lse, const float* delta, const void* dO,
+                     void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                     int causal, void* stream) {
+  return bwd_common(q, k, v, lse, delta, dO, nullptr, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale,
+                    causal, 2, stream);
 }
 
 }  // extern "C"

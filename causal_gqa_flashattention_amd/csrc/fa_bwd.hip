@@ -412,9 +412,9 @@ hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t stream) {
 }
 
 template <int D, int BN_Q, int BM_KV>
-static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, hipStream_t stream) {
-  const int ndq = a.B * a.Hq * a.nqt;
-  const int ndkv = a.B * a.Hkv * a.nkt;
+static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int which, hipStream_t stream) {
+  const int ndq = (which & 1) ? a.B * a.Hq * a.nqt : 0;
+  const int ndkv = (which & 2) ? a.B * a.Hkv * a.nkt : 0;
   if (causal) {
     if (ndq > 0) hipLaunchKernelGGL((fa_dq_kernel<D, BN_Q, true>), dim3(ndq), dim3(256), 0, stream, a);
     if (ndkv > 0) hipLaunchKernelGGL((fa_dkv_kernel<D, BM_KV, true>), dim3(ndkv), dim3(256), 0, stream, a);
@@ -425,11 +425,11 @@ static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, hipStream_t stream
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, hipStream_t stream) {
+hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, hipStream_t stream) {
   switch (D) {
-    case 64: return launch_bwd_d<64, 64, 64>(a, causal, stream);
-    case 96: return launch_bwd_d<96, 64, 64>(a, causal, stream);
-    case 128: return launch_bwd_d<128, 64, 64>(a, causal, stream);
+    case 64: return launch_bwd_d<64, 64, 64>(a, causal, which, stream);
+    case 96: return launch_bwd_d<96, 64, 64>(a, causal, which, stream);
+    case 128: return launch_bwd_d<128, 64, 64>(a, causal, which, stream);
     default: return hipErrorInvalidValue;
   }
 }

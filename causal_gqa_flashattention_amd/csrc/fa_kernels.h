@@ -46,6 +46,7 @@ struct BwdArgs {
 // Each launcher enqueues on `stream` and returns hipGetLastError().
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, hipStream_t stream);
+// which: 1 = dQ kernel, 2 = dK/dV kernel, 3 = both (dQ first).
+hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, hipStream_t stream);
 
 }  // namespace cgqa

@@ -101,6 +101,23 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                  int causal, void* stream);
 
+/*
+ * The two halves of fa_bwd, for callers that run them on separate streams
+ * (the two gradient kernels are independent: the VJP page runs them
+ * concurrently, Architecture / Two-Kernel Design).  fa_bwd_dq writes dq only;
+ * fa_bwd_dkv writes dk and dv only.  Arguments, checks and errors are those
+ * of fa_bwd; pointers a half does not use may be NULL.
+ */
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
+                    const float* lse, const float* delta, const void* dO, void* dq,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                    int causal, void* stream);
+fa_status fa_bwd_dkv(const void* q, const void* k, const void* v,
+                     const float* lse, const float* delta, const void* dO,
+                     void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                     int causal, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_str(fa_status s);
 

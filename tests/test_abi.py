@@ -1,0 +1,84 @@
+"""The C-ABI library: it loads without a GPU, exports every symbol the
+header declares, and its host-side validation returns the documented typed
+errors before touching the device (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import causal_gqa_flashattention_amd as fa
+    if not os.path.exists(fa.lib_path()):
+        pytest.skip("library not built (run __graft_entry__.build())")
+    return fa.load_library()
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_bwd_delta", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkv", "fa_status_str", "fa_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert lib.fa_status_str(s)
+    assert b"Lq <= Lk" in lib.fa_status_str(6)
+
+
+P = 4096  # a fake, 16-byte aligned pointer value: validation never dereferences
+
+
+@pytest.mark.parametrize("args,status", [
+    # q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal
+    ((P, P, P, P, P, 1, 2, 1, 8, 8, 48, 0.1, 1), 4),     # head dim
+    ((P, P, P, P, P, 1, 3, 2, 8, 8, 64, 0.1, 1), 5),     # Hq % Hkv
+    ((P, P, P, P, P, 1, 2, 0, 8, 8, 64, 0.1, 1), 5),     # Hkv == 0
+    ((P, P, P, P, P, 1, 2, 1, 9, 8, 64, 0.1, 1), 6),     # causal Lq > Lk
+    ((P, P, P, P, P, 1, 2, 1, 8, 0, 64, 0.1, 0), 3),     # no keys
+    ((P, P, P, P, P, -1, 2, 1, 8, 8, 64, 0.1, 0), 3),    # negative size
+    ((P, P, P, P, P, 1, 2, 1, 8, 8, 64, float("nan"), 0), 7),
+    ((P, P, P, P, P, 1, 2, 1, 8, 8, 64, -1.0, 0), 7),
+    ((0, P, P, P, P, 1, 2, 1, 8, 8, 64, 0.1, 1), 1),     # null q
+    ((P, P, P + 2, P, P, 1, 2, 1, 8, 8, 64, 0.1, 1), 2), # misaligned v
+    ((P, P, P, P, P, 65536, 65536, 1, 65536, 65536, 256, 0.1, 0), 3),  # int64 overflow
+])
+def test_fwd_validation(lib, args, status):
+    assert lib.fa_fwd(*args, None) == status
+
+
+def test_empty_forward_is_ok_without_pointers(lib):
+    assert lib.fa_fwd(0, 0, 0, 0, 0, 0, 2, 1, 8, 8, 64, 0.1, 1, None) == 0
+    assert lib.fa_fwd(0, 0, 0, 0, 0, 1, 2, 1, 0, 8, 64, 0.1, 1, None) == 0
+
+
+def test_bwd_validation(lib):
+    a = [P] * 10
+    assert lib.fa_bwd(*a, 1, 2, 1, 8, 8, 256, 0.1, 1, None) == 4   # no D=256 backward
+    assert lib.fa_bwd(*a, 1, 4, 3, 8, 8, 64, 0.1, 1, None) == 5
+    assert lib.fa_bwd(*a, 1, 2, 1, 9, 8, 64, 0.1, 1, None) == 6
+    bad = list(a)
+    bad[7] = 0  # dq NULL
+    assert lib.fa_bwd(*bad, 1, 2, 1, 8, 8, 64, 0.1, 1, None) == 1
+    # the dK/dV half does not need dq
+    assert lib.fa_bwd_dq(P, P, P, P, P, P, 0, 1, 2, 1, 8, 8, 64, 0.1, 1, None) == 1
+    assert lib.fa_bwd_dkv(P, P, P, P, P, P, 0, P, 1, 2, 1, 8, 8, 64, 0.1, 1, None) == 1
+    assert lib.fa_bwd_delta(P, P, P, 1, 2, 8, 80, None) == 4
+    assert lib.fa_bwd_delta(P, 0, P, 1, 2, 8, 64, None) == 1
+    assert lib.fa_bwd_delta(0, 0, 0, 1, 2, 0, 64, None) == 0

@@ -1,0 +1,44 @@
+"""Pins of bench.py's accounting against numbers the pages print
+(tests/golden/*, each file names its page and table)."""
+import os
+
+import pytest
+
+import bench
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [list(map(float, ln.split())) for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def test_flop_model_reproduces_printed_throughput():
+    for Lq, Lk, ms, tf in _rows("d256_forward_timings.txt"):
+        _, fwd = bench.model_flops(1, 16, int(Lq), int(Lk), 256, causal=True)
+        assert round(fwd / (ms * 1e-3) / 1e12, 1) == pytest.approx(tf, abs=0.05)
+
+
+def test_training_shape_flops():
+    # 8192-token training shape: 0.5498 TFLOP forward + 2.5x backward
+    total, fwd = bench.model_flops(1, 32, 8192, 8192, 128, causal=True)
+    assert fwd == 4 * 32 * 8192 * 8192 * 128 / 2
+    assert total == pytest.approx(3.5 * fwd)
+    assert round(total / 1e12, 4) == 1.9241
+
+
+def test_unfused_score_matrix_size():
+    for L, mb in _rows("unfused_score_matrix_mb.txt"):
+        assert round(bench.unfused_score_bytes(32, int(L), 2) / 1e6) == pytest.approx(mb, abs=1)
+
+
+@pytest.mark.parametrize("Lq,Lk,causal", [(7, 7, True), (5, 9, True), (1, 4, True), (6, 3, False), (0, 5, True)])
+def test_visible_pairs_brute_force(Lq, Lk, causal):
+    want = sum(1 for i in range(Lq) for j in range(Lk) if (not causal) or j <= i + (Lk - Lq))
+    assert bench.visible_pairs(Lq, Lk, causal) == want
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
