@@ -46,26 +46,28 @@ __global__ __launch_bounds__(256) void fa_delta_kernel(DeltaArgs a) {
 // ---------------------------------------------------------------- dQ
 // One workgroup = 4 wavefronts = 128 query rows of one query head; each
 // wavefront owns 32 rows, one row per lane pair (transposed products, as in
-// the forward).  Per key tile:
+// the forward).  Per key tile (K, V double buffered in LDS, direct loads one
+// tile ahead):
 //   S^T  = K Q^T        (A = K from LDS, B = Q^T in registers)
 //   dP^T = V dO^T       (A = V from LDS, B = dO^T in registers)
 //   dS^T = P^T * (dP^T - delta)
 //   dQ^T += K^T dS^T    (A = K^T by transposed LDS reads, B = dS^T)
 template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void fa_dq_kernel(BwdArgs a) {
   constexpr int BM = 128;
-  constexpr int KP = D + 8;
+  constexpr int P = Tile<D>::P;
   constexpr int NKD = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NNB = BN / 32;
   constexpr int NKS = BN / 16;
-  constexpr int CPR = D / 8;
-  constexpr int CPT = BN * CPR / 256;
-  static_assert(BN * CPR % 256 == 0, "tile must split evenly over the workgroup");
 
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][2][BN * KP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK0[BN * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV0[BN * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK1[BN * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV1[BN * P];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.G;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int per_group = a.nqt * G;
@@ -78,8 +80,6 @@ __global__ __launch_bounds__(256, 1) void fa_dq_kernel(BwdArgs a) {
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
   const int64_t qh = (int64_t)(b * a.Hq + hq) * Lq;
-  const bf16_t* qp = a.q + qh * D;
-  const bf16_t* dop = a.dO + qh * D;
   const bf16_t* kp = a.k + ((int64_t)(b * a.Hkv + hk) * Lk) * D;
   const bf16_t* vp = a.v + ((int64_t)(b * a.Hkv + hk) * Lk) * D;
 
@@ -87,68 +87,46 @@ __global__ __launch_bounds__(256, 1) void fa_dq_kernel(BwdArgs a) {
   const int qrow = q0 + 32 * w + lr;
   const bool row_ok = qrow < Lq;
 
+  int kv_end = Lk;
+  if (CAUSAL) kv_end = min(Lk, min(q0 + BM, Lq) + off);
+  const int nkt = (kv_end + BN - 1) / BN;
+  int n_full = Lk / BN;  // tiles that need no mask (keys past Lk repeat the last key)
+  if (CAUSAL) n_full = min(n_full, (q0 + off + 1) / BN);
+  n_full = max(0, min(n_full, nkt));
+
+  const TileLoader<D> ld(w, lane);
+  auto issue = [&](int j, bf16_t* kt, bf16_t* vt) {
+    ld.template load<BN>(kt, kp, j * BN, Lk, w);
+    ld.template load<BN>(vt, vp, j * BN, Lk, w);
+  };
+  if (nkt > 0) issue(0, sK0, sV0);
+
   bf16x8 qf[NKD], dof[NKD];
+  {
+    const int qr = min(qrow, Lq - 1);
 #pragma unroll
-  for (int kd = 0; kd < NKD; ++kd) {
-    if (row_ok) {
-      qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qrow * D + 16 * kd + 8 * lg));
-      dof[kd] = as_bf16x8(ldg16(dop + (int64_t)qrow * D + 16 * kd + 8 * lg));
-    } else {
-      qf[kd] = as_bf16x8(make_uint4(0, 0, 0, 0));
-      dof[kd] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    for (int kd = 0; kd < NKD; ++kd) {
+      qf[kd] = as_bf16x8(ldg16(a.q + (qh + qr) * D + 16 * kd + 8 * lg));
+      dof[kd] = as_bf16x8(ldg16(a.dO + (qh + qr) * D + 16 * kd + 8 * lg));
     }
   }
   // rows past Lq: lse = +inf makes every P exactly 0
   const float lse2 = row_ok ? a.lse[qh + qrow] * kLog2e : INFINITY;
   const float dl = row_ok ? a.delta[qh + qrow] : 0.f;
 
-  int kv_end = Lk;
-  if (CAUSAL) kv_end = min(Lk, min(q0 + BM, Lq) + off);
-  const int nkt = (kv_end + BN - 1) / BN;
-
-  uint4 rk[CPT], rv[CPT];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int chunk = tid + 256 * c;
-      const int row = chunk / CPR, col = (chunk % CPR) * 8;
-      const int key = j * BN + row;
-      if (key < Lk) {
-        rk[c] = ldg16(kp + (int64_t)key * D + col);
-        rv[c] = ldg16(vp + (int64_t)key * D + col);
-      } else {
-        rk[c] = make_uint4(0, 0, 0, 0);
-        rv[c] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int chunk = tid + 256 * c;
-      const int row = chunk / CPR, col = (chunk % CPR) * 8;
-      *reinterpret_cast<uint4*>(&lds[buf][0][row * KP + col]) = rk[c];
-      *reinterpret_cast<uint4*>(&lds[buf][1][row * KP + col]) = rv[c];
-    }
-  };
-
+  const TileReader<D> rd(lane);
   const float c2 = a.scale_log2;
   f32x16 dq[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq[db] = zero16();
-  const int troff = tr_lane_offset(lane, KP);
 
-  if (nkt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  wait_vmem();
   __syncthreads();
-
   for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkt) load_tile(j + 1);
-    const bf16_t* Ks = lds[buf][0];
-    const bf16_t* Vs = lds[buf][1];
+    const bool odd = j & 1;
+    if (j + 1 < nkt) issue(j + 1, odd ? sK0 : sK1, odd ? sV0 : sV1);
+    const bf16_t* Ks = odd ? sK1 : sK0;
+    const bf16_t* Vs = odd ? sV1 : sV0;
 
     f32x16 s[NNB], dp[NNB];
 #pragma unroll
@@ -157,37 +135,37 @@ __global__ __launch_bounds__(256, 1) void fa_dq_kernel(BwdArgs a) {
       dp[nb] = zero16();
 #pragma unroll
       for (int kd = 0; kd < NKD; ++kd) {
-        s[nb] = mfma32(lds_read16(Ks + (nb * 32 + lr) * KP + 16 * kd + 8 * lg), qf[kd], s[nb]);
-        dp[nb] = mfma32(lds_read16(Vs + (nb * 32 + lr) * KP + 16 * kd + 8 * lg), dof[kd], dp[nb]);
+        s[nb] = mfma32(rd.row16(Ks, nb * 32, kd), qf[kd], s[nb]);
+        dp[nb] = mfma32(rd.row16(Vs, nb * 32, kd), dof[kd], dp[nb]);
       }
     }
-
-    const int kbase = j * BN;
-    const bool need_mask = (kbase + BN > Lk) || (CAUSAL && kbase + BN - 1 > q0 + off);
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(s[nb][i], c2, -lse2));
-        if (need_mask) {
-          const int key = kbase + nb * 32 + crow(i, lg);
-          const bool vis = key < Lk && (!CAUSAL || key <= qrow + off);
-          p = vis ? p : 0.f;
-        }
-        s[nb][i] = p * (dp[nb][i] - dl);  // dS^T (scale applied at the end)
+      for (int i = 0; i < 16; ++i) s[nb][i] = fast_exp2(fmaf(s[nb][i], c2, -lse2));
+    if (j >= n_full) {  // diagonal or ragged tile
+      __asm__ volatile("");
+      const int last = CAUSAL ? min(qrow + off, Lk - 1) : Lk - 1;
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb) {
+        const int thr = last - (j * BN + nb * 32 + 4 * lg);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[nb][i] = (crow(i, 0) <= thr) ? s[nb][i] : 0.f;
       }
-
+    }
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[nb][i] = s[nb][i] * (dp[nb][i] - dl);  // dS^T
     bf16x8 dsf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) dsf[ks] = pack8(s[ks / 2], ks % 2);
-
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        dq[db] = mfma32(lds_read_trA(Ks, troff, 16 * ks, 32 * db, KP), dsf[ks], dq[db]);
+      for (int ks = 0; ks < NKS; ++ks) dq[db] = mfma32(rd.trA(Ks, 16 * ks, db), dsf[ks], dq[db]);
 
-    if (j + 1 < nkt) store_tile(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -209,29 +187,31 @@ __global__ __launch_bounds__(256, 1) void fa_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- dK / dV
 // One workgroup = 4 wavefronts = 128 keys of one key/value head; each
 // wavefront owns 32 keys, one key per lane pair.  K and V stay in registers;
-// query tiles of BM rows of Q and dO (plus their LSE and delta) stream
-// through LDS, for every query head of the group in turn.  Per query tile:
+// query tiles of BM rows of Q and dO stream through LDS (double buffered,
+// direct loads one tile ahead) together with their LSE and delta, for every
+// query head of the group in turn.  Per query tile:
 //   S  = Q K^T          (A = Q from LDS, B = K^T in registers)
 //   dP = dO V^T         (A = dO from LDS, B = V^T in registers)
 //   dS = P * (dP - delta)
 //   dV^T += dO^T P      (A = dO^T by transposed LDS reads, B = P)
 //   dK^T += Q^T dS      (A = Q^T by transposed LDS reads, B = dS)
 template <int D, int BM, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void fa_dkv_kernel(BwdArgs a) {
   constexpr int BN = 128;
-  constexpr int QP = D + 8;
+  constexpr int P = Tile<D>::P;
   constexpr int NKD = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NMB = BM / 32;
   constexpr int NKS = BM / 16;
-  constexpr int CPR = D / 8;
-  constexpr int CPT = BM * CPR / 256;
-  static_assert(BM * CPR % 256 == 0, "tile must split evenly over the workgroup");
 
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][2][BM * QP];  // [buf][Q / dO]
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];       // [buf][lse*log2e / delta]
+  __shared__ __attribute__((aligned(1024))) bf16_t sQ0[BM * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t sD0[BM * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t sQ1[BM * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t sD1[BM * P];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buf][lse*log2e / delta]
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.G;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / a.nkt;
@@ -244,18 +224,6 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_kernel(BwdArgs a) {
   const int krow = k0 + 32 * w + lr;
   const bool key_ok = krow < Lk;
 
-  bf16x8 kf[NKD], vf[NKD];
-#pragma unroll
-  for (int kd = 0; kd < NKD; ++kd) {
-    if (key_ok) {
-      kf[kd] = as_bf16x8(ldg16(a.k + (kvh + krow) * D + 16 * kd + 8 * lg));
-      vf[kd] = as_bf16x8(ldg16(a.v + (kvh + krow) * D + 16 * kd + 8 * lg));
-    } else {
-      kf[kd] = as_bf16x8(make_uint4(0, 0, 0, 0));
-      vf[kd] = as_bf16x8(make_uint4(0, 0, 0, 0));
-    }
-  }
-
   // first query row that can see key k0: i >= k0 - off
   const int qfirst = CAUSAL ? max(0, k0 - off) : 0;
   const int qt_first = qfirst / BM;
@@ -263,45 +231,41 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_kernel(BwdArgs a) {
   const int nq = max(0, nqt - qt_first);
   const int niter = G * nq;
 
-  uint4 rq[CPT], rd[CPT];
+  const TileLoader<D> ld(w, lane);
   float rstat = 0.f;
-  auto load_tile = [&](int n) {
-    const int hi = n / nq, qt = qt_first + (n - (n / nq) * nq);
+  auto issue = [&](int n, bf16_t* qt_lds, bf16_t* dt_lds) {
+    const int hi = n / nq, qtile = qt_first + (n - (n / nq) * nq);
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
-    const int qbase = qt * BM;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int chunk = tid + 256 * c;
-      const int row = chunk / CPR, col = (chunk % CPR) * 8;
-      const int qr = qbase + row;
-      if (qr < Lq) {
-        rq[c] = ldg16(a.q + (qh + qr) * D + col);
-        rd[c] = ldg16(a.dO + (qh + qr) * D + col);
-      } else {
-        rq[c] = make_uint4(0, 0, 0, 0);
-        rd[c] = make_uint4(0, 0, 0, 0);
-      }
-    }
+    const int qbase = qtile * BM;
+    ld.template load<BM>(qt_lds, a.q + qh * D, qbase, Lq, w);
+    ld.template load<BM>(dt_lds, a.dO + qh * D, qbase, Lq, w);
     if (tid < 2 * BM) {
-      const int r = tid % BM;
-      const int qr = qbase + r;
+      const int qr = qbase + (tid % BM);
       if (tid < BM)
         rstat = qr < Lq ? a.lse[qh + qr] * kLog2e : INFINITY;  // +inf: P = 0 on padded rows
       else
         rstat = qr < Lq ? a.delta[qh + qr] : 0.f;
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int chunk = tid + 256 * c;
-      const int row = chunk / CPR, col = (chunk % CPR) * 8;
-      *reinterpret_cast<uint4*>(&lds[buf][0][row * QP + col]) = rq[c];
-      *reinterpret_cast<uint4*>(&lds[buf][1][row * QP + col]) = rd[c];
-    }
+  auto put_stat = [&](int buf) {
     if (tid < 2 * BM) stat[buf][tid / BM][tid % BM] = rstat;
   };
+  if (niter > 0) {
+    issue(0, sQ0, sD0);
+    put_stat(0);
+  }
 
+  bf16x8 kf[NKD], vf[NKD];
+  {
+    const int kr = min(krow, Lk - 1);  // keys past Lk: a copy, never stored
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) {
+      kf[kd] = as_bf16x8(ldg16(a.k + (kvh + kr) * D + 16 * kd + 8 * lg));
+      vf[kd] = as_bf16x8(ldg16(a.v + (kvh + kr) * D + 16 * kd + 8 * lg));
+    }
+  }
+
+  const TileReader<D> rd(lane);
   const float c2 = a.scale_log2;
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -309,20 +273,15 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_kernel(BwdArgs a) {
     dk[db] = zero16();
     dv[db] = zero16();
   }
-  const int troff = tr_lane_offset(lane, QP);
 
-  if (niter > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  wait_vmem();
   __syncthreads();
-
   for (int n = 0; n < niter; ++n) {
     const int buf = n & 1;
     const int q0 = (qt_first + (n - (n / nq) * nq)) * BM;
-    if (n + 1 < niter) load_tile(n + 1);
-    const bf16_t* Qs = lds[buf][0];
-    const bf16_t* dOs = lds[buf][1];
+    if (n + 1 < niter) issue(n + 1, buf ? sQ0 : sQ1, buf ? sD0 : sD1);
+    const bf16_t* Qs = buf ? sQ1 : sQ0;
+    const bf16_t* Ds = buf ? sD1 : sD0;
 
     f32x16 s[NMB], dp[NMB];
 #pragma unroll
@@ -331,27 +290,37 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_kernel(BwdArgs a) {
       dp[mb] = zero16();
 #pragma unroll
       for (int kd = 0; kd < NKD; ++kd) {
-        s[mb] = mfma32(lds_read16(Qs + (mb * 32 + lr) * QP + 16 * kd + 8 * lg), kf[kd], s[mb]);
-        dp[mb] = mfma32(lds_read16(dOs + (mb * 32 + lr) * QP + 16 * kd + 8 * lg), vf[kd], dp[mb]);
+        s[mb] = mfma32(rd.row16(Qs, mb * 32, kd), kf[kd], s[mb]);
+        dp[mb] = mfma32(rd.row16(Ds, mb * 32, kd), vf[kd], dp[mb]);
       }
     }
-
-    const bool need_mask = CAUSAL && (k0 + BN - 1 > q0 + off);
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int r0 = mb * 32 + 8 * i4 + 4 * lg;  // 4 consecutive query rows
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][r0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[mb][4 * i4 + e] = fast_exp2(fmaf(s[mb][4 * i4 + e], c2, -l4[e]));
+      }
+    if (CAUSAL && k0 + BN - 1 > q0 + off) {  // tile crosses the diagonal
+      __asm__ volatile("");
+      // key krow is visible to row q0 + mb*32 + crow(i, lg) iff crow(i, 0) >= thr
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int thr = krow - off - q0 - mb * 32 - 4 * lg;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[mb][i] = (crow(i, 0) >= thr) ? s[mb][i] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int r0 = mb * 32 + 8 * i4 + 4 * lg;
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][r0]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
-          float p = fast_exp2(fmaf(s[mb][i], c2, -l4[e]));
-          if (need_mask) p = (krow <= q0 + r0 + e + off) ? p : 0.f;
-          s[mb][i] = p;
-          dp[mb][i] = p * (dp[mb][i] - d4[e]);
-        }
+        for (int e = 0; e < 4; ++e) dp[mb][4 * i4 + e] = s[mb][4 * i4 + e] * (dp[mb][4 * i4 + e] - d4[e]);
       }
 
     bf16x8 pf[NKS], dsf[NKS];
@@ -360,16 +329,16 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_kernel(BwdArgs a) {
       pf[ks] = pack8(s[ks / 2], ks % 2);
       dsf[ks] = pack8(dp[ks / 2], ks % 2);
     }
-
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        dv[db] = mfma32(lds_read_trA(dOs, troff, 16 * ks, 32 * db, QP), pf[ks], dv[db]);
-        dk[db] = mfma32(lds_read_trA(Qs, troff, 16 * ks, 32 * db, QP), dsf[ks], dk[db]);
+        dv[db] = mfma32(rd.trA(Ds, 16 * ks, db), pf[ks], dv[db]);
+        dk[db] = mfma32(rd.trA(Qs, 16 * ks, db), dsf[ks], dk[db]);
       }
 
-    if (n + 1 < niter) store_tile(buf ^ 1);
+    if (n + 1 < niter) put_stat(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 

@@ -8,9 +8,16 @@
 //   C/D      : lane l holds column (l % 32), register i holds row
 //              8*(i / 4) + 4*(l / 32) + (i % 4), i = 0..15
 // A contraction only needs the A and B operands to agree on which logical k
-// sits in which (lane group, slot); the kernels below rely on that to feed a
+// sits in which (lane group, slot); the kernels rely on that to feed a
 // C-layout result (P, dS) straight back in as an operand, with the other
 // operand read in the matching key order.
+//
+// LDS tiles are row-major with 16-byte chunks; logical chunk c of tile row r
+// sits at physical chunk c ^ swz(r), swz(r) = 2*(r%4) + (r/4)%2.  Measured on
+// gfx950 this spreads both access patterns used below over distinct banks:
+// 16-byte row reads of 32 consecutive rows, and the transposed 8-byte reads
+// (4 rows x 32 bytes per 16-lane group).  Rows are not padded, so a wave's
+// 64 x 16-byte direct global->LDS load fills 1 KiB of consecutive chunks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,7 +27,6 @@ namespace cgqa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -57,13 +63,9 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int half) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Exchange with the lane 32 positions away (the other half of a C column).
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
-}
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-// 16-byte global load / store helpers.
 __device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
 __device__ __forceinline__ bf16x8 lds_read16(const bf16_t* p) {
@@ -85,21 +87,98 @@ __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
   return r;
 }
 
-// Per-lane offset (in elements, row pitch `pitch`) used to gather an A
-// operand whose rows run along the tile's columns ("transposed" operand) from
-// a row-major LDS tile with two transposed reads.  The operand covers tile
-// rows r0 + 8*(s/4) + 4*(l/32) + (s%4) (the key order of a C-layout result,
-// see crow) and tile columns c0 + (l % 32).  Lane l addresses row
-// 4*(l/32) + (l/4)%4 and column 16*((l/16)%2) + 4*(l%4); the second read adds
-// 8 rows.
-__device__ __forceinline__ int tr_lane_offset(int lane, int pitch) {
-  return (4 * (lane >> 5) + ((lane >> 2) & 3)) * pitch + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-}
+// ------------------------------------------------------------ tile layout
 
-__device__ __forceinline__ bf16x8 lds_read_trA(const bf16_t* tile, int lane_off, int r0, int c0, int pitch) {
-  const bf16_t* p = tile + lane_off + r0 * pitch + c0;
-  return cat8(lds_read_tr4(p), lds_read_tr4(p + 8 * pitch));
-}
+__device__ __forceinline__ constexpr int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;                  // logical 16-byte chunks per row
+  static constexpr int PC = (D == 96) ? 16 : CPR;    // physical chunks per row (power of two)
+  static constexpr int P = PC * 8;                   // row pitch in elements
+};
+
+// Per-lane element offsets for reading a tile from LDS.
+//  row16(kd, r0): A/B operand fragment of rows r0 + (lane % 32) (r0 a multiple
+//    of 8), head-dim slots 16*kd + 8*(lane/32) + s  (one 16-byte read).
+//  trA(r0, db): A operand whose rows are tile columns 32*db + lane % 32 and
+//    whose k slots are tile rows r0 + 8*(s/4) + 4*(lane/32) + s%4 (the row
+//    order of a C-layout result), r0 a multiple of 16; two transposed reads.
+template <int D>
+struct TileReader {
+  static constexpr int P = Tile<D>::P;
+  int ra[4];
+  int trE, trO;
+  __device__ __forceinline__ explicit TileReader(int lane) {
+    const int lr = lane & 31, lg = lane >> 5;
+    const int s = swz(lr);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ra[j] = lr * P + (((2 * j + lg) ^ s) << 3);
+    // transposed read: lane addresses row rl, chunk y, 8-byte half `within`
+    const int rl = 4 * (lane >> 5) + ((lane >> 2) & 3);
+    const int y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int within = 4 * (lane & 1);
+    const int st = swz(rl);
+    const int tb = rl * P + ((y ^ (st & 3)) << 3) + within;
+    const int sb = st >> 2;
+    trE = tb + 32 * sb;
+    trO = tb - 32 * sb;
+  }
+  __device__ __forceinline__ bf16x8 row16(const bf16_t* tile, int r0, int kd) const {
+    return lds_read16(tile + r0 * P + ra[kd & 3] + 64 * (kd >> 2));
+  }
+  __device__ __forceinline__ bf16x8 trA(const bf16_t* tile, int r0, int db) const {
+    const bf16_t* p = tile + r0 * P + ((db & 1) ? trO : trE) + 32 * db;
+    return cat8(lds_read_tr4(p), lds_read_tr4(p + 8 * P));
+  }
+};
+
+// Direct global->LDS copy of a ROWS x D bf16 tile into the swizzled layout.
+// Load round i of wave w fills the 1 KiB block 4*i + w of the tile, i.e. tile
+// rows 4*RW*i + RW*w + lane / PC (RW = 64 / PC rows per block), physical
+// chunk lane % PC.  Because 4*RW is a multiple of 8 the swizzle, and so the
+// lane's source column and in-block row, are the same in every round: one
+// 32-bit lane offset serves the whole tile and each round only moves a
+// wave-uniform base.
+template <int D>
+struct TileLoader {
+  static constexpr int PC = Tile<D>::PC, CPR = Tile<D>::CPR;
+  static constexpr int RW = 64 / PC;  // tile rows per wave block
+  int rl;    // tile row within the block group (0 .. 4*RW-1)
+  int loff;  // element offset of this lane's source chunk relative to its row start
+  __device__ __forceinline__ TileLoader(int w, int lane) {
+    rl = RW * w + lane / PC;
+    int c = (lane % PC) ^ swz(rl);
+    if (c >= CPR) c = 0;  // padding slots (D = 96): load any in-bounds data
+    loff = c * 8;
+  }
+  // Rows row0 .. row0+ROWS-1 of `g` (row stride D).  Rows at or past `nrows`
+  // repeat row nrows-1, which keeps every value finite; kernels mask them.
+  template <int ROWS>
+  __device__ __forceinline__ void load(bf16_t* tile, const bf16_t* g, int row0, int nrows, int w) const {
+    constexpr int ROUNDS = ROWS * PC / 256;
+    static_assert(ROWS * PC % 256 == 0, "tile must split evenly over four waves");
+    if (row0 + ROWS <= nrows) {
+#pragma unroll
+      for (int i = 0; i < ROUNDS; ++i) {
+        const bf16_t* base = g + (int64_t)(row0 + 4 * RW * i) * D;  // wave-uniform
+        __builtin_amdgcn_global_load_lds((const void*)(base + rl * D + loff),
+                                         (LDS_AS void*)(tile + (4 * i + w) * 512), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < ROUNDS; ++i) {
+        const int gr = min(row0 + 4 * RW * i + rl, nrows - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)gr * D + loff),
+                                         (LDS_AS void*)(tile + (4 * i + w) * 512), 16, 0, 0);
+      }
+    }
+  }
+};
+
+// s_waitcnt vmcnt(0), leaving expcnt/lgkmcnt unconstrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Map a launch-order block id to a logical work id so that the blocks the
 // hardware places on one XCD (block id mod 8, round robin) get a contiguous

@@ -13,13 +13,19 @@
 // query head; each wavefront owns 32 rows):
 //   S^T = K Q^T on MFMA: K (the A operand) comes from LDS, Q^T (B operand)
 //   stays in registers for the whole key loop.  Computing the transpose puts
-//   one query row per lane (two lanes per row), so row max / row sum are
-//   per-lane plus one exchange with the lane 32 away.
+//   one query row per lane pair, so row max / row sum are per-lane plus one
+//   exchange with the lane 32 away.
 //   O^T += V^T P^T on MFMA: P^T goes from the fp32 C layout to bf16 operand
 //   registers directly; V^T is read from the row-major V tile with the
 //   transposed LDS read.
-// K and V tiles are double buffered in LDS; the next tile's global loads are
-// in flight while the current tile is computed.
+// K and V tiles are double buffered in LDS and filled by direct global->LDS
+// loads issued one tile ahead.  Tiles that need no mask (fully below the
+// diagonal and inside Lk) run a mask-free body.
+//
+// Running max with slack: the accumulator is rescaled only when some row's
+// max grows by more than 2^8 (in exp2 units) over the max it was last scaled
+// with.  O = acc / l and L = m + log2 l do not depend on which m is used, and
+// with the slack every p = exp2(s - m) stays <= 256, far from overflow.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -28,18 +34,20 @@ namespace cgqa {
 template <int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs a) {
   constexpr int BM = 128;
-  constexpr int KP = D + 8;        // LDS row pitch in elements (pads banks)
+  constexpr int P = Tile<D>::P;
   constexpr int NKD = D / 16;      // 16-wide k steps over the head dim
   constexpr int NDB = D / 32;      // 32-row blocks of O^T
   constexpr int NNB = BN / 32;     // 32-key blocks per key tile
   constexpr int NKS = BN / 16;     // 16-key k steps per key tile
-  constexpr int CPR = D / 8;       // 16-byte chunks per row
-  constexpr int CPT = BN * CPR / 256;
-  static_assert(BN * CPR % 256 == 0, "tile must split evenly over the workgroup");
+  constexpr float kSlack = 8.f;
 
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][2][BN * KP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK0[BN * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV0[BN * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK1[BN * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV1[BN * P];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- which (batch, head, query tile) this workgroup computes
   const int G = a.G;
@@ -60,100 +68,81 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
   const int q0 = qt * BM;
   const int qrow = q0 + 32 * w + lr;
 
-  // ---- Q^T operand (B): lane holds query qrow, head-dim slots 16*kd + 8*lg + s
-  bf16x8 qf[NKD];
-  if (qrow < Lq) {
-#pragma unroll
-    for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qrow * D + 16 * kd + 8 * lg));
-  } else {
-#pragma unroll
-    for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(make_uint4(0, 0, 0, 0));
-  }
-
   // ---- key range: causal rows see keys j <= i + off
   int kv_end = Lk;
   if (CAUSAL) kv_end = min(Lk, min(q0 + BM, Lq) + off);
   const int nkt = (kv_end + BN - 1) / BN;
+  int n_full = Lk / BN;  // tiles that need no mask
+  if (CAUSAL) n_full = min(n_full, (q0 + off + 1) / BN);
+  n_full = max(0, min(n_full, nkt));
 
-  uint4 rk[CPT], rv[CPT];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int chunk = tid + 256 * c;
-      const int row = chunk / CPR, col = (chunk % CPR) * 8;
-      const int key = j * BN + row;
-      if (key < Lk) {
-        rk[c] = ldg16(kp + (int64_t)key * D + col);
-        rv[c] = ldg16(vp + (int64_t)key * D + col);
-      } else {
-        rk[c] = make_uint4(0, 0, 0, 0);  // zero rows past Lk: no NaN can leak
-        rv[c] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  const TileLoader<D> ld(w, lane);
+  auto issue = [&](int j, bf16_t* kt, bf16_t* vt) {
+    ld.template load<BN>(kt, kp, j * BN, Lk, w);
+    ld.template load<BN>(vt, vp, j * BN, Lk, w);
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int chunk = tid + 256 * c;
-      const int row = chunk / CPR, col = (chunk % CPR) * 8;
-      *reinterpret_cast<uint4*>(&lds[buf][0][row * KP + col]) = rk[c];
-      *reinterpret_cast<uint4*>(&lds[buf][1][row * KP + col]) = rv[c];
-    }
-  };
+  if (nkt > 0) issue(0, sK0, sV0);
 
+  // ---- Q^T operand (B): lane holds query qrow, head-dim slots 16*kd + 8*lg + s
+  bf16x8 qf[NKD];
+  {
+    const int qr = min(qrow, Lq - 1);  // rows past Lq compute on a copy; never stored
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qr * D + 16 * kd + 8 * lg));
+  }
+
+  const TileReader<D> rd(lane);
   const float c2 = a.scale_log2;
-  float m_run = -INFINITY;  // running max of scaled scores (base-2 units)
+  float m_run = -INFINITY;  // max (exp2 units) the accumulator is scaled with
   float l_run = 0.f;        // this lane's share of the running denominator
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = zero16();
 
-  const int troff = tr_lane_offset(lane, KP);
-
-  if (nkt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  wait_vmem();
   __syncthreads();
-
   for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkt) load_tile(j + 1);
-    const bf16_t* Ks = lds[buf][0];
-    const bf16_t* Vs = lds[buf][1];
+    const bool odd = j & 1;
+    if (j + 1 < nkt) issue(j + 1, odd ? sK0 : sK1, odd ? sV0 : sV1);
+    const bf16_t* Ks = odd ? sK1 : sK0;
+    const bf16_t* Vs = odd ? sV1 : sV0;
 
-    // S^T block: rows = keys, lane column = query
     f32x16 s[NNB];
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb) {
       s[nb] = zero16();
 #pragma unroll
-      for (int kd = 0; kd < NKD; ++kd)
-        s[nb] = mfma32(lds_read16(Ks + (nb * 32 + lr) * KP + 16 * kd + 8 * lg), qf[kd], s[nb]);
+      for (int kd = 0; kd < NKD; ++kd) s[nb] = mfma32(rd.row16(Ks, nb * 32, kd), qf[kd], s[nb]);
     }
-
-    const int kbase = j * BN;
-    const bool need_mask = (kbase + BN > Lk) || (CAUSAL && kbase + BN - 1 > q0 + off);
-    if (need_mask) {
+    if (j >= n_full) {  // diagonal or ragged tile: hide keys past the diagonal or past Lk
+      __asm__ volatile("");  // keep this a real branch (not speculated into every tile)
+      // key = base + crow(i, 0) is visible iff crow(i, 0) <= last - base
+      const int last = CAUSAL ? min(qrow + off, Lk - 1) : Lk - 1;
 #pragma unroll
-      for (int nb = 0; nb < NNB; ++nb)
+      for (int nb = 0; nb < NNB; ++nb) {
+        const int thr = last - (j * BN + nb * 32 + 4 * lg);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase + nb * 32 + crow(i, lg);
-          const bool vis = key < Lk && (!CAUSAL || key <= qrow + off);
-          if (!vis) s[nb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i) s[nb][i] = (crow(i, 0) <= thr) ? s[nb][i] : -INFINITY;
+      }
     }
-
     float mx = -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nb][i]);
     mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    const float m_cand = mx * c2;
+    if (__any(m_cand > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb)
@@ -163,24 +152,16 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
         s[nb][i] = p;
         rs += p;
       }
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-
+    l_run += rs;
     bf16x8 pf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) pf[ks] = pack8(s[ks / 2], ks % 2);
-
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        acc[db] = mfma32(lds_read_trA(Vs, troff, 16 * ks, 32 * db, KP), pf[ks], acc[db]);
+      for (int ks = 0; ks < NKS; ++ks) acc[db] = mfma32(rd.trA(Vs, 16 * ks, db), pf[ks], acc[db]);
 
-    if (j + 1 < nkt) store_tile(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
