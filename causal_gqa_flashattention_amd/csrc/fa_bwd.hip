@@ -185,25 +185,29 @@ __global__ __launch_bounds__(256, 2) void fa_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK / dV
-// One workgroup = 4 wavefronts = 128 keys of one key/value head; each
-// wavefront owns 32 keys, one key per lane pair.  K and V stay in registers;
-// query tiles of BM rows of Q and dO stream through LDS (double buffered,
-// direct loads one tile ahead) together with their LSE and delta, for every
-// query head of the group in turn.  Per query tile:
-//   S  = Q K^T          (A = Q from LDS, B = K^T in registers)
-//   dP = dO V^T         (A = dO from LDS, B = V^T in registers)
+// One workgroup = 8 wavefronts = 128 keys of one key/value head.  The keys
+// form four 32-key blocks; wavefront w owns block w % 4 for the query rows
+// 32*(w / 4) .. +31 of every query tile, so two wavefronts accumulate partial
+// dK/dV for the same keys over different rows and add them once at the end.
+// K and V sit in LDS for the whole kernel; query tiles of 64 rows of Q and dO
+// stream through LDS (double buffered, direct loads one tile ahead) with
+// their LSE and delta, for every query head of the group in turn.
+// Per query tile and wavefront (32 rows x 32 keys):
+//   S  = Q K^T          (A = Q rows, B = K rows, both from LDS)
+//   dP = dO V^T         (A = dO rows, B = V rows)
 //   dS = P * (dP - delta)
 //   dV^T += dO^T P      (A = dO^T by transposed LDS reads, B = P)
 //   dK^T += Q^T dS      (A = Q^T by transposed LDS reads, B = dS)
-template <int D, int BM, bool CAUSAL>
-__global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void fa_dkv_kernel(BwdArgs a) {
-  constexpr int BN = 128;
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
+  constexpr int BN = 128;   // keys per workgroup
+  constexpr int BM = 64;    // query rows per tile (two halves of 32)
   constexpr int P = Tile<D>::P;
   constexpr int NKD = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int NMB = BM / 32;
-  constexpr int NKS = BM / 16;
 
+  __shared__ __attribute__((aligned(1024))) bf16_t sK[BN * P];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV[BN * P];
   __shared__ __attribute__((aligned(1024))) bf16_t sQ0[BM * P];
   __shared__ __attribute__((aligned(1024))) bf16_t sD0[BM * P];
   __shared__ __attribute__((aligned(1024))) bf16_t sQ1[BM * P];
@@ -212,6 +216,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void fa_dkv_kernel(BwdArgs 
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = w & 3, qhalf = w >> 2;
   const int G = a.G;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / a.nkt;
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void fa_dkv_kernel(BwdArgs 
 
   const int64_t kvh = (int64_t)(b * a.Hkv + hk) * Lk;
   const int k0 = kt * BN;
-  const int krow = k0 + 32 * w + lr;
+  const int krow = k0 + 32 * kb + lr;
   const bool key_ok = krow < Lk;
 
   // first query row that can see key k0: i >= k0 - off
@@ -231,14 +236,18 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void fa_dkv_kernel(BwdArgs 
   const int nq = max(0, nqt - qt_first);
   const int niter = G * nq;
 
-  const TileLoader<D> ld(w, lane);
+  // the 8 waves load as two groups of four: waves 0-3 fill Q, waves 4-7 fill dO
+  const int wl = w & 3;
+  const TileLoader<D> ld(wl, lane);
   float rstat = 0.f;
   auto issue = [&](int n, bf16_t* qt_lds, bf16_t* dt_lds) {
     const int hi = n / nq, qtile = qt_first + (n - (n / nq) * nq);
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
     const int qbase = qtile * BM;
-    ld.template load<BM>(qt_lds, a.q + qh * D, qbase, Lq, w);
-    ld.template load<BM>(dt_lds, a.dO + qh * D, qbase, Lq, w);
+    if (w < 4)
+      ld.template load<BM>(qt_lds, a.q + qh * D, qbase, Lq, wl);
+    else
+      ld.template load<BM>(dt_lds, a.dO + qh * D, qbase, Lq, wl);
     if (tid < 2 * BM) {
       const int qr = qbase + (tid % BM);
       if (tid < BM)
@@ -250,19 +259,14 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void fa_dkv_kernel(BwdArgs 
   auto put_stat = [&](int buf) {
     if (tid < 2 * BM) stat[buf][tid / BM][tid % BM] = rstat;
   };
+  // K and V of this key tile, once (rows past Lk repeat the last key)
+  if (w < 4)
+    ld.template load<BN>(sK, a.k + kvh * D, k0, Lk, wl);
+  else
+    ld.template load<BN>(sV, a.v + kvh * D, k0, Lk, wl);
   if (niter > 0) {
     issue(0, sQ0, sD0);
     put_stat(0);
-  }
-
-  bf16x8 kf[NKD], vf[NKD];
-  {
-    const int kr = min(krow, Lk - 1);  // keys past Lk: a copy, never stored
-#pragma unroll
-    for (int kd = 0; kd < NKD; ++kd) {
-      kf[kd] = as_bf16x8(ldg16(a.k + (kvh + kr) * D + 16 * kd + 8 * lg));
-      vf[kd] = as_bf16x8(ldg16(a.v + (kvh + kr) * D + 16 * kd + 8 * lg));
-    }
   }
 
   const TileReader<D> rd(lane);
@@ -282,67 +286,72 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void fa_dkv_kernel(BwdArgs 
     if (n + 1 < niter) issue(n + 1, buf ? sQ0 : sQ1, buf ? sD0 : sD1);
     const bf16_t* Qs = buf ? sQ1 : sQ0;
     const bf16_t* Ds = buf ? sD1 : sD0;
+    const int r0 = 32 * qhalf;  // this wave's rows within the tile
 
-    f32x16 s[NMB], dp[NMB];
+    f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      s[mb] = zero16();
-      dp[mb] = zero16();
-#pragma unroll
-      for (int kd = 0; kd < NKD; ++kd) {
-        s[mb] = mfma32(rd.row16(Qs, mb * 32, kd), kf[kd], s[mb]);
-        dp[mb] = mfma32(rd.row16(Ds, mb * 32, kd), vf[kd], dp[mb]);
-      }
+    for (int kd = 0; kd < NKD; ++kd) {
+      s = mfma32(rd.row16(Qs, r0, kd), rd.row16(sK, 32 * kb, kd), s);
+      dp = mfma32(rd.row16(Ds, r0, kd), rd.row16(sV, 32 * kb, kd), dp);
     }
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][r0 + 8 * i4 + 4 * lg]);
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int r0 = mb * 32 + 8 * i4 + 4 * lg;  // 4 consecutive query rows
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][r0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[mb][4 * i4 + e] = fast_exp2(fmaf(s[mb][4 * i4 + e], c2, -l4[e]));
-      }
+      for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fast_exp2(fmaf(s[4 * i4 + e], c2, -l4[e]));
+    }
     if (CAUSAL && k0 + BN - 1 > q0 + off) {  // tile crosses the diagonal
       __asm__ volatile("");
-      // key krow is visible to row q0 + mb*32 + crow(i, lg) iff crow(i, 0) >= thr
+      // key krow is visible to row q0 + r0 + crow(i, lg) iff crow(i, 0) >= thr
+      const int thr = krow - off - q0 - r0 - 4 * lg;
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const int thr = krow - off - q0 - mb * 32 - 4 * lg;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[mb][i] = (crow(i, 0) >= thr) ? s[mb][i] : 0.f;
-      }
+      for (int i = 0; i < 16; ++i) s[i] = (crow(i, 0) >= thr) ? s[i] : 0.f;
     }
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][r0 + 8 * i4 + 4 * lg]);
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int r0 = mb * 32 + 8 * i4 + 4 * lg;
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][r0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dp[mb][4 * i4 + e] = s[mb][4 * i4 + e] * (dp[mb][4 * i4 + e] - d4[e]);
-      }
-
-    bf16x8 pf[NKS], dsf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      pf[ks] = pack8(s[ks / 2], ks % 2);
-      dsf[ks] = pack8(dp[ks / 2], ks % 2);
+      for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = s[4 * i4 + e] * (dp[4 * i4 + e] - d4[e]);
     }
+    const bf16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 1);
+    const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 1);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        dv[db] = mfma32(rd.trA(Ds, 16 * ks, db), pf[ks], dv[db]);
-        dk[db] = mfma32(rd.trA(Qs, 16 * ks, db), dsf[ks], dk[db]);
-      }
+    for (int db = 0; db < NDB; ++db) {
+      dv[db] = mfma32(rd.trA(Ds, r0, db), pf0, dv[db]);
+      dv[db] = mfma32(rd.trA(Ds, r0 + 16, db), pf1, dv[db]);
+      dk[db] = mfma32(rd.trA(Qs, r0, db), ds0, dk[db]);
+      dk[db] = mfma32(rd.trA(Qs, r0 + 16, db), ds1, dk[db]);
+    }
 
     if (n + 1 < niter) put_stat(buf ^ 1);
     wait_vmem();
     __syncthreads();
   }
 
-  if (key_ok) {
+  // ---- add the two row halves: waves 4-7 hand their partials to waves 0-3
+  // through LDS (the tile buffers are free now), lane-contiguous per register
+  float* red = reinterpret_cast<float*>(sK);  // sK + sV: 2 * BN * P bf16 >= 4 waves * NDB*16*64 floats
+  static_assert(2 * BN * P * 2 >= 4 * NDB * 16 * 64 * 4, "reduction buffer too small");
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    f32x16* acc = pass == 0 ? dk : dv;
+    if (w >= 4) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[((kb * NDB + db) * 16 + i) * 64 + lane] = acc[db][i];
+    }
+    __syncthreads();
+    if (w < 4) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] += red[((kb * NDB + db) * 16 + i) * 64 + lane];
+    }
+    __syncthreads();
+  }
+
+  if (w < 4 && key_ok) {
     bf16_t* dkp = a.dk + (kvh + krow) * D;
     bf16_t* dvp = a.dv + (kvh + krow) * D;
     const float sc = a.scale;
@@ -380,25 +389,25 @@ hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int BN_Q, int BM_KV>
+template <int D, int BN_Q>
 static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int which, hipStream_t stream) {
   const int ndq = (which & 1) ? a.B * a.Hq * a.nqt : 0;
   const int ndkv = (which & 2) ? a.B * a.Hkv * a.nkt : 0;
   if (causal) {
     if (ndq > 0) hipLaunchKernelGGL((fa_dq_kernel<D, BN_Q, true>), dim3(ndq), dim3(256), 0, stream, a);
-    if (ndkv > 0) hipLaunchKernelGGL((fa_dkv_kernel<D, BM_KV, true>), dim3(ndkv), dim3(256), 0, stream, a);
+    if (ndkv > 0) hipLaunchKernelGGL((fa_dkv_kernel<D, true>), dim3(ndkv), dim3(512), 0, stream, a);
   } else {
     if (ndq > 0) hipLaunchKernelGGL((fa_dq_kernel<D, BN_Q, false>), dim3(ndq), dim3(256), 0, stream, a);
-    if (ndkv > 0) hipLaunchKernelGGL((fa_dkv_kernel<D, BM_KV, false>), dim3(ndkv), dim3(256), 0, stream, a);
+    if (ndkv > 0) hipLaunchKernelGGL((fa_dkv_kernel<D, false>), dim3(ndkv), dim3(512), 0, stream, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, hipStream_t stream) {
   switch (D) {
-    case 64: return launch_bwd_d<64, 64, 64>(a, causal, which, stream);
-    case 96: return launch_bwd_d<96, 64, 64>(a, causal, which, stream);
-    case 128: return launch_bwd_d<128, 64, 64>(a, causal, which, stream);
+    case 64: return launch_bwd_d<64, 64>(a, causal, which, stream);
+    case 96: return launch_bwd_d<96, 64>(a, causal, which, stream);
+    case 128: return launch_bwd_d<128, 64>(a, causal, which, stream);
     default: return hipErrorInvalidValue;
   }
 }

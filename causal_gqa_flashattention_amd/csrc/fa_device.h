@@ -12,12 +12,9 @@
 // C-layout result (P, dS) straight back in as an operand, with the other
 // operand read in the matching key order.
 //
-// LDS tiles are row-major with 16-byte chunks; logical chunk c of tile row r
-// sits at physical chunk c ^ swz(r), swz(r) = 2*(r%4) + (r/4)%2.  Measured on
-// gfx950 this spreads both access patterns used below over distinct banks:
-// 16-byte row reads of 32 consecutive rows, and the transposed 8-byte reads
-// (4 rows x 32 bytes per 16-lane group).  Rows are not padded, so a wave's
-// 64 x 16-byte direct global->LDS load fills 1 KiB of consecutive chunks.
+// LDS tiles are row-major with 16-byte chunks, unpadded, with the chunk index
+// XOR-swizzled per row (see Tile below), so a wave's 64 x 16-byte direct
+// global->LDS load fills 1 KiB of consecutive chunks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -88,72 +85,86 @@ __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
 }
 
 // ------------------------------------------------------------ tile layout
-
-__device__ __forceinline__ constexpr int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+//
+// LDS has 64 banks of 4 bytes.  A 16-byte read is served 16 lanes at a time,
+// an 8-byte transposed read 32 lanes at a time; a read runs at full rate when
+// the lanes served together touch 16 distinct 16-byte bank groups.  The row
+// swizzle below gives that for both patterns the kernels use: 16 consecutive
+// rows at one logical chunk (row reads), and 4 rows x 4 consecutive chunks
+// (transposed reads).  Measured on gfx950 both then run near the LDS peak.
 
 template <int D>
 struct Tile {
   static constexpr int CPR = D / 8;                  // logical 16-byte chunks per row
   static constexpr int PC = (D == 96) ? 16 : CPR;    // physical chunks per row (power of two)
   static constexpr int P = PC * 8;                   // row pitch in elements
+  // physical chunk of logical chunk c in row r is c ^ swz(r)
+  __device__ __forceinline__ static constexpr int swz(int r) {
+    return PC >= 16 ? 4 * (r & 3) + ((r >> 2) & 3)          // rows of >= 256 bytes
+                    : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);  // 128-byte rows: two per bank row
+  }
 };
 
 // Per-lane element offsets for reading a tile from LDS.
-//  row16(kd, r0): A/B operand fragment of rows r0 + (lane % 32) (r0 a multiple
-//    of 8), head-dim slots 16*kd + 8*(lane/32) + s  (one 16-byte read).
-//  trA(r0, db): A operand whose rows are tile columns 32*db + lane % 32 and
-//    whose k slots are tile rows r0 + 8*(s/4) + 4*(lane/32) + s%4 (the row
+//  row16(tile, r0, kd): A/B operand fragment of rows r0 + (lane % 32) (r0 a
+//    multiple of 16), head-dim slots 16*kd + 8*(lane/32) + s (one 16-byte read).
+//  trA(tile, r0, db): A operand whose rows are tile columns 32*db + lane % 32
+//    and whose k slots are tile rows r0 + 8*(s/4) + 4*(lane/32) + s%4 (the row
 //    order of a C-layout result), r0 a multiple of 16; two transposed reads.
+// The swizzle mixes the low four chunk bits, so the offsets for the first
+// 8 k steps / 4 column blocks are precomputed per lane and higher steps add a
+// constant.
 template <int D>
 struct TileReader {
-  static constexpr int P = Tile<D>::P;
-  int ra[4];
-  int trE, trO;
+  using T = Tile<D>;
+  static constexpr int P = T::P;
+  static constexpr int NRA = (D / 16) < 8 ? (D / 16) : 8;
+  static constexpr int NTR = (D / 32) < 4 ? (D / 32) : 4;
+  int ra[NRA];
+  int tr[2][NTR];
   __device__ __forceinline__ explicit TileReader(int lane) {
     const int lr = lane & 31, lg = lane >> 5;
-    const int s = swz(lr);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ra[j] = lr * P + (((2 * j + lg) ^ s) << 3);
-    // transposed read: lane addresses row rl, chunk y, 8-byte half `within`
+    for (int j = 0; j < NRA; ++j) ra[j] = lr * P + (((2 * j + lg) ^ T::swz(lr)) << 3);
+    // transposed read: lane addresses row rl (+8), chunk 4*db + y, 8-byte half `within`
     const int rl = 4 * (lane >> 5) + ((lane >> 2) & 3);
     const int y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     const int within = 4 * (lane & 1);
-    const int st = swz(rl);
-    const int tb = rl * P + ((y ^ (st & 3)) << 3) + within;
-    const int sb = st >> 2;
-    trE = tb + 32 * sb;
-    trO = tb - 32 * sb;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dm = 0; dm < NTR; ++dm)
+        tr[h][dm] = (rl + 8 * h) * P + (((4 * dm + y) ^ T::swz(rl + 8 * h)) << 3) + within;
   }
   __device__ __forceinline__ bf16x8 row16(const bf16_t* tile, int r0, int kd) const {
-    return lds_read16(tile + r0 * P + ra[kd & 3] + 64 * (kd >> 2));
+    return lds_read16(tile + r0 * P + ra[kd % NRA] + 128 * (kd / NRA));
   }
   __device__ __forceinline__ bf16x8 trA(const bf16_t* tile, int r0, int db) const {
-    const bf16_t* p = tile + r0 * P + ((db & 1) ? trO : trE) + 32 * db;
-    return cat8(lds_read_tr4(p), lds_read_tr4(p + 8 * P));
+    const bf16_t* p = tile + r0 * P + 128 * (db / NTR);
+    return cat8(lds_read_tr4(p + tr[0][db % NTR]), lds_read_tr4(p + tr[1][db % NTR]));
   }
 };
 
 // Direct global->LDS copy of a ROWS x D bf16 tile into the swizzled layout.
 // Load round i of wave w fills the 1 KiB block 4*i + w of the tile, i.e. tile
 // rows 4*RW*i + RW*w + lane / PC (RW = 64 / PC rows per block), physical
-// chunk lane % PC.  Because 4*RW is a multiple of 8 the swizzle, and so the
-// lane's source column and in-block row, are the same in every round: one
-// 32-bit lane offset serves the whole tile and each round only moves a
-// wave-uniform base.
+// chunk lane % PC; the lane's source chunk follows from the row's swizzle.
 template <int D>
 struct TileLoader {
-  static constexpr int PC = Tile<D>::PC, CPR = Tile<D>::CPR;
+  using T = Tile<D>;
+  static constexpr int PC = T::PC, CPR = T::CPR;
   static constexpr int RW = 64 / PC;  // tile rows per wave block
-  int rl;    // tile row within the block group (0 .. 4*RW-1)
-  int loff;  // element offset of this lane's source chunk relative to its row start
-  __device__ __forceinline__ TileLoader(int w, int lane) {
-    rl = RW * w + lane / PC;
-    int c = (lane % PC) ^ swz(rl);
-    if (c >= CPR) c = 0;  // padding slots (D = 96): load any in-bounds data
-    loff = c * 8;
+  int rl;    // this lane's row within a round's rows
+  int x;     // physical chunk this lane fills
+  __device__ __forceinline__ TileLoader(int w, int lane) : rl(RW * w + lane / PC), x(lane % PC) {}
+  __device__ __forceinline__ int src_off(int r) const {  // element offset within the source row
+    int c = x ^ T::swz(r);
+    return (c < CPR ? c : 0) * 8;  // padding slots (D = 96): any in-bounds data
   }
   // Rows row0 .. row0+ROWS-1 of `g` (row stride D).  Rows at or past `nrows`
   // repeat row nrows-1, which keeps every value finite; kernels mask them.
+  // Each wave issues ROWS*PC/256 loads of 64 x 16 bytes; the caller waits on
+  // vmcnt and synchronises before reading.
   template <int ROWS>
   __device__ __forceinline__ void load(bf16_t* tile, const bf16_t* g, int row0, int nrows, int w) const {
     constexpr int ROUNDS = ROWS * PC / 256;
@@ -161,15 +172,17 @@ struct TileLoader {
     if (row0 + ROWS <= nrows) {
 #pragma unroll
       for (int i = 0; i < ROUNDS; ++i) {
+        const int r = 4 * RW * i + rl;
         const bf16_t* base = g + (int64_t)(row0 + 4 * RW * i) * D;  // wave-uniform
-        __builtin_amdgcn_global_load_lds((const void*)(base + rl * D + loff),
+        __builtin_amdgcn_global_load_lds((const void*)(base + rl * D + src_off(r)),
                                          (LDS_AS void*)(tile + (4 * i + w) * 512), 16, 0, 0);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < ROUNDS; ++i) {
-        const int gr = min(row0 + 4 * RW * i + rl, nrows - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)gr * D + loff),
+        const int r = 4 * RW * i + rl;
+        const int gr = min(row0 + r, nrows - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)gr * D + src_off(r)),
                                          (LDS_AS void*)(tile + (4 * i + w) * 512), 16, 0, 0);
       }
     }
