@@ -129,6 +129,7 @@ __global__ __launch_bounds__(256, 2) void fa_dq_kernel(BwdArgs a) {
     const bf16_t* Vs = odd ? sV1 : sV0;
 
     f32x16 s[NNB], dp[NNB];
+    prio_hi();
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb) {
       s[nb] = zero16();
@@ -139,6 +140,7 @@ __global__ __launch_bounds__(256, 2) void fa_dq_kernel(BwdArgs a) {
         dp[nb] = mfma32(rd.row16(Vs, nb * 32, kd), dof[kd], dp[nb]);
       }
     }
+    prio_lo();
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
@@ -160,10 +162,12 @@ __global__ __launch_bounds__(256, 2) void fa_dq_kernel(BwdArgs a) {
     bf16x8 dsf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) dsf[ks] = pack8(s[ks / 2], ks % 2);
+    prio_hi();
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) dq[db] = mfma32(rd.trA(Ks, 16 * ks, db), dsf[ks], dq[db]);
+    prio_lo();
 
     wait_vmem();
     __syncthreads();
@@ -289,11 +293,13 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     const int r0 = 32 * qhalf;  // this wave's rows within the tile
 
     f32x16 s = zero16(), dp = zero16();
+    prio_hi();
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
       s = mfma32(rd.row16(Qs, r0, kd), rd.row16(sK, 32 * kb, kd), s);
       dp = mfma32(rd.row16(Ds, r0, kd), rd.row16(sV, 32 * kb, kd), dp);
     }
+    prio_lo();
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][r0 + 8 * i4 + 4 * lg]);
@@ -315,6 +321,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     }
     const bf16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 1);
     const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 1);
+    prio_hi();
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       dv[db] = mfma32(rd.trA(Ds, r0, db), pf0, dv[db]);
@@ -322,6 +329,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
       dk[db] = mfma32(rd.trA(Qs, r0, db), ds0, dk[db]);
       dk[db] = mfma32(rd.trA(Qs, r0 + 16, db), ds1, dk[db]);
     }
+    prio_lo();
 
     if (n + 1 < niter) put_stat(buf ^ 1);
     wait_vmem();

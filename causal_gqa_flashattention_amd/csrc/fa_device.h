@@ -57,6 +57,19 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int half) {
   return r;
 }
 
+// Wave priority around matrix-core phases: a wave about to issue a run of
+// MFMAs asks the sequencer to prefer it, so a co-resident wave's vector work
+// fills the matrix-core time instead of competing with it.
+#ifndef CGQA_SETPRIO
+#define CGQA_SETPRIO 0
+#endif
+__device__ __forceinline__ void prio_hi() {
+  if (CGQA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+}
+__device__ __forceinline__ void prio_lo() {
+  if (CGQA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Exchange with the lane 32 positions away (the other half of a C column).

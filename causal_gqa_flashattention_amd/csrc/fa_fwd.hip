@@ -108,12 +108,14 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
     const bf16_t* Vs = odd ? sV1 : sV0;
 
     f32x16 s[NNB];
+    prio_hi();
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb) {
       s[nb] = zero16();
 #pragma unroll
       for (int kd = 0; kd < NKD; ++kd) s[nb] = mfma32(rd.row16(Ks, nb * 32, kd), qf[kd], s[nb]);
     }
+    prio_lo();
     if (j >= n_full) {  // diagonal or ragged tile: hide keys past the diagonal or past Lk
       __asm__ volatile("");  // keep this a real branch (not speculated into every tile)
       // key = base + crow(i, 0) is visible iff crow(i, 0) <= last - base
@@ -156,10 +158,12 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
     bf16x8 pf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) pf[ks] = pack8(s[ks / 2], ks % 2);
+    prio_hi();
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) acc[db] = mfma32(rd.trA(Vs, 16 * ks, db), pf[ks], acc[db]);
+    prio_lo();
 
     wait_vmem();
     __syncthreads();
