@@ -95,6 +95,49 @@ def load_traffic(kernel, workload):
     return None if k is None else k.get("hbm_bytes")
 
 
+COPY_MIB = [256, 1024]
+
+
+def summarize_pmc(fetch_csv, write_csv, workload):
+    """HBM bytes per kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by the factor that maps the same counter to the
+    known size of the calibration copies."""
+    import csv
+
+    def load(path, counter):
+        rows = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        return sorted(rows)
+
+    out = {"workload": workload, "source_digest": source_digest(), "kernels": {}, "calibration": {}}
+    vals = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = load(path, counter)
+        copies = [v for _, n, v in rows if "copy" in n.lower()]
+        if len(copies) != len(COPY_MIB):
+            raise SystemExit(f"expected {len(COPY_MIB)} copy dispatches in {path}, found {len(copies)}")
+        factors = [mib * 1024 / kib for mib, kib in zip(COPY_MIB, copies)]  # true KiB / counted KiB
+        factor = sum(factors) / len(factors)
+        out["calibration"][counter] = {"copy_mib": COPY_MIB, "counted_kib": copies, "factor": factor}
+        for _, n, v in rows:
+            for key, tag in (("fwd", "fa_fwd_kernel"), ("delta", "fa_delta_kernel"),
+                             ("dq", "fa_dq_kernel"), ("dkv", "fa_dkv_kernel")):
+                if tag in n:
+                    vals.setdefault(key, {})[counter] = v * factor * 1024
+    for key, d in vals.items():
+        out["kernels"][key] = {"fetch_bytes": round(d.get("FETCH_SIZE", 0.0)),
+                               "write_bytes": round(d.get("WRITE_SIZE", 0.0)),
+                               "hbm_bytes": round(d.get("FETCH_SIZE", 0.0) + d.get("WRITE_SIZE", 0.0))}
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    dst = os.path.join(PROFILE_DIR, f"traffic_{workload}.json")
+    with open(dst, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+    return 0
+
+
 # ------------------------------------------------------------ CPU oracle leg
 
 def cpu_baseline(w, bits, budget_s=30.0):
@@ -139,8 +182,14 @@ def main(argv=None):
     ap.add_argument("--workload", default="train8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
-                    help="one copy kernel of known size plus one step, for counter runs")
+                    help="copy kernels of known size plus one step, for counter runs")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --profile-pass run into profiles/traffic_<workload>.json")
     args = ap.parse_args(argv)
+
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -184,14 +233,18 @@ def main(argv=None):
             ev[4].record(stream)
 
     if args.profile_pass:
-        # a plain copy of known size (calibrates the byte counters), then one step
-        src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
+        # plain device copies of known sizes (they calibrate the byte
+        # counters), then one step of the workload
+        for mib in COPY_MIB:
+            src = torch.empty(mib * 1024 * 1024, dtype=torch.uint8, device=dev).fill_(1)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
         step()
         torch.cuda.synchronize()
-        print(json.dumps({"profile_pass": True, "copy_bytes": src.numel(), "workload": w.name}))
+        print(json.dumps({"profile_pass": True, "copy_mib": COPY_MIB, "workload": w.name}))
         return 0
 
     resident = torch.cuda.memory_allocated()
