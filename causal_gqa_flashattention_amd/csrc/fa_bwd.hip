@@ -61,10 +61,10 @@ __global__ __launch_bounds__(256, 2) void fa_dq_kernel(BwdArgs a) {
   constexpr int NNB = BN / 32;
   constexpr int NKS = BN / 16;
 
-  __shared__ __attribute__((aligned(1024))) bf16_t sK0[BN * P];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV0[BN * P];
-  __shared__ __attribute__((aligned(1024))) bf16_t sK1[BN * P];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV1[BN * P];
+  // two buffers of [K tile | V tile], BUF elements apart (a power of two)
+  constexpr int BUF = 2 * BN * P;
+  static_assert((BUF & (BUF - 1)) == 0, "buffer size must be a power of two");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -95,11 +95,12 @@ __global__ __launch_bounds__(256, 2) void fa_dq_kernel(BwdArgs a) {
   n_full = max(0, min(n_full, nkt));
 
   const TileLoader<D> ld(w, lane);
-  auto issue = [&](int j, bf16_t* kt, bf16_t* vt) {
-    ld.template load<BN>(kt, kp, j * BN, Lk, w);
-    ld.template load<BN>(vt, vp, j * BN, Lk, w);
+  auto issue = [&](int j) {
+    bf16_t* buf = smem + (j & 1) * BUF;
+    ld.template load<BN>(buf, kp, j * BN, Lk, w);
+    ld.template load<BN>(buf + BN * P, vp, j * BN, Lk, w);
   };
-  if (nkt > 0) issue(0, sK0, sV0);
+  if (nkt > 0) issue(0);
 
   bf16x8 qf[NKD], dof[NKD];
   {
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void fa_dq_kernel(BwdArgs a) {
   const float lse2 = row_ok ? a.lse[qh + qrow] * kLog2e : INFINITY;
   const float dl = row_ok ? a.delta[qh + qrow] : 0.f;
 
-  const TileReader<D> rd(lane);
+  TileReader<D> rd(lane);
   const float c2 = a.scale_log2;
   f32x16 dq[NDB];
 #pragma unroll
@@ -123,10 +124,9 @@ __global__ __launch_bounds__(256, 2) void fa_dq_kernel(BwdArgs a) {
   wait_vmem();
   __syncthreads();
   for (int j = 0; j < nkt; ++j) {
-    const bool odd = j & 1;
-    if (j + 1 < nkt) issue(j + 1, odd ? sK0 : sK1, odd ? sV0 : sV1);
-    const bf16_t* Ks = odd ? sK1 : sK0;
-    const bf16_t* Vs = odd ? sV1 : sV0;
+    if (j + 1 < nkt) issue(j + 1);
+    const bf16_t* Ks = smem;  // + (j & 1) * BUF through the reader's offsets
+    const bf16_t* Vs = smem + BN * P;
 
     f32x16 s[NNB], dp[NNB];
     prio_hi();
@@ -169,6 +169,7 @@ __global__ __launch_bounds__(256, 2) void fa_dq_kernel(BwdArgs a) {
       for (int ks = 0; ks < NKS; ++ks) dq[db] = mfma32(rd.trA(Ks, 16 * ks, db), dsf[ks], dq[db]);
     prio_lo();
 
+    rd.flip(BUF);
     wait_vmem();
     __syncthreads();
   }
@@ -210,12 +211,13 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   constexpr int NKD = D / 16;
   constexpr int NDB = D / 32;
 
-  __shared__ __attribute__((aligned(1024))) bf16_t sK[BN * P];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV[BN * P];
-  __shared__ __attribute__((aligned(1024))) bf16_t sQ0[BM * P];
-  __shared__ __attribute__((aligned(1024))) bf16_t sD0[BM * P];
-  __shared__ __attribute__((aligned(1024))) bf16_t sQ1[BM * P];
-  __shared__ __attribute__((aligned(1024))) bf16_t sD1[BM * P];
+  // two buffers of [Q tile | dO tile], BUF elements apart (a power of two),
+  // then the K and V tiles of this workgroup
+  constexpr int BUF = 2 * BM * P;
+  static_assert((BUF & (BUF - 1)) == 0, "buffer size must be a power of two");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF + 2 * BN * P];
+  bf16_t* const sK = smem + 2 * BUF;
+  bf16_t* const sV = sK + BN * P;
   __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buf][lse*log2e / delta]
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
@@ -244,7 +246,9 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   const int wl = w & 3;
   const TileLoader<D> ld(wl, lane);
   float rstat = 0.f;
-  auto issue = [&](int n, bf16_t* qt_lds, bf16_t* dt_lds) {
+  auto issue = [&](int n) {
+    bf16_t* qt_lds = smem + (n & 1) * BUF;
+    bf16_t* dt_lds = qt_lds + BM * P;
     const int hi = n / nq, qtile = qt_first + (n - (n / nq) * nq);
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
     const int qbase = qtile * BM;
@@ -269,11 +273,11 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   else
     ld.template load<BN>(sV, a.v + kvh * D, k0, Lk, wl);
   if (niter > 0) {
-    issue(0, sQ0, sD0);
+    issue(0);
     put_stat(0);
   }
 
-  const TileReader<D> rd(lane);
+  TileReader<D> rd(lane);
   const float c2 = a.scale_log2;
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -287,9 +291,11 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   for (int n = 0; n < niter; ++n) {
     const int buf = n & 1;
     const int q0 = (qt_first + (n - (n / nq) * nq)) * BM;
-    if (n + 1 < niter) issue(n + 1, buf ? sQ0 : sQ1, buf ? sD0 : sD1);
-    const bf16_t* Qs = buf ? sQ1 : sQ0;
-    const bf16_t* Ds = buf ? sD1 : sD0;
+    if (n + 1 < niter) issue(n + 1);
+    const bf16_t* Qs = smem + buf * BUF;   // row reads: explicit buffer base
+    const bf16_t* Ds = Qs + BM * P;
+    const bf16_t* Qt = smem;               // transposed reads: + buf * BUF via the
+    const bf16_t* Dt = smem + BM * P;      // reader's flipped offsets
     const int r0 = 32 * qhalf;  // this wave's rows within the tile
 
     f32x16 s = zero16(), dp = zero16();
@@ -324,22 +330,23 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     prio_hi();
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      dv[db] = mfma32(rd.trA(Ds, r0, db), pf0, dv[db]);
-      dv[db] = mfma32(rd.trA(Ds, r0 + 16, db), pf1, dv[db]);
-      dk[db] = mfma32(rd.trA(Qs, r0, db), ds0, dk[db]);
-      dk[db] = mfma32(rd.trA(Qs, r0 + 16, db), ds1, dk[db]);
+      dv[db] = mfma32(rd.trA(Dt, r0, db), pf0, dv[db]);
+      dv[db] = mfma32(rd.trA(Dt, r0 + 16, db), pf1, dv[db]);
+      dk[db] = mfma32(rd.trA(Qt, r0, db), ds0, dk[db]);
+      dk[db] = mfma32(rd.trA(Qt, r0 + 16, db), ds1, dk[db]);
     }
     prio_lo();
 
     if (n + 1 < niter) put_stat(buf ^ 1);
+    rd.flip_tr(BUF);
     wait_vmem();
     __syncthreads();
   }
 
   // ---- add the two row halves: waves 4-7 hand their partials to waves 0-3
   // through LDS (the tile buffers are free now), lane-contiguous per register
-  float* red = reinterpret_cast<float*>(sK);  // sK + sV: 2 * BN * P bf16 >= 4 waves * NDB*16*64 floats
-  static_assert(2 * BN * P * 2 >= 4 * NDB * 16 * 64 * 4, "reduction buffer too small");
+  float* red = reinterpret_cast<float*>(smem);
+  static_assert((2 * BUF + 2 * BN * P) * 2 >= 4 * NDB * 16 * 64 * 4, "reduction buffer too small");
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     f32x16* acc = pass == 0 ? dk : dv;

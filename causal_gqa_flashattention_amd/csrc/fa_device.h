@@ -133,12 +133,12 @@ struct TileReader {
   static constexpr int P = T::P;
   static constexpr int NRA = (D / 16) < 8 ? (D / 16) : 8;
   static constexpr int NTR = (D / 32) < 4 ? (D / 32) : 4;
-  int ra[NRA];
-  int tr[2][NTR];
+  int ra[NRA];      // byte offsets
+  int tr[2][NTR];   // byte offsets
   __device__ __forceinline__ explicit TileReader(int lane) {
     const int lr = lane & 31, lg = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < NRA; ++j) ra[j] = lr * P + (((2 * j + lg) ^ T::swz(lr)) << 3);
+    for (int j = 0; j < NRA; ++j) ra[j] = 2 * (lr * P + (((2 * j + lg) ^ T::swz(lr)) << 3));
     // transposed read: lane addresses row rl (+8), chunk 4*db + y, 8-byte half `within`
     const int rl = 4 * (lane >> 5) + ((lane >> 2) & 3);
     const int y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
@@ -147,14 +147,30 @@ struct TileReader {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int dm = 0; dm < NTR; ++dm)
-        tr[h][dm] = (rl + 8 * h) * P + (((4 * dm + y) ^ T::swz(rl + 8 * h)) << 3) + within;
+        tr[h][dm] = 2 * ((rl + 8 * h) * P + (((4 * dm + y) ^ T::swz(rl + 8 * h)) << 3) + within);
+  }
+  // Move every offset to the other half of a double buffer whose halves sit
+  // `half` elements apart (`half` a power of two above every offset used):
+  // one XOR per register per tile instead of an address add per read.
+  __device__ __forceinline__ void flip(int half) {
+#pragma unroll
+    for (int j = 0; j < NRA; ++j) ra[j] ^= 2 * half;
+    flip_tr(half);
+  }
+  __device__ __forceinline__ void flip_tr(int half) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dm = 0; dm < NTR; ++dm) tr[h][dm] ^= 2 * half;
   }
   __device__ __forceinline__ bf16x8 row16(const bf16_t* tile, int r0, int kd) const {
-    return lds_read16(tile + r0 * P + ra[kd % NRA] + 128 * (kd / NRA));
+    const char* p = reinterpret_cast<const char*>(tile + r0 * P + 128 * (kd / NRA)) + ra[kd % NRA];
+    return lds_read16(reinterpret_cast<const bf16_t*>(p));
   }
   __device__ __forceinline__ bf16x8 trA(const bf16_t* tile, int r0, int db) const {
-    const bf16_t* p = tile + r0 * P + 128 * (db / NTR);
-    return cat8(lds_read_tr4(p + tr[0][db % NTR]), lds_read_tr4(p + tr[1][db % NTR]));
+    const char* p = reinterpret_cast<const char*>(tile + r0 * P + 128 * (db / NTR));
+    return cat8(lds_read_tr4(reinterpret_cast<const bf16_t*>(p + tr[0][db % NTR])),
+                lds_read_tr4(reinterpret_cast<const bf16_t*>(p + tr[1][db % NTR])));
   }
 };
 

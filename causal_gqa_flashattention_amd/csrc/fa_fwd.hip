@@ -41,10 +41,10 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
   constexpr int NKS = BN / 16;     // 16-key k steps per key tile
   constexpr float kSlack = 8.f;
 
-  __shared__ __attribute__((aligned(1024))) bf16_t sK0[BN * P];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV0[BN * P];
-  __shared__ __attribute__((aligned(1024))) bf16_t sK1[BN * P];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV1[BN * P];
+  // two buffers of [K tile | V tile], BUF elements apart (a power of two)
+  constexpr int BUF = 2 * BN * P;
+  static_assert((BUF & (BUF - 1)) == 0, "buffer size must be a power of two");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -77,11 +77,12 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
   n_full = max(0, min(n_full, nkt));
 
   const TileLoader<D> ld(w, lane);
-  auto issue = [&](int j, bf16_t* kt, bf16_t* vt) {
-    ld.template load<BN>(kt, kp, j * BN, Lk, w);
-    ld.template load<BN>(vt, vp, j * BN, Lk, w);
+  auto issue = [&](int j) {
+    bf16_t* buf = smem + (j & 1) * BUF;
+    ld.template load<BN>(buf, kp, j * BN, Lk, w);
+    ld.template load<BN>(buf + BN * P, vp, j * BN, Lk, w);
   };
-  if (nkt > 0) issue(0, sK0, sV0);
+  if (nkt > 0) issue(0);
 
   // ---- Q^T operand (B): lane holds query qrow, head-dim slots 16*kd + 8*lg + s
   bf16x8 qf[NKD];
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
     for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qr * D + 16 * kd + 8 * lg));
   }
 
-  const TileReader<D> rd(lane);
+  TileReader<D> rd(lane);  // offsets point into buffer (j & 1); flipped every tile
   const float c2 = a.scale_log2;
   float m_run = -INFINITY;  // max (exp2 units) the accumulator is scaled with
   float l_run = 0.f;        // this lane's share of the running denominator
@@ -102,10 +103,9 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
   wait_vmem();
   __syncthreads();
   for (int j = 0; j < nkt; ++j) {
-    const bool odd = j & 1;
-    if (j + 1 < nkt) issue(j + 1, odd ? sK0 : sK1, odd ? sV0 : sV1);
-    const bf16_t* Ks = odd ? sK1 : sK0;
-    const bf16_t* Vs = odd ? sV1 : sV0;
+    if (j + 1 < nkt) issue(j + 1);
+    const bf16_t* Ks = smem;           // + (j & 1) * BUF through the reader's offsets
+    const bf16_t* Vs = smem + BN * P;
 
     f32x16 s[NNB];
     prio_hi();
@@ -165,6 +165,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
       for (int ks = 0; ks < NKS; ++ks) acc[db] = mfma32(rd.trA(Vs, 16 * ks, db), pf[ks], acc[db]);
     prio_lo();
 
+    rd.flip(BUF);
     wait_vmem();
     __syncthreads();
   }
