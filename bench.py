@@ -283,8 +283,11 @@ def main(argv=None):
                 "traffic": load_traffic(dom, w.name),
                 "flop_per_launch": work[dom], "avg_launch_ms": round(per[dom], 4)}
 
+    metric = METRIC if w.name == "train8k" else (
+        f"fwd+bwd TFLOP/s, {'causal' if w.causal else 'dense'} GQA bf16 attention D={w.D} "
+        f"Lq={w.Lq} Lk={w.Lk}; % of MFMA peak")
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

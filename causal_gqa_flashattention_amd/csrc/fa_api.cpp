@@ -6,8 +6,9 @@
 // typed errors; runtime rather than debug-only shape/stride checks and the
 // null-buffer check: page "feat(attention): complete Flash Attention VJP
 // implementation", review-comment resolutions).  Supported head dimensions:
-// 64, 96, 128 and 256 for the forward; 64, 96 and 128 for the backward (the
-// same set the VJP page's backward supports).
+// 64, 96, 128 and 256, forward and backward (the VJP page's Metal backward
+// stops at 128 for a 32 KB threadgroup-memory limit that gfx950's 160 KB LDS
+// does not have).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -23,7 +24,7 @@ constexpr int kDqBM = 128;    // query rows per dQ workgroup
 constexpr int kDkvBN = 128;   // keys per dK/dV workgroup
 
 bool fwd_head_dim_ok(int D) { return D == 64 || D == 96 || D == 128 || D == 256; }
-bool bwd_head_dim_ok(int D) { return D == 64 || D == 96 || D == 128; }
+bool bwd_head_dim_ok(int D) { return D == 64 || D == 96 || D == 128 || D == 256; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

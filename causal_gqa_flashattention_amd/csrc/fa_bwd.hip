@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void fa_delta_kernel(DeltaArgs a) {
 //   dS^T = P^T * (dP^T - delta)
 //   dQ^T += K^T dS^T    (A = K^T by transposed LDS reads, B = dS^T)
 template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fa_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs a) {
   constexpr int BM = 128;
   constexpr int P = Tile<D>::P;
   constexpr int NKD = D / 16;
@@ -386,6 +386,159 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- dK / dV, wide heads
+// Head dim 256: the dK/dV accumulators of 32 keys take 256 registers per
+// wavefront, so two wavefronts cannot share a SIMD.  One workgroup = 4
+// wavefronts = 128 keys, one wavefront per SIMD; each wavefront owns 32 keys
+// for all rows, keeps its K and V operand fragments in registers, and query
+// tiles of 32 rows of Q and dO (with LSE and delta) stream through LDS,
+// double buffered.  Per query tile the products are those of fa_dkv_kernel.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
+  constexpr int BN = 128;   // keys per workgroup
+  constexpr int BM = 32;    // query rows per tile
+  constexpr int P = Tile<D>::P;
+  constexpr int NKD = D / 16;
+  constexpr int NDB = D / 32;
+
+  constexpr int BUF = 2 * BM * P;  // [Q tile | dO tile]
+  static_assert((BUF & (BUF - 1)) == 0, "buffer size must be a power of two");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buf][lse*log2e / delta]
+
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = a.G;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / a.nkt;
+  const int kt = logical - bh * a.nkt;
+  const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
+  const int Lq = a.Lq, Lk = a.Lk, off = a.off;
+
+  const int64_t kvh = (int64_t)(b * a.Hkv + hk) * Lk;
+  const int k0 = kt * BN;
+  const int krow = k0 + 32 * w + lr;
+  const bool key_ok = krow < Lk;
+
+  const int qfirst = CAUSAL ? max(0, k0 - off) : 0;
+  const int qt_first = qfirst / BM;
+  const int nqt = (Lq + BM - 1) / BM;
+  const int nq = max(0, nqt - qt_first);
+  const int niter = G * nq;
+
+  const TileLoader<D> ld(w, lane);
+  float rstat = 0.f;
+  auto issue = [&](int n) {
+    bf16_t* qt_lds = smem + (n & 1) * BUF;
+    const int hi = n / nq, qtile = qt_first + (n - (n / nq) * nq);
+    const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
+    const int qbase = qtile * BM;
+    ld.template load<BM>(qt_lds, a.q + qh * D, qbase, Lq, w);
+    ld.template load<BM>(qt_lds + BM * P, a.dO + qh * D, qbase, Lq, w);
+    if (tid < 2 * BM) {
+      const int qr = qbase + (tid % BM);
+      if (tid < BM)
+        rstat = qr < Lq ? a.lse[qh + qr] * kLog2e : INFINITY;  // +inf: P = 0 on padded rows
+      else
+        rstat = qr < Lq ? a.delta[qh + qr] : 0.f;
+    }
+  };
+  auto put_stat = [&](int buf) {
+    if (tid < 2 * BM) stat[buf][tid / BM][tid % BM] = rstat;
+  };
+  if (niter > 0) {
+    issue(0);
+    put_stat(0);
+  }
+
+  bf16x8 kf[NKD], vf[NKD];
+  {
+    const int kr = min(krow, Lk - 1);  // keys past Lk: a copy, never stored
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) {
+      kf[kd] = as_bf16x8(ldg16(a.k + (kvh + kr) * D + 16 * kd + 8 * lg));
+      vf[kd] = as_bf16x8(ldg16(a.v + (kvh + kr) * D + 16 * kd + 8 * lg));
+    }
+  }
+
+  TileReader<D> rd(lane);
+  const float c2 = a.scale_log2;
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+
+  wait_vmem();
+  __syncthreads();
+  for (int n = 0; n < niter; ++n) {
+    const int buf = n & 1;
+    const int q0 = (qt_first + (n - (n / nq) * nq)) * BM;
+    if (n + 1 < niter) issue(n + 1);
+    const bf16_t* Qs = smem;  // + buf * BUF through the reader's flipped offsets
+    const bf16_t* Ds = smem + BM * P;
+
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) {
+      s = mfma32(rd.row16(Qs, 0, kd), kf[kd], s);
+      dp = mfma32(rd.row16(Ds, 0, kd), vf[kd], dp);
+    }
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][8 * i4 + 4 * lg]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fast_exp2(fmaf(s[4 * i4 + e], c2, -l4[e]));
+    }
+    if (CAUSAL && k0 + BN - 1 > q0 + off) {  // tile crosses the diagonal
+      __asm__ volatile("");
+      const int thr = krow - off - q0 - 4 * lg;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = (crow(i, 0) >= thr) ? s[i] : 0.f;
+    }
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][8 * i4 + 4 * lg]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = s[4 * i4 + e] * (dp[4 * i4 + e] - d4[e]);
+    }
+    const bf16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 1);
+    const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 1);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      dv[db] = mfma32(rd.trA(Ds, 0, db), pf0, dv[db]);
+      dv[db] = mfma32(rd.trA(Ds, 16, db), pf1, dv[db]);
+      dk[db] = mfma32(rd.trA(Qs, 0, db), ds0, dk[db]);
+      dk[db] = mfma32(rd.trA(Qs, 16, db), ds1, dk[db]);
+    }
+
+    if (n + 1 < niter) put_stat(buf ^ 1);
+    rd.flip(BUF);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  if (key_ok) {
+    bf16_t* dkp = a.dk + (kvh + krow) * D;
+    bf16_t* dvp = a.dv + (kvh + krow) * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 k4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = (__bf16)(dk[db][4 * q4 + e] * sc);
+          v4[e] = (__bf16)(dv[db][4 * q4 + e]);
+        }
+        *reinterpret_cast<bf16x4*>(dkp + 32 * db + 8 * q4 + 4 * lg) = k4;
+        *reinterpret_cast<bf16x4*>(dvp + 32 * db + 8 * q4 + 4 * lg) = v4;
+      }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t stream) {
@@ -410,10 +563,20 @@ static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int which, hipStre
   const int ndkv = (which & 2) ? a.B * a.Hkv * a.nkt : 0;
   if (causal) {
     if (ndq > 0) hipLaunchKernelGGL((fa_dq_kernel<D, BN_Q, true>), dim3(ndq), dim3(256), 0, stream, a);
-    if (ndkv > 0) hipLaunchKernelGGL((fa_dkv_kernel<D, true>), dim3(ndkv), dim3(512), 0, stream, a);
+    if (ndkv > 0) {
+      if constexpr (D > 128)
+        hipLaunchKernelGGL((fa_dkv_reg_kernel<D, true>), dim3(ndkv), dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((fa_dkv_kernel<D, true>), dim3(ndkv), dim3(512), 0, stream, a);
+    }
   } else {
     if (ndq > 0) hipLaunchKernelGGL((fa_dq_kernel<D, BN_Q, false>), dim3(ndq), dim3(256), 0, stream, a);
-    if (ndkv > 0) hipLaunchKernelGGL((fa_dkv_kernel<D, false>), dim3(ndkv), dim3(512), 0, stream, a);
+    if (ndkv > 0) {
+      if constexpr (D > 128)
+        hipLaunchKernelGGL((fa_dkv_reg_kernel<D, false>), dim3(ndkv), dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((fa_dkv_kernel<D, false>), dim3(ndkv), dim3(512), 0, stream, a);
+    }
   }
   return hipGetLastError();
 }
@@ -423,6 +586,7 @@ hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, hipStream
     case 64: return launch_bwd_d<64, 64>(a, causal, which, stream);
     case 96: return launch_bwd_d<96, 64>(a, causal, which, stream);
     case 128: return launch_bwd_d<128, 64>(a, causal, which, stream);
+    case 256: return launch_bwd_d<256, 32>(a, causal, which, stream);
     default: return hipErrorInvalidValue;
   }
 }

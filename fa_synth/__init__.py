@@ -84,6 +84,7 @@ WORKLOADS = {
     "d256_4064x4096": AttnShape("d256_4064x4096", 1, 16, 2, 4064, 4096, 256, True, seed=4100, scale=1.0 / 16, backward=False),
     "d256_8200": AttnShape("d256_8200", 1, 16, 2, 8200, 8200, 256, True, seed=4200, scale=1.0 / 16, backward=False),
     "long23k": AttnShape("long23k", 1, 32, 8, 23040, 23040, 128, True, seed=5000),
+    "d256_train8k": AttnShape("d256_train8k", 1, 16, 2, 8192, 8192, 256, True, seed=6000, scale=1.0 / 16),
 }
 
 

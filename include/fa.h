@@ -44,8 +44,7 @@
  * FA_ERR_LAUNCH.  Sizes:
  *   B, Hq, Hkv, Lq, Lk >= 0 and < 2^31; B*H*L*D element counts must fit
  *   in int64; Hq % Hkv == 0 (Hkv >= 1 when Hq >= 1);
- *   D in {64, 96, 128, 256} for fa_fwd and fa_bwd_delta,
- *   D in {64, 96, 128} for fa_bwd;
+ *   D in {64, 96, 128, 256} for every call;
  *   causal requires Lq <= Lk (otherwise the first rows see no key);
  *   Lk == 0 with Lq > 0 is rejected (softmax over no keys).
  * Empty problems (B == 0, Hq == 0, or Lq == 0) are valid no-ops, except that

@@ -70,7 +70,7 @@ def test_empty_forward_is_ok_without_pointers(lib):
 
 def test_bwd_validation(lib):
     a = [P] * 10
-    assert lib.fa_bwd(*a, 1, 2, 1, 8, 8, 256, 0.1, 1, None) == 4   # no D=256 backward
+    assert lib.fa_bwd(*a, 1, 2, 1, 8, 8, 80, 0.1, 1, None) == 4    # unsupported head dim
     assert lib.fa_bwd(*a, 1, 4, 3, 8, 8, 64, 0.1, 1, None) == 5
     assert lib.fa_bwd(*a, 1, 2, 1, 9, 8, 64, 0.1, 1, None) == 6
     bad = list(a)

@@ -117,6 +117,11 @@ def test_head_dim_256_forward(Lq, Lk, causal):
     run_case(1, 4, 2, Lq, Lk, 256, causal, seed=7700 + Lq, backward=False)
 
 
+@pytest.mark.parametrize("Lq,Lk,causal", [(300, 300, True), (200, 520, True), (257, 100, False), (33, 33, True)])
+def test_head_dim_256_backward(Lq, Lk, causal):
+    run_case(1, 4, 2, Lq, Lk, 256, causal, seed=7750 + Lq)
+
+
 # ---------------------------------------------------------------- structure
 
 def test_bitwise_repeatable():
@@ -138,7 +143,7 @@ def _guarded(shape, dtype, fill):
     return buf, buf[pad:pad + n].view(shape), pad
 
 
-@pytest.mark.parametrize("D,backward", [(64, True), (128, True), (96, True), (256, False)])
+@pytest.mark.parametrize("D,backward", [(64, True), (128, True), (96, True), (256, True)])
 def test_guard_bands_and_nan_poison(D, backward):
     """Inputs sit between NaN guard bands (an out-of-bounds read would make
     NaN appear in the outputs); outputs sit between sentinel guard bands that
@@ -199,13 +204,17 @@ def test_empty_problems():
 
 def test_typed_errors_on_device():
     import causal_gqa_flashattention_amd as fa
-    q = to_gpu(normal_bf16_bits((1, 2, 8, 256), 1))
-    o, lse = fa.fa_fwd(q, q[:, :1].contiguous(), q[:, :1].contiguous(), scale=0.0625, causal=True)
+    q = to_gpu(normal_bf16_bits((1, 2, 8, 80), 1))
+    kv = q[:, :1].contiguous()
     with pytest.raises(fa.FAError) as e:
-        fa.fa_bwd(q, q[:, :1].contiguous(), q[:, :1].contiguous(), o, lse, lse, q, scale=0.0625, causal=True)
-    assert e.value.status == 4  # FA_ERR_HEAD_DIM: the backward stops at D = 128
+        fa.fa_fwd(q, kv, kv, scale=0.1, causal=True)
+    assert e.value.status == 4  # FA_ERR_HEAD_DIM
     q = to_gpu(normal_bf16_bits((1, 2, 9, 64), 1))
     k = to_gpu(normal_bf16_bits((1, 1, 8, 64), 2))
     with pytest.raises(fa.FAError) as e:
         fa.fa_fwd(q, k, k, scale=0.125, causal=True)
     assert e.value.status == 6  # causal needs Lq <= Lk
+    lse = torch.zeros((1, 2, 9), dtype=torch.float32, device="cuda")
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_bwd(q, k, k, None, lse, lse, q, scale=0.125, causal=True)
+    assert e.value.status == 6

@@ -149,3 +149,28 @@ def test_long23k_sampled_and_identities():
     dos = g["do"].float().reshape(w.B, w.Hkv, G, w.Lq, w.D).sum(dim=(2, 3))
     err = (dvs - dos).abs().max().item()
     assert err <= 1e-2 * dv.float().abs().sum(dim=2).max().item(), err
+
+
+def test_d256_fwd_bwd_sampled():
+    """Head dim 256 forward + backward at 8192 tokens (16/2 heads, causal):
+    sampled rows of one group for O, LSE, dQ and the last 512 keys' dK/dV."""
+    w, bits, g, out = run_workload("d256_train8k")
+    G = w.Hq // w.Hkv
+    kvh = 1
+    k = oracle.bf16_bits_to_f64(bits["k"][0, kvh])
+    v = oracle.bf16_bits_to_f64(bits["v"][0, kvh])
+    rows = sample_rows(w.Lq, 128, seed=w.seed, tile=128)
+    tail = np.arange(w.Lq - 512, w.Lq)
+    dk_tail = np.zeros((512, w.D))
+    dv_tail = np.zeros((512, w.D))
+    for h in range(kvh * G, (kvh + 1) * G):
+        q = oracle.bf16_bits_to_f64(bits["q"][0, h])
+        do = oracle.bf16_bits_to_f64(bits["do"][0, h])
+        r = oracle.head_backward(q, k, v, do, w.softmax_scale, True, rows=rows)
+        for n in ("o", "lse", "dq"):
+            check(n, to_f64(out[n][0, h, rows]), r[n], f"d256_train8k head {h}")
+        rt = oracle.head_backward(q, k, v, do, w.softmax_scale, True, rows=tail, key_rows=tail)
+        dk_tail += rt["dk"]
+        dv_tail += rt["dv"]
+    check("dk", to_f64(out["dk"][0, kvh, tail]), dk_tail, f"d256_train8k kv head {kvh} last 512 keys")
+    check("dv", to_f64(out["dv"][0, kvh, tail]), dv_tail, f"d256_train8k kv head {kvh} last 512 keys")
