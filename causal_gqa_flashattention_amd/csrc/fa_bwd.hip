@@ -253,9 +253,9 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
     const int qbase = qtile * BM;
     if (w < 4)
-      ld.template load<BM>(qt_lds, a.q + qh * D, qbase, Lq, wl);
+      ld.template load<BM, false>(qt_lds, a.q + qh * D, qbase, Lq, wl);
     else
-      ld.template load<BM>(dt_lds, a.dO + qh * D, qbase, Lq, wl);
+      ld.template load<BM, false>(dt_lds, a.dO + qh * D, qbase, Lq, wl);
     if (tid < 2 * BM) {
       const int qr = qbase + (tid % BM);
       if (tid < BM)
@@ -269,9 +269,9 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   };
   // K and V of this key tile, once (rows past Lk repeat the last key)
   if (w < 4)
-    ld.template load<BN>(sK, a.k + kvh * D, k0, Lk, wl);
+    ld.template load<BN, false>(sK, a.k + kvh * D, k0, Lk, wl);
   else
-    ld.template load<BN>(sV, a.v + kvh * D, k0, Lk, wl);
+    ld.template load<BN, false>(sV, a.v + kvh * D, k0, Lk, wl);
   if (niter > 0) {
     issue(0);
     put_stat(0);

@@ -193,28 +193,53 @@ struct TileLoader {
   // Rows row0 .. row0+ROWS-1 of `g` (row stride D).  Rows at or past `nrows`
   // repeat row nrows-1, which keeps every value finite; kernels mask them.
   // Each wave issues ROWS*PC/256 loads of 64 x 16 bytes; the caller waits on
-  // vmcnt and synchronises before reading.
-  template <int ROWS>
+  // vmcnt and synchronises before reading.  ASM issues them as inline
+  // assembly (see lds_dma16); without it they go through the compiler's
+  // builtin, which makes every later LDS read wait for them.
+  template <int ROWS, bool ASM = true>
   __device__ __forceinline__ void load(bf16_t* tile, const bf16_t* g, int row0, int nrows, int w) const {
     constexpr int ROUNDS = ROWS * PC / 256;
     static_assert(ROWS * PC % 256 == 0, "tile must split evenly over four waves");
     if (row0 + ROWS <= nrows) {
+      // whole tile: the per-lane offsets do not depend on the tile, so they
+      // stay in registers across the loop; the row step goes in the scalar base
 #pragma unroll
       for (int i = 0; i < ROUNDS; ++i) {
         const int r = 4 * RW * i + rl;
         const bf16_t* base = g + (int64_t)(row0 + 4 * RW * i) * D;  // wave-uniform
-        __builtin_amdgcn_global_load_lds((const void*)(base + rl * D + src_off(r)),
-                                         (LDS_AS void*)(tile + (4 * i + w) * 512), 16, 0, 0);
+        if constexpr (ASM)
+          lds_dma16(tile + (4 * i + w) * 512, base, (uint32_t)(rl * D + src_off(r)) * 2u);
+        else
+          __builtin_amdgcn_global_load_lds((const void*)(base + rl * D + src_off(r)),
+                                           (LDS_AS void*)(tile + (4 * i + w) * 512), 16, 0, 0);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < ROUNDS; ++i) {
         const int r = 4 * RW * i + rl;
-        const int gr = min(row0 + r, nrows - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)gr * D + src_off(r)),
-                                         (LDS_AS void*)(tile + (4 * i + w) * 512), 16, 0, 0);
+        if constexpr (ASM) {
+          const int last = nrows - 1 - row0;  // last tile row that exists
+          lds_dma16(tile + (4 * i + w) * 512, g + (int64_t)row0 * D,
+                    (uint32_t)(min(r, last) * D + src_off(r)) * 2u);
+        } else {
+          const int gr = min(row0 + r, nrows - 1);
+          __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)gr * D + src_off(r)),
+                                           (LDS_AS void*)(tile + (4 * i + w) * 512), 16, 0, 0);
+        }
       }
     }
+  }
+
+  // One global_load_lds_dwordx4: lane l's 16 bytes at sbase + voff go to LDS
+  // address dst + 16*l (dst and sbase wave-uniform).  Issued as inline
+  // assembly so that the compiler does not treat the load as a write to LDS
+  // that every later LDS read must wait for: the kernels read the other
+  // buffer meanwhile and wait (vmcnt) and synchronise before reading this one.
+  __device__ __forceinline__ static void lds_dma16(bf16_t* dst, const bf16_t* sbase, uint32_t voff) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(LDS_AS void*)(dst));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(m0v), "v"(voff), "s"(sbase) : "memory");
   }
 };
 
