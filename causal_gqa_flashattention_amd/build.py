@@ -28,8 +28,18 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-file scheduler choice.  The backward kernels run two 256-register
+# waves per SIMD; LLVM's default scheduler keeps enough LDS reads in flight
+# there to spill, and every spill reload then waits on the vector-memory
+# counter behind the in-flight tile loads.  The occupancy-first iterative
+# strategy schedules them without spills.
+FILE_FLAGS = {
+    "fa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-maxocc"],
+}
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [_hipcc(), *HIP_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

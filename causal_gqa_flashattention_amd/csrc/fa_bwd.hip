@@ -14,6 +14,8 @@
 // looping over key blocks; dK/dV grid over key blocks and key/value heads,
 // looping over the group, then over query blocks).  The scale of dS is
 // applied once to the finished dQ and dK.
+#include <climits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF + 2 * BN * P];
   bf16_t* const sK = smem + 2 * BUF;
   bf16_t* const sV = sK + BN * P;
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buf][lse*log2e / delta]
+  __shared__ __attribute__((aligned(16))) float stat[2][2][64];  // [buf][lse / delta][row]
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -245,7 +247,8 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   // the 8 waves load as two groups of four: waves 0-3 fill Q, waves 4-7 fill dO
   const int wl = w & 3;
   const TileLoader<D> ld(wl, lane);
-  float rstat = 0.f;
+  // every load of the loop is a direct global->LDS load: Q, dO and the rows'
+  // LSE (wave 0) and delta (wave 4), rows past Lq repeating the last row
   auto issue = [&](int n) {
     bf16_t* qt_lds = smem + (n & 1) * BUF;
     bf16_t* dt_lds = qt_lds + BM * P;
@@ -253,29 +256,18 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
     const int qbase = qtile * BM;
     if (w < 4)
-      ld.template load<BM, false>(qt_lds, a.q + qh * D, qbase, Lq, wl);
+      ld.template load<BM>(qt_lds, a.q + qh * D, qbase, Lq, wl);
     else
-      ld.template load<BM, false>(dt_lds, a.dO + qh * D, qbase, Lq, wl);
-    if (tid < 2 * BM) {
-      const int qr = qbase + (tid % BM);
-      if (tid < BM)
-        rstat = qr < Lq ? a.lse[qh + qr] * kLog2e : INFINITY;  // +inf: P = 0 on padded rows
-      else
-        rstat = qr < Lq ? a.delta[qh + qr] : 0.f;
-    }
-  };
-  auto put_stat = [&](int buf) {
-    if (tid < 2 * BM) stat[buf][tid / BM][tid % BM] = rstat;
+      ld.template load<BM>(dt_lds, a.dO + qh * D, qbase, Lq, wl);
+    if (w == 0) load_row_stat(&stat[n & 1][0][0], a.lse + qh, qbase, Lq, lane);
+    if (w == 4) load_row_stat(&stat[n & 1][1][0], a.delta + qh, qbase, Lq, lane);
   };
   // K and V of this key tile, once (rows past Lk repeat the last key)
   if (w < 4)
-    ld.template load<BN, false>(sK, a.k + kvh * D, k0, Lk, wl);
+    ld.template load<BN>(sK, a.k + kvh * D, k0, Lk, wl);
   else
-    ld.template load<BN, false>(sV, a.v + kvh * D, k0, Lk, wl);
-  if (niter > 0) {
-    issue(0);
-    put_stat(0);
-  }
+    ld.template load<BN>(sV, a.v + kvh * D, k0, Lk, wl);
+  if (niter > 0) issue(0);
 
   TileReader<D> rd(lane);
   const float c2 = a.scale_log2;
@@ -310,14 +302,17 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     for (int i4 = 0; i4 < 4; ++i4) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][r0 + 8 * i4 + 4 * lg]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fast_exp2(fmaf(s[4 * i4 + e], c2, -l4[e]));
+      for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fast_exp2(fmaf(s[4 * i4 + e], c2, l4[e] * -kLog2e));
     }
-    if (CAUSAL && k0 + BN - 1 > q0 + off) {  // tile crosses the diagonal
+    // tiles that cross the diagonal or hold rows past Lq
+    if ((CAUSAL && k0 + BN - 1 > q0 + off) || q0 + BM > Lq) {
       __asm__ volatile("");
-      // key krow is visible to row q0 + r0 + crow(i, lg) iff crow(i, 0) >= thr
-      const int thr = krow - off - q0 - r0 - 4 * lg;
+      // key krow is visible to row q0 + r0 + crow(i, lg) iff crow(i, 0) >= thr,
+      // and that row exists iff crow(i, 0) < rlim
+      const int thr = CAUSAL ? krow - off - q0 - r0 - 4 * lg : INT_MIN;
+      const int rlim = Lq - q0 - r0 - 4 * lg;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = (crow(i, 0) >= thr) ? s[i] : 0.f;
+      for (int i = 0; i < 16; ++i) s[i] = (crow(i, 0) >= thr && crow(i, 0) < rlim) ? s[i] : 0.f;
     }
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
@@ -337,7 +332,6 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     }
     prio_lo();
 
-    if (n + 1 < niter) put_stat(buf ^ 1);
     rd.flip_tr(BUF);
     wait_vmem();
     __syncthreads();
@@ -404,7 +398,7 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   constexpr int BUF = 2 * BM * P;  // [Q tile | dO tile]
   static_assert((BUF & (BUF - 1)) == 0, "buffer size must be a power of two");
   __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF];
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buf][lse*log2e / delta]
+  __shared__ __attribute__((aligned(16))) float stat[2][2][64];  // [buf][lse / delta][row]
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -427,7 +421,8 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   const int niter = G * nq;
 
   const TileLoader<D> ld(w, lane);
-  float rstat = 0.f;
+  // Q, dO and the rows' LSE (wave 0) and delta (wave 1) by direct loads; the
+  // stat loads fill 64 rows, the first BM of which belong to the tile
   auto issue = [&](int n) {
     bf16_t* qt_lds = smem + (n & 1) * BUF;
     const int hi = n / nq, qtile = qt_first + (n - (n / nq) * nq);
@@ -435,21 +430,10 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     const int qbase = qtile * BM;
     ld.template load<BM>(qt_lds, a.q + qh * D, qbase, Lq, w);
     ld.template load<BM>(qt_lds + BM * P, a.dO + qh * D, qbase, Lq, w);
-    if (tid < 2 * BM) {
-      const int qr = qbase + (tid % BM);
-      if (tid < BM)
-        rstat = qr < Lq ? a.lse[qh + qr] * kLog2e : INFINITY;  // +inf: P = 0 on padded rows
-      else
-        rstat = qr < Lq ? a.delta[qh + qr] : 0.f;
-    }
+    if (w == 0) load_row_stat(&stat[n & 1][0][0], a.lse + qh, qbase, Lq, lane);
+    if (w == 1) load_row_stat(&stat[n & 1][1][0], a.delta + qh, qbase, Lq, lane);
   };
-  auto put_stat = [&](int buf) {
-    if (tid < 2 * BM) stat[buf][tid / BM][tid % BM] = rstat;
-  };
-  if (niter > 0) {
-    issue(0);
-    put_stat(0);
-  }
+  if (niter > 0) issue(0);
 
   bf16x8 kf[NKD], vf[NKD];
   {
@@ -489,13 +473,15 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     for (int i4 = 0; i4 < 4; ++i4) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][8 * i4 + 4 * lg]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fast_exp2(fmaf(s[4 * i4 + e], c2, -l4[e]));
+      for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fast_exp2(fmaf(s[4 * i4 + e], c2, l4[e] * -kLog2e));
     }
-    if (CAUSAL && k0 + BN - 1 > q0 + off) {  // tile crosses the diagonal
+    // tiles that cross the diagonal or hold rows past Lq
+    if ((CAUSAL && k0 + BN - 1 > q0 + off) || q0 + BM > Lq) {
       __asm__ volatile("");
-      const int thr = krow - off - q0 - 4 * lg;
+      const int thr = CAUSAL ? krow - off - q0 - 4 * lg : INT_MIN;
+      const int rlim = Lq - q0 - 4 * lg;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = (crow(i, 0) >= thr) ? s[i] : 0.f;
+      for (int i = 0; i < 16; ++i) s[i] = (crow(i, 0) >= thr && crow(i, 0) < rlim) ? s[i] : 0.f;
     }
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
@@ -513,7 +499,6 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
       dk[db] = mfma32(rd.trA(Qs, 16, db), ds1, dk[db]);
     }
 
-    if (n + 1 < niter) put_stat(buf ^ 1);
     rd.flip(BUF);
     wait_vmem();
     __syncthreads();

@@ -243,6 +243,22 @@ struct TileLoader {
   }
 };
 
+// One global_load_lds_dword: lane l's 4 bytes at sbase + voff go to LDS
+// address dst + 4*l (dst and sbase wave-uniform); inline assembly for the
+// reason given at TileLoader::lds_dma16.
+__device__ __forceinline__ void lds_dma4(void* dst, const void* sbase, uint32_t voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS void*)(dst));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(m0v), "v"(voff), "s"(sbase) : "memory");
+}
+
+// Per-row fp32 statistics of one query tile into LDS: dst[l] = src[row0 + l]
+// for the 64 lanes l of the calling wave, rows past nrows-1 repeating the
+// last row (row0 < nrows).  Waited for like the tile loads.
+__device__ __forceinline__ void load_row_stat(float* dst, const float* src, int row0, int nrows, int lane) {
+  lds_dma4(dst, src + row0, (uint32_t)min(lane, nrows - 1 - row0) * 4u);
+}
+
 // s_waitcnt vmcnt(0), leaving expcnt/lgkmcnt unconstrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
