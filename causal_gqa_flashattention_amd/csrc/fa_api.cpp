@@ -19,7 +19,6 @@
 
 namespace {
 
-constexpr int kFwdBM = 128;   // query rows per forward workgroup
 constexpr int kDqBM = 128;    // query rows per dQ workgroup
 constexpr int kDkvBN = 128;   // keys per dK/dV workgroup
 
@@ -108,7 +107,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.G = Hq / Hkv;
   a.off = Lk - Lq;
-  a.nqt = (Lq + kFwdBM - 1) / kFwdBM;
+  a.nqt = 0;  // set by the launcher from the kernel's tile height
   a.scale_log2 = scale * 1.4426950408889634f;
   const hipError_t e = cgqa::launch_fwd(a, D, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

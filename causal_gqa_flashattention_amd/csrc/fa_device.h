@@ -75,6 +75,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Exchange with the lane 32 positions away (the other half of a C column).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max(x, x[lane ^ 32]) on the VALU: v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second; starting from
+// two copies of x, lane l then holds x[l] in one and x[l ^ 32] in the other.
+// (Inline assembly: the compiler folds an fmax over the pair of results of
+// the intrinsic to its first result.  The s_nop covers the VALU-write to
+// permlane-read hazard.)
+__device__ __forceinline__ float max_xor32(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 __device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -153,9 +165,12 @@ struct TileReader {
   // `half` elements apart (`half` a power of two above every offset used):
   // one XOR per register per tile instead of an address add per read.
   __device__ __forceinline__ void flip(int half) {
+    flip_ra(half);
+    flip_tr(half);
+  }
+  __device__ __forceinline__ void flip_ra(int half) {
 #pragma unroll
     for (int j = 0; j < NRA; ++j) ra[j] ^= 2 * half;
-    flip_tr(half);
   }
   __device__ __forceinline__ void flip_tr(int half) {
 #pragma unroll
@@ -171,6 +186,45 @@ struct TileReader {
     const char* p = reinterpret_cast<const char*>(tile + r0 * P + 128 * (db / NTR));
     return cat8(lds_read_tr4(reinterpret_cast<const bf16_t*>(p + tr[0][db % NTR])),
                 lds_read_tr4(reinterpret_cast<const bf16_t*>(p + tr[1][db % NTR])));
+  }
+};
+
+// The same reads from two registers.  Within a row the chunk of k step j is
+// (2j | lane/32) ^ swz = 2j ^ (lane/32 ^ swz), so ra[j] = ra[0] ^ 32 j; the
+// transposed chunk of column block dm is 4 dm ^ (y ^ swz), and row r + 8 has
+// swz(r) ^ 2 with the row term's bit 16 P clear in every offset, so
+// tr[h][dm] = tr[0][0] ^ 64 dm ^ h (32 | 16 P).  One XOR per read instead of
+// 2 + 2 * NTR + NRA - 2 more offset registers.
+template <int D>
+struct TileReaderX {
+  using T = Tile<D>;
+  static constexpr int P = T::P;
+  static constexpr int NRA = (D / 16) < 8 ? (D / 16) : 8;
+  static constexpr int NTR = (D / 32) < 4 ? (D / 32) : 4;
+  static_assert(2 * 7 * P + 16 * (T::PC - 1) + 8 < 16 * P, "offsets of rows 0-7 must clear bit 16 P");
+  int ra0, tr0;  // byte offsets
+  __device__ __forceinline__ explicit TileReaderX(int lane) {
+    const int lr = lane & 31, lg = lane >> 5;
+    ra0 = 2 * (lr * P + ((lg ^ T::swz(lr)) << 3));
+    const int rl = 4 * (lane >> 5) + ((lane >> 2) & 3);
+    const int y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    tr0 = 2 * (rl * P + ((y ^ T::swz(rl)) << 3) + 4 * (lane & 1));
+  }
+  __device__ __forceinline__ void flip_ra(int half) { ra0 ^= 2 * half; }
+  __device__ __forceinline__ void flip_tr(int half) { tr0 ^= 2 * half; }
+  __device__ __forceinline__ void flip(int half) {
+    flip_ra(half);
+    flip_tr(half);
+  }
+  __device__ __forceinline__ bf16x8 row16(const bf16_t* tile, int r0, int kd) const {
+    const char* p = reinterpret_cast<const char*>(tile + r0 * P + 128 * (kd / NRA)) + (ra0 ^ (32 * (kd % NRA)));
+    return lds_read16(reinterpret_cast<const bf16_t*>(p));
+  }
+  __device__ __forceinline__ bf16x8 trA(const bf16_t* tile, int r0, int db) const {
+    const char* p = reinterpret_cast<const char*>(tile + r0 * P + 128 * (db / NTR));
+    const int o = tr0 ^ (64 * (db % NTR));
+    return cat8(lds_read_tr4(reinterpret_cast<const bf16_t*>(p + o)),
+                lds_read_tr4(reinterpret_cast<const bf16_t*>(p + (o ^ (32 | 16 * P)))));
   }
 };
 
@@ -262,6 +316,12 @@ __device__ __forceinline__ void load_row_stat(float* dst, const float* src, int 
 // s_waitcnt vmcnt(0), leaving expcnt/lgkmcnt unconstrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): all but the N most recent vector-memory loads done.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // Map a launch-order block id to a logical work id so that the blocks the
 // hardware places on one XCD (block id mod 8, round robin) get a contiguous

@@ -31,6 +31,9 @@
 
 namespace cgqa {
 
+// LDS reads kept this many fragments ahead of the MFMAs that use them
+constexpr int kLookahead = 6;
+
 template <int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs a) {
   constexpr int BM = 128;
@@ -115,6 +118,14 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
 #pragma unroll
       for (int kd = 0; kd < NKD; ++kd) s[nb] = mfma32(rd.row16(Ks, nb * 32, kd), qf[kd], s[nb]);
     }
+    // keep LDS reads kLookahead fragments ahead of the products that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, kLookahead, 0);
+#pragma unroll
+    for (int t = 0; t < NNB * NKD - kLookahead; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kLookahead, 0);
     prio_lo();
     if (j >= n_full) {  // diagonal or ragged tile: hide keys past the diagonal or past Lk
       __asm__ volatile("");  // keep this a real branch (not speculated into every tile)
@@ -188,13 +199,275 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
   }
 }
 
+// ---------------------------------------------------------------- ping-pong
+// Head dims 96 and 128.  One workgroup = 8 wavefronts = 256 query rows of one
+// query head, 32 rows per wavefront, the same per-tile products as above.
+// Wavefronts w and w + 4 share a SIMD.  On gfx950 a tile's softmax costs a
+// wavefront about as much vector time (32 exponentials at a quarter of the
+// FMA rate, plus max, sum and conversion) as its products cost matrix time,
+// and within one wavefront the two depend on each other.  So the two groups
+// (waves 0-3 and 4-7) run half a key tile apart, in phases separated by
+// workgroup barriers:
+//   phase 2j     group A: S(j) = K_j Q^T and O += P(j-1) V(j-1)   (matrix)
+//                group B: softmax of S(j-1) -> P(j-1)             (vector)
+//   phase 2j + 1 group A: softmax of S(j) -> P(j)                 (vector)
+//                group B: S(j) and O += P(j-1) V(j-1)             (matrix)
+// K and V tiles each rotate through four LDS buffers.  Only matrix steps
+// issue loads (a load issue can stall its wavefront): group A's matrix step j
+// loads K_{j+2}, group B's loads V_{j+1}, and each ends by waiting for its
+// previous batch, so a tile is resident at least one phase before it is read.
+// A vector step also reads the next matrix step's K fragments into registers,
+// so that step's S products start on register operands.
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
+  constexpr int BM = 256;
+  constexpr int P = Tile<D>::P;
+  constexpr int NKD = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int NNB = BN / 32;
+  constexpr int NKS = BN / 16;
+  constexpr int ROUNDS = BN * Tile<D>::PC / 256;  // direct loads per wavefront per tile
+  constexpr float kSlack = 8.f;
+
+  // K tiles at [0, 4*TILE), V tiles at [4*TILE, 8*TILE); tile j in buffer j & 3
+  constexpr int TILE = BN * P;
+  static_assert((TILE & (TILE - 1)) == 0, "tile size must be a power of two");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[8 * TILE];
+  bf16_t* const sK = smem;
+  bf16_t* const sV = smem + 4 * TILE;
+
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grp_b = w >= 4;
+
+  const int G = a.G;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_group = a.nqt * G;
+  const int bg = logical / per_group;
+  const int rr = logical - bg * per_group;
+  const int t = rr / G, hi = rr - (rr / G) * G;
+  const int qt = CAUSAL ? (a.nqt - 1 - t) : t;  // heaviest tiles first
+  const int b = bg / a.Hkv, hk = bg - (bg / a.Hkv) * a.Hkv;
+  const int hq = hk * G + hi;
+  const int Lq = a.Lq, Lk = a.Lk, off = a.off;
+
+  const bf16_t* qp = a.q + ((int64_t)(b * a.Hq + hq) * Lq) * D;
+  const bf16_t* kp = a.k + ((int64_t)(b * a.Hkv + hk) * Lk) * D;
+  const bf16_t* vp = a.v + ((int64_t)(b * a.Hkv + hk) * Lk) * D;
+
+  const int q0 = qt * BM;
+  const int r0 = q0 + 32 * w;  // this wavefront's first row
+  const int qrow = r0 + lr;
+
+  // key tiles of the workgroup, and of this wavefront (a prefix of them)
+  int kv_end = Lk;
+  if (CAUSAL) kv_end = min(Lk, min(q0 + BM, Lq) + off);
+  const int nkt = (kv_end + BN - 1) / BN;
+  int wv_end = Lk;
+  if (CAUSAL) wv_end = min(Lk, min(r0 + 32, Lq) + off);
+  const int wnkt = r0 < Lq ? (wv_end + BN - 1) / BN : 0;
+  int n_full = Lk / BN;  // tiles this wavefront reads without a mask
+  if (CAUSAL) n_full = min(n_full, (r0 + off + 1) / BN);
+  n_full = max(0, min(n_full, wnkt));
+
+  const TileLoader<D> ld(w & 3, lane);
+  if (w < 4) {
+    if (nkt > 0) ld.template load<BN>(sK, kp, 0, Lk, w);
+    if (nkt > 1) ld.template load<BN>(sK + TILE, kp, BN, Lk, w);
+  } else {
+    if (nkt > 0) ld.template load<BN>(sV, vp, 0, Lk, w & 3);
+  }
+
+  bf16x8 qf[NKD];
+  {
+    const int qr = min(qrow, Lq - 1);  // rows past Lq compute on a copy; never stored
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qr * D + 16 * kd + 8 * lg));
+  }
+
+  // row reads (K) follow tile j of the matrix step, transposed reads (V) tile
+  // j - 1; buffer b sits b * TILE elements in, so moving from buffer j & 3 to
+  // (j + 1) & 3 is an XOR of the offsets with (j odd ? 3 : 1) * TILE
+  TileReaderX<D> rd(lane);
+  const float c2 = a.scale_log2;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+  f32x16 s[NNB];
+#pragma unroll
+  for (int nb = 0; nb < NNB; ++nb) s[nb] = zero16();
+  bf16x8 pf[NKS];
+
+  // loads issued in phase 2j; returns whether this wavefront issued any
+  auto loads = [&](int j) -> bool {
+    if (w < 4) {
+      if (j + 2 >= nkt) return false;
+      ld.template load<BN>(sK + ((j + 2) & 3) * TILE, kp, (j + 2) * BN, Lk, w);
+    } else {
+      if (j + 1 >= nkt) return false;
+      ld.template load<BN>(sV + ((j + 1) & 3) * TILE, vp, (j + 1) * BN, Lk, w & 3);
+    }
+    return true;
+  };
+  // end of a matrix step: this wavefront's previous batch of loads must have
+  // landed, the one just issued may still be in flight
+  auto wait_loads = [&](bool issued) {
+    if (issued)
+      wait_vmem_n<ROUNDS>();
+    else
+      wait_vmem();
+  };
+  // K fragments of the next matrix step, read into registers during the
+  // vector step before it (the tile is resident by then)
+  bf16x8 kf[NNB * NKD];
+  auto prefetch_k = [&]() {
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+      for (int kd = 0; kd < NKD; ++kd) kf[nb * NKD + kd] = rd.row16(sK, nb * 32, kd);
+  };
+  // matrix step j: S(j), then O += P(j-1) V(j-1); independent accumulators
+  // interleaved so that consecutive MFMAs do not wait on each other.  The
+  // step also issues this wavefront's tile loads, so that the wavefronts in
+  // their vector step never wait on a load issue, and ends with the wait for
+  // its previous batch.
+  auto mstep = [&](int j) {
+    const bool issued = loads(j);
+    if (j < wnkt) {
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb) s[nb] = zero16();
+#pragma unroll
+      for (int kd = 0; kd < NKD; ++kd)
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb) s[nb] = mfma32(kf[nb * NKD + kd], qf[kd], s[nb]);
+    }
+    if (j >= 1 && j <= wnkt) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = mfma32(rd.trA(sV, 16 * ks, db), pf[ks], acc[db]);
+      // the transposed reads run kLookahead ahead of the products (the K
+      // fragments' registers are free by now)
+      constexpr int NM = NKS * NDB, NR = 2 * NM, LA = kLookahead < NR ? kLookahead : NR;
+      static_assert(LA % 2 == 0 && LA <= NR, "read pattern");
+      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+      for (int t = 0; t < (NR - LA) / 2; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - LA) / 2, 0);
+    }
+    rd.flip_ra(((j & 1) ? 3 : 1) * TILE);
+    if (j >= 1) rd.flip_tr((((j - 1) & 1) ? 3 : 1) * TILE);
+    wait_loads(issued);
+  };
+  // vector step j: softmax of S(j) into P(j)
+  auto vstep = [&](int j) {
+    if (j < 0 || j >= wnkt) return;
+    if (j >= n_full) {  // diagonal or ragged tile
+      __asm__ volatile("");
+      const int last = CAUSAL ? min(qrow + off, Lk - 1) : Lk - 1;
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb) {
+        const int thr = last - (j * BN + nb * 32 + 4 * lg);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[nb][i] = (crow(i, 0) <= thr) ? s[nb][i] : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nb][i]);
+    mx = max_xor32(mx);
+    const float m_cand = mx * c2;
+    if (__any(m_cand > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[nb][i], c2, -m_use));
+        s[nb][i] = p;
+        rs += p;
+      }
+    l_run += rs;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) pf[ks] = pack8(s[ks / 2], ks % 2);
+  };
+
+  wait_vmem();
+  __syncthreads();
+  // 2 * (nkt + 1) phases; every wavefront passes the same barriers
+  if (!grp_b) {
+    if (wnkt > 0) prefetch_k();
+    for (int j = 0; j <= nkt; ++j) {
+      mstep(j);
+      __syncthreads();
+      if (j + 1 < wnkt) prefetch_k();
+      vstep(j);
+      __syncthreads();
+    }
+  } else {
+    for (int j = 0; j <= nkt; ++j) {
+      if (j < wnkt) prefetch_k();
+      vstep(j - 1);
+      __syncthreads();
+      mstep(j);
+      __syncthreads();
+    }
+  }
+
+  const float l_tot = l_run + xor32(l_run);
+  if (qrow < Lq) {
+    const float inv = 1.f / l_tot;
+    bf16_t* op = a.o + ((int64_t)(b * a.Hq + hq) * Lq + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[db][4 * q4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * q4 + 4 * lg) = v4;
+      }
+    if (lg == 0) a.lse[(int64_t)(b * a.Hq + hq) * Lq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
 template <int D, int BN>
-static hipError_t launch_fwd_d(const FwdArgs& a, bool causal, hipStream_t stream) {
-  const int nblocks = a.B * a.Hq * a.nqt;
-  if (causal)
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BN, true>), dim3(nblocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BN, false>), dim3(nblocks), dim3(256), 0, stream, a);
+static hipError_t launch_fwd_d(const FwdArgs& a0, bool causal, hipStream_t stream) {
+  FwdArgs a = a0;
+  // ping-pong for D = 96 and 128; at D = 64 the 4-wavefront kernel runs four
+  // wavefronts per SIMD, which hides latency better (measured faster)
+  if constexpr (D == 96 || D == 128) {
+    a.nqt = (a.Lq + 255) / 256;
+    const int nblocks = a.B * a.Hq * a.nqt;
+    if (causal)
+      hipLaunchKernelGGL((fa_fwd_pp_kernel<D, BN, true>), dim3(nblocks), dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fa_fwd_pp_kernel<D, BN, false>), dim3(nblocks), dim3(512), 0, stream, a);
+  } else {
+    a.nqt = (a.Lq + 127) / 128;
+    const int nblocks = a.B * a.Hq * a.nqt;
+    if (causal)
+      hipLaunchKernelGGL((fa_fwd_kernel<D, BN, true>), dim3(nblocks), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fa_fwd_kernel<D, BN, false>), dim3(nblocks), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

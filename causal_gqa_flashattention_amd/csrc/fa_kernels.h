@@ -14,7 +14,7 @@ struct FwdArgs {
   float* lse;
   int B, Hq, Hkv, Lq, Lk, G;
   int off;          // Lk - Lq: causal diagonal offset
-  int nqt;          // number of query tiles
+  int nqt;          // number of query tiles (set by launch_fwd)
   float scale_log2; // scale * log2(e)
 };
 
