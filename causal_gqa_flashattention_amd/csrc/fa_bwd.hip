@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
   const float lse2 = row_ok ? a.lse[qh + qrow] * kLog2e : INFINITY;
   const float dl = row_ok ? a.delta[qh + qrow] : 0.f;
 
-  TileReader<D> rd(lane);
+  TileReaderX<D> rd(lane);
   const float c2 = a.scale_log2;
   f32x16 dq[NDB];
 #pragma unroll
@@ -142,6 +142,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
         dp[nb] = mfma32(rd.row16(Vs, nb * 32, kd), dof[kd], dp[nb]);
       }
     }
+    read_ahead<2 * NNB * NKD, 1>();
     prio_lo();
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb)
@@ -166,9 +167,10 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
     for (int ks = 0; ks < NKS; ++ks) dsf[ks] = pack8(s[ks / 2], ks % 2);
     prio_hi();
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) dq[db] = mfma32(rd.trA(Ks, 16 * ks, db), dsf[ks], dq[db]);
+      for (int db = 0; db < NDB; ++db) dq[db] = mfma32(rd.trA(Ks, 16 * ks, db), dsf[ks], dq[db]);
+    read_ahead<NKS * NDB, 2>();
     prio_lo();
 
     rd.flip(BUF);

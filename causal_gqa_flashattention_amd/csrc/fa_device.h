@@ -313,6 +313,25 @@ __device__ __forceinline__ void load_row_stat(float* dst, const float* src, int 
   lds_dma4(dst, src + row0, (uint32_t)min(lane, nrows - 1 - row0) * 4u);
 }
 
+// Scheduling pattern for a block of NM MFMAs that each consume RPM LDS reads:
+// the first LA reads go out ahead, then every MFMA is followed by the reads
+// of the one LA reads later.  Placed after the block's code; the compiler
+// drops a pattern it cannot meet (for instance for want of registers).
+template <int NM, int RPM, int LA = 6>
+__device__ __forceinline__ void read_ahead() {
+  constexpr int NR = NM * RPM;
+  constexpr int L = LA < NR ? LA : NR;
+  constexpr int MID = (NR - L) / RPM;
+  static_assert((NR - L) % RPM == 0, "read pattern");
+  __builtin_amdgcn_sched_group_barrier(0x100, L, 0);
+#pragma unroll
+  for (int t = 0; t < MID; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - MID, 0);
+}
+
 // s_waitcnt vmcnt(0), leaving expcnt/lgkmcnt unconstrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
