@@ -122,8 +122,9 @@ def summarize_pmc(fetch_csv, write_csv, workload):
         factor = sum(factors) / len(factors)
         out["calibration"][counter] = {"copy_mib": COPY_MIB, "counted_kib": copies, "factor": factor}
         for _, n, v in rows:
-            for key, tag in (("fwd", "fa_fwd_kernel"), ("delta", "fa_delta_kernel"),
-                             ("dq", "fa_dq_kernel"), ("dkv", "fa_dkv_kernel")):
+            # every kernel variant of a stage (e.g. fa_fwd_kernel, fa_fwd_pp_kernel)
+            for key, tag in (("fwd", "cgqa::fa_fwd_"), ("delta", "cgqa::fa_delta_"),
+                             ("dq", "cgqa::fa_dq_"), ("dkv", "cgqa::fa_dkv_")):
                 if tag in n:
                     vals.setdefault(key, {})[counter] = v * factor * 1024
     for key, d in vals.items():

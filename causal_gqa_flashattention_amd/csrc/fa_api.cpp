@@ -20,7 +20,6 @@
 namespace {
 
 constexpr int kDqBM = 128;    // query rows per dQ workgroup
-constexpr int kDkvBN = 128;   // keys per dK/dV workgroup
 
 bool fwd_head_dim_ok(int D) { return D == 64 || D == 96 || D == 128 || D == 256; }
 bool bwd_head_dim_ok(int D) { return D == 64 || D == 96 || D == 128 || D == 256; }
@@ -172,7 +171,7 @@ fa_status bwd_common(const void* q, const void* k, const void* v, const float* l
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.G = Hq / Hkv;
   a.off = Lk - Lq;
   a.nqt = (Lq + kDqBM - 1) / kDqBM;
-  a.nkt = (Lk + kDkvBN - 1) / kDkvBN;
+  a.nkt = 0;  // set by the launcher from the dK/dV kernel's key tile
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   const hipError_t e = cgqa::launch_bwd(a, D, causal != 0, which, static_cast<hipStream_t>(stream));

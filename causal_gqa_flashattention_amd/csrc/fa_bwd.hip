@@ -244,6 +244,10 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   const int qt_first = qfirst / BM;
   const int nqt = (Lq + BM - 1) / BM;
   const int nq = max(0, nqt - qt_first);
+  // iteration n: query tile nqt - 1 - n / G of query head n % G.  Last tile
+  // first and heads innermost, so the workgroups of one key/value head (placed
+  // on one XCD) read the same Q/dO tile at about the same time and share it
+  // in L2, whatever their first tile.
   const int niter = G * nq;
 
   // the 8 waves load as two groups of four: waves 0-3 fill Q, waves 4-7 fill dO
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   auto issue = [&](int n) {
     bf16_t* qt_lds = smem + (n & 1) * BUF;
     bf16_t* dt_lds = qt_lds + BM * P;
-    const int hi = n / nq, qtile = qt_first + (n - (n / nq) * nq);
+    const int hi = n % G, qtile = nqt - 1 - n / G;
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
     const int qbase = qtile * BM;
     if (w < 4)
@@ -271,7 +275,8 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     ld.template load<BN>(sV, a.v + kvh * D, k0, Lk, wl);
   if (niter > 0) issue(0);
 
-  TileReader<D> rd(lane);
+  TileReaderX<D> rq(lane);  // Q and dO tiles: offsets flip with the buffer
+  TileReaderX<D> rk(lane);  // K and V tiles (resident)
   const float c2 = a.scale_log2;
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -284,21 +289,21 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   __syncthreads();
   for (int n = 0; n < niter; ++n) {
     const int buf = n & 1;
-    const int q0 = (qt_first + (n - (n / nq) * nq)) * BM;
+    const int q0 = (nqt - 1 - n / G) * BM;
     if (n + 1 < niter) issue(n + 1);
-    const bf16_t* Qs = smem + buf * BUF;   // row reads: explicit buffer base
-    const bf16_t* Ds = Qs + BM * P;
-    const bf16_t* Qt = smem;               // transposed reads: + buf * BUF via the
-    const bf16_t* Dt = smem + BM * P;      // reader's flipped offsets
+    const bf16_t* Qs = smem;            // + buf * BUF through rq's flipped offsets
+    const bf16_t* Ds = smem + BM * P;
     const int r0 = 32 * qhalf;  // this wave's rows within the tile
 
     f32x16 s = zero16(), dp = zero16();
     prio_hi();
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
-      s = mfma32(rd.row16(Qs, r0, kd), rd.row16(sK, 32 * kb, kd), s);
-      dp = mfma32(rd.row16(Ds, r0, kd), rd.row16(sV, 32 * kb, kd), dp);
+      s = mfma32(rq.row16(Qs, r0, kd), rk.row16(sK, 32 * kb, kd), s);
+      dp = mfma32(rq.row16(Ds, r0, kd), rk.row16(sV, 32 * kb, kd), dp);
     }
+    // (no read-ahead pattern here: with eight wavefronts in step it only
+    // bunches the LDS reads, measured slower)
     prio_lo();
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
@@ -322,19 +327,19 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = s[4 * i4 + e] * (dp[4 * i4 + e] - d4[e]);
     }
-    const bf16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 1);
-    const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 1);
+    const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
+    const bf16x8 ds[2] = {pack8(dp, 0), pack8(dp, 1)};
     prio_hi();
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      dv[db] = mfma32(rd.trA(Dt, r0, db), pf0, dv[db]);
-      dv[db] = mfma32(rd.trA(Dt, r0 + 16, db), pf1, dv[db]);
-      dk[db] = mfma32(rd.trA(Qt, r0, db), ds0, dk[db]);
-      dk[db] = mfma32(rd.trA(Qt, r0 + 16, db), ds1, dk[db]);
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dv[db] = mfma32(rq.trA(Ds, r0 + 16 * h, db), pf[h], dv[db]);
+        dk[db] = mfma32(rq.trA(Qs, r0 + 16 * h, db), ds[h], dk[db]);
+      }
     prio_lo();
 
-    rd.flip_tr(BUF);
+    rq.flip(BUF);
     wait_vmem();
     __syncthreads();
   }
@@ -385,14 +390,17 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- dK / dV, wide heads
 // Head dim 256: the dK/dV accumulators of 32 keys take 256 registers per
 // wavefront, so two wavefronts cannot share a SIMD.  One workgroup = 4
-// wavefronts = 128 keys, one wavefront per SIMD; each wavefront owns 32 keys
-// for all rows, keeps its K and V operand fragments in registers, and query
-// tiles of 32 rows of Q and dO (with LSE and delta) stream through LDS,
-// double buffered.  Per query tile the products are those of fa_dkv_kernel.
+// wavefronts = 64 keys, one wavefront per SIMD: wavefront w owns keys
+// 32 (w & 1) .. + 31 and row half w >> 1 of every query tile, keeps its K and
+// V operand fragments in registers, and query tiles of 64 rows of Q and dO
+// (with LSE and delta) stream through LDS, double buffered.  Per query tile
+// the products are those of fa_dkv_kernel; the two row halves' dK/dV are
+// added through LDS at the end.  (64-key workgroups: at 8192 tokens and two
+// key/value heads that is 256 workgroups, one per CU.)
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
-  constexpr int BN = 128;   // keys per workgroup
-  constexpr int BM = 32;    // query rows per tile
+  constexpr int BN = 64;    // keys per workgroup
+  constexpr int BM = 64;    // query rows per tile (two halves of 32)
   constexpr int P = Tile<D>::P;
   constexpr int NKD = D / 16;
   constexpr int NDB = D / 32;
@@ -404,36 +412,43 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = w & 1, qhalf = w >> 1;
+  const int r0 = 32 * qhalf;  // this wavefront's rows within a tile
   const int G = a.G;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / a.nkt;
-  const int kt = logical - bh * a.nkt;
+  const int kt = logical - bh * a.nkt;  // key tile 0 sees the most queries: heaviest first
   const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
   const int64_t kvh = (int64_t)(b * a.Hkv + hk) * Lk;
   const int k0 = kt * BN;
-  const int krow = k0 + 32 * w + lr;
+  const int krow = k0 + 32 * kb + lr;
   const bool key_ok = krow < Lk;
 
   const int qfirst = CAUSAL ? max(0, k0 - off) : 0;
   const int qt_first = qfirst / BM;
   const int nqt = (Lq + BM - 1) / BM;
   const int nq = max(0, nqt - qt_first);
+  // iteration n: query tile nqt - 1 - n / G of query head n % G.  Last tile
+  // first and heads innermost, so the workgroups of one key/value head (placed
+  // on one XCD) read the same Q/dO tile at about the same time and share it
+  // in L2, whatever their first tile.
   const int niter = G * nq;
 
   const TileLoader<D> ld(w, lane);
-  // Q, dO and the rows' LSE (wave 0) and delta (wave 1) by direct loads; the
-  // stat loads fill 64 rows, the first BM of which belong to the tile
+  // Q, dO and the rows' LSE (wave 0) and delta (wave 1) by direct loads
   auto issue = [&](int n) {
     bf16_t* qt_lds = smem + (n & 1) * BUF;
-    const int hi = n / nq, qtile = qt_first + (n - (n / nq) * nq);
+    const int hi = n % G, qtile = nqt - 1 - n / G;
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
     const int qbase = qtile * BM;
-    ld.template load<BM>(qt_lds, a.q + qh * D, qbase, Lq, w);
-    ld.template load<BM>(qt_lds + BM * P, a.dO + qh * D, qbase, Lq, w);
+    // stats first: anything the compiler reloads for them then waits on
+    // nothing but its own load
     if (w == 0) load_row_stat(&stat[n & 1][0][0], a.lse + qh, qbase, Lq, lane);
     if (w == 1) load_row_stat(&stat[n & 1][1][0], a.delta + qh, qbase, Lq, lane);
+    ld.template load<BM>(qt_lds, a.q + qh * D, qbase, Lq, w);
+    ld.template load<BM>(qt_lds + BM * P, a.dO + qh * D, qbase, Lq, w);
   };
   if (niter > 0) issue(0);
 
@@ -460,7 +475,7 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   __syncthreads();
   for (int n = 0; n < niter; ++n) {
     const int buf = n & 1;
-    const int q0 = (qt_first + (n - (n / nq) * nq)) * BM;
+    const int q0 = (nqt - 1 - n / G) * BM;
     if (n + 1 < niter) issue(n + 1);
     const bf16_t* Qs = smem;  // + buf * BUF through the reader's flipped offsets
     const bf16_t* Ds = smem + BM * P;
@@ -468,26 +483,26 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     f32x16 s = zero16(), dp = zero16();
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
-      s = mfma32(rd.row16(Qs, 0, kd), kf[kd], s);
-      dp = mfma32(rd.row16(Ds, 0, kd), vf[kd], dp);
+      s = mfma32(rd.row16(Qs, r0, kd), kf[kd], s);
+      dp = mfma32(rd.row16(Ds, r0, kd), vf[kd], dp);
     }
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][8 * i4 + 4 * lg]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][r0 + 8 * i4 + 4 * lg]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fast_exp2(fmaf(s[4 * i4 + e], c2, l4[e] * -kLog2e));
     }
     // tiles that cross the diagonal or hold rows past Lq
     if ((CAUSAL && k0 + BN - 1 > q0 + off) || q0 + BM > Lq) {
       __asm__ volatile("");
-      const int thr = CAUSAL ? krow - off - q0 - 4 * lg : INT_MIN;
-      const int rlim = Lq - q0 - 4 * lg;
+      const int thr = CAUSAL ? krow - off - q0 - r0 - 4 * lg : INT_MIN;
+      const int rlim = Lq - q0 - r0 - 4 * lg;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = (crow(i, 0) >= thr && crow(i, 0) < rlim) ? s[i] : 0.f;
     }
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][8 * i4 + 4 * lg]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][r0 + 8 * i4 + 4 * lg]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = s[4 * i4 + e] * (dp[4 * i4 + e] - d4[e]);
     }
@@ -495,10 +510,10 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 1);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      dv[db] = mfma32(rd.trA(Ds, 0, db), pf0, dv[db]);
-      dv[db] = mfma32(rd.trA(Ds, 16, db), pf1, dv[db]);
-      dk[db] = mfma32(rd.trA(Qs, 0, db), ds0, dk[db]);
-      dk[db] = mfma32(rd.trA(Qs, 16, db), ds1, dk[db]);
+      dv[db] = mfma32(rd.trA(Ds, r0, db), pf0, dv[db]);
+      dv[db] = mfma32(rd.trA(Ds, r0 + 16, db), pf1, dv[db]);
+      dk[db] = mfma32(rd.trA(Qs, r0, db), ds0, dk[db]);
+      dk[db] = mfma32(rd.trA(Qs, r0 + 16, db), ds1, dk[db]);
     }
 
     rd.flip(BUF);
@@ -506,7 +521,30 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  if (key_ok) {
+  // ---- add the two row halves: waves 2-3 hand their partials to waves 0-1
+  // through LDS (the tile buffers are free now), lane-contiguous per register
+  float* red = reinterpret_cast<float*>(smem);
+  static_assert(2 * BUF * 2 >= 2 * NDB * 16 * 64 * 4, "reduction buffer too small");
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    f32x16* acc = pass == 0 ? dk : dv;
+    if (qhalf == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[((kb * NDB + db) * 16 + i) * 64 + lane] = acc[db][i];
+    }
+    __syncthreads();
+    if (qhalf == 0) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] += red[((kb * NDB + db) * 16 + i) * 64 + lane];
+    }
+    __syncthreads();
+  }
+
+  if (qhalf == 0 && key_ok) {
     bf16_t* dkp = a.dk + (kvh + krow) * D;
     bf16_t* dvp = a.dv + (kvh + krow) * D;
     const float sc = a.scale;
@@ -545,7 +583,9 @@ hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t stream) {
 }
 
 template <int D, int BN_Q>
-static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int which, hipStream_t stream) {
+static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStream_t stream) {
+  BwdArgs a = a0;
+  a.nkt = (a.Lk + (D > 128 ? 63 : 127)) / (D > 128 ? 64 : 128);  // keys per dK/dV workgroup
   const int ndq = (which & 1) ? a.B * a.Hq * a.nqt : 0;
   const int ndkv = (which & 2) ? a.B * a.Hkv * a.nkt : 0;
   if (causal) {
