@@ -76,6 +76,8 @@ def source_digest():
     import glob
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "causal_gqa_flashattention_amd", "csrc", "*"))):
+        if not os.path.isfile(p):
+            continue
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -175,6 +177,34 @@ def cpu_baseline(w, bits, budget_s=30.0):
 
 # ------------------------------------------------------------ main
 
+def mfma_ceiling(dev, cus):
+    """Sustained MFMA throughput (csrc/probe) with constant and with random
+    bf16 operands: the second is what kernels on real data can approach,
+    since the chip lowers its clock as operand toggling raises its power."""
+    import ctypes
+    import torch
+    from causal_gqa_flashattention_amd.build import PKG_DIR, PROBE_LIB_NAME
+    from fa_synth import normal_bf16_bits
+    path = os.path.join(PKG_DIR, PROBE_LIB_NAME)
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.cgqa_mfma_ceiling
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    fn.restype = ctypes.c_int
+    bits = torch.from_numpy(normal_bf16_bits((8192 * 8,), seed=7, sigma=1.0).view("int16")).to(dev)
+    out = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    c, r = ctypes.c_double(), ctypes.c_double()
+    torch.cuda.synchronize()
+    rc = fn(bits.data_ptr(), out.data_ptr(), cus, 2048, 10, ctypes.byref(c), ctypes.byref(r))
+    torch.cuda.synchronize()
+    if rc != 0:
+        raise RuntimeError(f"mfma ceiling probe failed: {rc}")
+    return {"constant_operands": round(c.value, 1), "random_operands": round(r.value, 1), "unit": "TFLOP/s",
+            "kernel": "v_mfma_f32_32x32x16_bf16, 2 wavefronts/SIMD, 4 accumulators each, operands in registers"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +214,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="copy kernels of known size plus one step, for counter runs")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the matrix-core throughput probe and print its JSON")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --profile-pass run into profiles/traffic_<workload>.json")
@@ -206,6 +238,10 @@ def main(argv=None):
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    if args.mfma_ceiling:
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(dev, cus)}), flush=True)
+        return 0
     fa.load_library()
     bits = make_inputs(w, with_grad=True)
     g = {n: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for n, b in bits.items()}
@@ -300,7 +336,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: causal GQA fwd+bwd, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
+        "config": {"workload": f"{w.name}: {'causal' if w.causal else 'dense'} GQA fwd+bwd, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
                                f"Lq={w.Lq} Lk={w.Lk} D={w.D}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Lq": w.Lq, "Lk": w.Lk, "D": w.D, "causal": w.causal},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
@@ -311,6 +347,10 @@ def main(argv=None):
                    "extra_over_resident": int(peak - resident),
                    "unfused_fp32_score_bytes": unfused_score_bytes(w.B * w.Hq, w.Lq, 4)},
     }
+    ceil = mfma_ceiling(dev, cus)
+    if ceil is not None:
+        ceil["dominant_kernel_frac_of_random"] = round(achieved / ceil["random_operands"], 4)
+        out["mfma_ceiling"] = ceil
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, bits)
     print(json.dumps(out), flush=True)

@@ -10,6 +10,7 @@ import subprocess
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libcgqa_fa.so"
+PROBE_LIB_NAME = "libcgqa_probe.so"  # matrix-core throughput probe (csrc/probe), not the attention ABI
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are switched off; the compiler would otherwise form
@@ -59,6 +60,22 @@ def build_library(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+    if verbose:
+        print(f"built {out}")
+    build_probe(verbose)
+    return out
+
+
+def build_probe(verbose: bool = True) -> str:
+    """The measurement probe used by ``bench.py --mfma-ceiling``."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip")))
+    out = os.path.join(PKG_DIR, PROBE_LIB_NAME)
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), *HIP_FLAGS, "-shared", *srcs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
     if verbose:
         print(f"built {out}")
