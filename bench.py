@@ -169,10 +169,80 @@ def cpu_baseline(w, bits, budget_s=30.0):
             break
     dt = time.perf_counter() - t0
     total, _ = model_flops(1, heads_done, w.Lq, w.Lk, w.D, w.causal)
+    full, _ = model_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal)
     del np
     return {"value": total / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{heads_done} query heads of key/value head 0 (one GQA group), all {w.Lq} rows, "
-                      f"fp64 forward+backward, {dt:.2f} s"}
+                      f"fp64 forward+backward, {dt:.2f} s",
+            "full_workload_s_extrapolated": round(dt * full / total, 1)}
+
+
+def executed_mfma(w):
+    """MFMA instructions the kernels issue for workload w, following their
+    tilings (diagonal tiles run whole, waves past Lq idle): the count that
+    SQ_INSTS_MFMA should read.  One instruction is 32x32x16, 32768 FLOP."""
+    cdiv = lambda a, b: -(-a // b)
+    D, B, Hq, Hkv, Lq, Lk = w.D, w.B, w.Hq, w.Hkv, w.Lq, w.Lk
+    G, off, causal = Hq // Hkv, Lk - Lq, w.causal
+    NKD, NDB = D // 16, D // 32
+
+    def kv_end(row_end):  # keys seen by rows < row_end
+        return min(Lk, min(row_end, Lq) + off) if causal else Lk
+
+    fwd = 0
+    if D in (96, 128):  # 8-wave ping-pong, 256 rows, 64-key tiles
+        per_tile = 2 * NKD + NDB * 4
+        for qt in range(cdiv(Lq, 256)):
+            for wv in range(8):
+                r0 = qt * 256 + 32 * wv
+                if r0 < Lq:
+                    fwd += per_tile * cdiv(kv_end(r0 + 32), 64)
+    else:  # 4 waves, 128 rows, 64-key tiles (D=256: 32)
+        bn = 32 if D == 256 else 64
+        per_tile = (bn // 32) * NKD + NDB * (bn // 16)
+        for qt in range(cdiv(Lq, 128)):
+            fwd += 4 * per_tile * cdiv(kv_end(qt * 128 + 128), bn)
+    bn = 32 if D == 256 else 64  # dQ: 4 waves, 128 rows
+    dq = 0
+    for qt in range(cdiv(Lq, 128)):
+        dq += 4 * (2 * (bn // 32) * NKD + NDB * (bn // 16)) * cdiv(kv_end(qt * 128 + 128), bn)
+    bnk, waves = (64, 4) if D == 256 else (128, 8)  # dK/dV: query tiles of 64
+    dkv = 0
+    for kt in range(cdiv(Lk, bnk)):
+        qfirst = max(0, kt * bnk - off) if causal else 0
+        nq = max(0, cdiv(Lq, 64) - qfirst // 64)
+        dkv += waves * G * nq * (2 * NKD + 4 * NDB)
+    return {"fwd": fwd * B * Hq, "dq": dq * B * Hq, "dkv": dkv * B * Hkv}
+
+
+def summarize_inst(csv_path, workload):
+    """SQ_INSTS_MFMA per launch against executed_mfma(); GRBM_GUI_ACTIVE over
+    the dispatch duration gives the mean shader clock (summed over XCDs)."""
+    import csv
+    from fa_synth import WORKLOADS
+    w = WORKLOADS[workload]
+    want = executed_mfma(w)
+    rows = {}
+    for r in csv.DictReader(open(csv_path)):
+        n = r["Kernel_Name"]
+        key = next((k for k, t in (("fwd", "cgqa::fa_fwd_"), ("dq", "cgqa::fa_dq_"), ("dkv", "cgqa::fa_dkv_"))
+                    if t in n), None)
+        if key is None:
+            continue
+        d = rows.setdefault(key, {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["dur_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    out = {"workload": workload, "kernels": {}}
+    for k, d in rows.items():
+        e = {"counted_mfma": int(d.get("SQ_INSTS_MFMA", 0)), "analytic_mfma": want[k]}
+        e["ratio"] = round(e["counted_mfma"] / e["analytic_mfma"], 4) if want[k] else None
+        if "GRBM_GUI_ACTIVE" in d and d["dur_ns"]:
+            e["clock_ghz"] = round(d["GRBM_GUI_ACTIVE"] / 8 / d["dur_ns"], 3)  # 8 XCDs
+        if "SQ_INSTS_VALU" in d:
+            e["valu_per_mfma"] = round(d["SQ_INSTS_VALU"] / max(1.0, d.get("SQ_INSTS_MFMA", 1.0)), 2)
+        out["kernels"][k] = e
+    print(json.dumps(out))
+    return 0
 
 
 # ------------------------------------------------------------ main
@@ -214,6 +284,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="copy kernels of known size plus one step, for counter runs")
+    ap.add_argument("--summarize-inst", metavar="CSV",
+                    help="SQ_INSTS_MFMA (and GRBM_GUI_ACTIVE, SQ_INSTS_VALU) of a --profile-pass "
+                         "counter run against the kernels' analytic MFMA counts")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only run the matrix-core throughput probe and print its JSON")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -223,6 +296,8 @@ def main(argv=None):
 
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+    if args.summarize_inst:
+        return summarize_inst(args.summarize_inst, args.workload)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -301,6 +376,7 @@ def main(argv=None):
 
     names = ["fwd", "delta", "dq", "dkv"]
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    step_ev = np.array([e[0].elapsed_time(e[4]) for e in evs])  # first launch to last, per step
     ms_step = wall * 1e3 / args.steps
     total_flops, fwd_flops = model_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal)
     value = total_flops / (ms_step * 1e-3) / 1e12
@@ -342,6 +418,8 @@ def main(argv=None):
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "model_tflop_per_step": round(total_flops / 1e12, 4),
         "kernels": {n: {kk: round(vv, 4) for kk, vv in d.items()} for n, d in kernels.items()},
+        "step_events_ms": {"median": round(float(np.median(step_ev)), 4), "min": round(float(step_ev.min()), 4),
+                           "p90": round(float(np.percentile(step_ev, 90)), 4)},
         "roofline": roofline,
         "memory": {"resident_bytes": int(resident), "peak_bytes": int(peak),
                    "extra_over_resident": int(peak - resident),

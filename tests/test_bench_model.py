@@ -42,3 +42,21 @@ def test_visible_pairs_brute_force(Lq, Lk, causal):
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_executed_mfma_counts():
+    """The kernels' analytic MFMA counts: exactly the algorithmic FLOPs / 32768
+    for dense shapes whose lengths are whole tiles; a few percent above it for
+    causal ones (diagonal tiles run whole); never below."""
+    import bench
+    from fa_synth import WORKLOADS
+    for name in ("dense4k_d64", "dense4k_d96", "train8k", "d256_train8k", "long23k"):
+        w = WORKLOADS[name]
+        e = bench.executed_mfma(w)
+        work = bench.kernel_work(w, bench.visible_pairs(w.Lq, w.Lk, w.causal))
+        for k in ("fwd", "dq", "dkv"):
+            ratio = e[k] * 32768 / work[k]
+            if not w.causal:
+                assert ratio == 1.0, (name, k, ratio)
+            else:
+                assert 1.0 <= ratio < 1.05, (name, k, ratio)

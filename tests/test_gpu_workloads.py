@@ -174,3 +174,33 @@ def test_d256_fwd_bwd_sampled():
         dv_tail += rt["dv"]
     check("dk", to_f64(out["dk"][0, kvh, tail]), dk_tail, f"d256_train8k kv head {kvh} last 512 keys")
     check("dv", to_f64(out["dv"][0, kvh, tail]), dv_tail, f"d256_train8k kv head {kvh} last 512 keys")
+
+
+@pytest.mark.parametrize("L", [4096, 8192, 16384])
+def test_memory_linear_in_length(L):
+    """Peak device memory of a forward + backward equals the resident tensors
+    (inputs, outputs, LSE, delta), which grow linearly in L; the library
+    allocates nothing, where an fp32 score matrix would grow as L^2."""
+    import causal_gqa_flashattention_amd as fa
+    from fa_synth import AttnShape
+    w = AttnShape(name=f"mem{L}", B=1, Hq=32, Hkv=8, Lq=L, Lk=L, D=128, causal=True, seed=7000 + L // 4096)
+    bits = make_inputs(w)
+    g = {n: to_gpu(b) for n, b in bits.items()}
+    o = torch.empty_like(g["q"])
+    lse = torch.empty((w.B, w.Hq, L), dtype=torch.float32, device="cuda")
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
+    torch.cuda.synchronize()
+    resident = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    fa.fa_fwd(g["q"], g["k"], g["v"], o, lse, scale=w.softmax_scale, causal=True)
+    fa.fa_bwd_delta(o, g["do"], delta)
+    fa.fa_bwd(g["q"], g["k"], g["v"], o, lse, delta, g["do"], dq, dk, dv, scale=w.softmax_scale, causal=True)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated()
+    tensors = sum(t.numel() * t.element_size() for t in (*g.values(), o, lse, delta, dq, dk, dv))
+    print(f"[memory] L={L} resident={resident} peak={peak} tensors={tensors} "
+          f"fp32 scores would be {w.Hq * L * L * 4}", flush=True)
+    assert peak == resident
+    assert resident >= tensors
+    assert torch.isfinite(o.float()).all() and torch.isfinite(dk.float()).all()
