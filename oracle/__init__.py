@@ -24,7 +24,14 @@ memory stays bounded), in float64:
   j <= i + (Lk - Lq) — page "Add a fused full-attention path for head_dim
   256 on NAX devices", Design, "Ragged causal inputs" (the query offset is
   taken from the true lengths).  Masked scores are -inf, so they get exactly
-  zero probability.
+  zero probability;
+* optional block-sparse mask — page "feat(attention): complete Flash
+  Attention VJP implementation", "Sparse Block Masks": a uint8 entry per
+  (query tile, key tile) pair, 0 = the pair is skipped; here tiles are 64
+  query rows by 64 keys, one mask for all batches and heads.  A row left
+  with no visible key gets O = 0, LSE = -inf and no gradient share (the
+  pages do not say; this is the reading that skipping every tile of the row
+  gives).
 
 The log-sum-exp is returned in natural-log units.  Pins for every function
 live in ``tests/test_oracle_pins.py``.
@@ -32,6 +39,7 @@ live in ``tests/test_oracle_pins.py``.
 from __future__ import annotations
 
 from .attention import (  # noqa: F401
+    MASK_BLOCK,
     bf16_bits_to_f64,
     visible_mask,
     head_forward,

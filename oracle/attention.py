@@ -11,6 +11,9 @@ import numpy as np
 
 _NEG_INF = -np.inf
 
+# Granularity of a block-sparse mask: 64 query rows x 64 keys per entry.
+MASK_BLOCK = 64
+
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bfloat16 bit patterns (uint16/int16) to float64."""
@@ -18,18 +21,31 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def visible_mask(Lq: int, Lk: int, causal: bool, rows=None) -> np.ndarray:
+def visible_mask(Lq: int, Lk: int, causal: bool, rows=None, block_mask=None) -> np.ndarray:
     """Boolean [len(rows), Lk]: may query row i attend to key j?
 
     Causal masking is bottom-right aligned: j <= i + (Lk - Lq)
     ("Add a fused full-attention path for head_dim 256 on NAX devices",
     Design, ragged causal inputs).  Without a causal mask every key is seen.
+
+    ``block_mask`` ([ceil(Lq/64), ceil(Lk/64)], nonzero = kept) additionally
+    hides every pair (i, j) whose entry [i // 64, j // 64] is 0: the sparse
+    block masks of "feat(attention): complete Flash Attention VJP
+    implementation", "Sparse Block Masks" (tile pairs with a 0 entry are
+    skipped), at a fixed 64 x 64 granularity.
     """
     rows = np.arange(Lq) if rows is None else np.asarray(rows)
     if not causal:
-        return np.ones((rows.shape[0], Lk), dtype=bool)
-    off = Lk - Lq
-    return np.arange(Lk)[None, :] <= (rows[:, None] + off)
+        vis = np.ones((rows.shape[0], Lk), dtype=bool)
+    else:
+        off = Lk - Lq
+        vis = np.arange(Lk)[None, :] <= (rows[:, None] + off)
+    if block_mask is not None:
+        bm = np.asarray(block_mask)
+        if bm.shape != (-(-Lq // MASK_BLOCK), -(-Lk // MASK_BLOCK)):
+            raise ValueError(f"block mask shape {bm.shape} does not match Lq={Lq}, Lk={Lk}")
+        vis = vis & (bm[rows // MASK_BLOCK][:, np.arange(Lk) // MASK_BLOCK] != 0)
+    return vis
 
 
 def _scores(qb: np.ndarray, kh: np.ndarray, scale: float, vis: np.ndarray) -> np.ndarray:
@@ -38,12 +54,25 @@ def _scores(qb: np.ndarray, kh: np.ndarray, scale: float, vis: np.ndarray) -> np
     return np.where(vis, s, _NEG_INF)
 
 
-def _lse(s: np.ndarray) -> np.ndarray:
-    """Natural-log log-sum-exp of each row: m + log(sum exp(s - m))."""
+def _lse(s: np.ndarray, allow_empty: bool = False) -> np.ndarray:
+    """Natural-log log-sum-exp of each row: m + log(sum exp(s - m)).
+
+    A row that sees no key has no softmax.  Without a block mask that cannot
+    happen for valid sizes and is an error; with one (``allow_empty``) such a
+    row gets LSE = -inf (the log of an empty sum).
+    """
     m = s.max(axis=1)
-    if not np.all(np.isfinite(m)):
+    empty = ~np.isfinite(m)
+    if np.any(empty) and not allow_empty:
         raise ValueError("a query row sees no key; its softmax is undefined")
-    return m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    safe = np.where(empty, 0.0, m)
+    tot = np.exp(s - safe[:, None]).sum(axis=1)
+    return np.where(empty, _NEG_INF, safe + np.log(np.where(empty, 1.0, tot)))
+
+
+def _probs(s: np.ndarray, l: np.ndarray) -> np.ndarray:
+    """P = exp(S - LSE) per row; all zero for a row that sees no key."""
+    return np.where(np.isfinite(l)[:, None], np.exp(s - np.where(np.isfinite(l), l, 0.0)[:, None]), 0.0)
 
 
 def _row_blocks(rows: np.ndarray, block: int):
@@ -51,10 +80,11 @@ def _row_blocks(rows: np.ndarray, block: int):
         yield rows[i:i + block]
 
 
-def head_forward(qh, kh, vh, scale, causal, rows=None, block=256):
+def head_forward(qh, kh, vh, scale, causal, rows=None, block=256, block_mask=None):
     """One head: O and LSE for the given query rows (default: all rows).
 
-    qh [Lq, D], kh/vh [Lk, D] float64.  Returns (o [n, D], lse [n]).
+    qh [Lq, D], kh/vh [Lk, D] float64.  Returns (o [n, D], lse [n]).  With a
+    block mask, a row that sees no key gets O = 0 and LSE = -inf.
     """
     Lq, Lk = qh.shape[0], kh.shape[0]
     rows = np.arange(Lq) if rows is None else np.asarray(rows)
@@ -62,9 +92,9 @@ def head_forward(qh, kh, vh, scale, causal, rows=None, block=256):
     lse = np.empty(rows.shape[0])
     pos = 0
     for rb in _row_blocks(rows, block):
-        s = _scores(qh[rb], kh, scale, visible_mask(Lq, Lk, causal, rb))
-        l = _lse(s)
-        p = np.exp(s - l[:, None])          # softmax rows, 0 where masked
+        s = _scores(qh[rb], kh, scale, visible_mask(Lq, Lk, causal, rb, block_mask))
+        l = _lse(s, allow_empty=block_mask is not None)
+        p = _probs(s, l)                    # softmax rows, 0 where masked
         o[pos:pos + rb.shape[0]] = p @ vh   # O = P V
         lse[pos:pos + rb.shape[0]] = l
         pos += rb.shape[0]
@@ -101,7 +131,7 @@ def head_forward_online(qh, kh, vh, scale, causal, block_n=32):
     return acc / l[:, None], m + np.log(l)
 
 
-def head_backward(qh, kh, vh, doh, scale, causal, rows=None, key_rows=None, block=256):
+def head_backward(qh, kh, vh, doh, scale, causal, rows=None, key_rows=None, block=256, block_mask=None):
     """One query head's backward by explicit recomputation.
 
     Per block of query rows: S, P from the row's own log-sum-exp, O = P V,
@@ -112,7 +142,8 @@ def head_backward(qh, kh, vh, doh, scale, causal, rows=None, key_rows=None, bloc
     ``rows`` limits the query rows (dK/dV are then partial sums over those
     rows only).  ``key_rows`` limits which key rows get dK/dV (dQ is then
     not computed).  Returns a dict with o, lse, delta, dq (rows) and dk, dv
-    ([len(key_rows) or Lk, D]).
+    ([len(key_rows) or Lk, D]).  With a block mask, a row that sees no key
+    has P = 0: O = 0, LSE = -inf, dQ = 0 and no share in dK/dV.
     """
     Lq, Lk = qh.shape[0], kh.shape[0]
     rows = np.arange(Lq) if rows is None else np.asarray(rows)
@@ -132,9 +163,9 @@ def head_backward(qh, kh, vh, doh, scale, causal, rows=None, key_rows=None, bloc
     for rb in _row_blocks(rows, block):
         nb = rb.shape[0]
         qb, dob = qh[rb], doh[rb]
-        s = _scores(qb, kh, scale, visible_mask(Lq, Lk, causal, rb))
-        l = _lse(s)
-        p = np.exp(s - l[:, None])
+        s = _scores(qb, kh, scale, visible_mask(Lq, Lk, causal, rb, block_mask))
+        l = _lse(s, allow_empty=block_mask is not None)
+        p = _probs(s, l)
         o = p @ vh
         dl = (dob * o).sum(axis=1)                      # delta = rowsum(dO * O)
         pk = p[:, kcols]
@@ -159,19 +190,21 @@ def _check(q, k, v):
     return B, Hq, Hkv, Lq, Lk, D, Hq // Hkv
 
 
-def forward(q, k, v, scale, causal, block=256):
-    """Full forward over [B, Hq, Lq, D] / [B, Hkv, Lk, D] float64 arrays."""
+def forward(q, k, v, scale, causal, block=256, block_mask=None):
+    """Full forward over [B, Hq, Lq, D] / [B, Hkv, Lk, D] float64 arrays
+    (one block mask, if any, for every batch and head)."""
     B, Hq, Hkv, Lq, Lk, D, G = _check(q, k, v)
     o = np.empty((B, Hq, Lq, D))
     lse = np.empty((B, Hq, Lq))
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            o[b, h], lse[b, h] = head_forward(q[b, h], k[b, g], v[b, g], scale, causal, block=block)
+            o[b, h], lse[b, h] = head_forward(q[b, h], k[b, g], v[b, g], scale, causal, block=block,
+                                              block_mask=block_mask)
     return o, lse
 
 
-def backward(q, k, v, do, scale, causal, block=256):
+def backward(q, k, v, do, scale, causal, block=256, block_mask=None):
     """Full backward; dK/dV of a key/value head sum over its query heads."""
     B, Hq, Hkv, Lq, Lk, D, G = _check(q, k, v)
     res = {
@@ -185,7 +218,8 @@ def backward(q, k, v, do, scale, causal, block=256):
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            r = head_backward(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal, block=block)
+            r = head_backward(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal, block=block,
+                              block_mask=block_mask)
             for name in ("o", "lse", "delta", "dq"):
                 res[name][b, h] = r[name]
             res["dk"][b, g] += r["dk"]

@@ -286,3 +286,108 @@ def test_bf16_widening_is_exact():
     np.testing.assert_array_equal(back, torch.tensor(x).to(torch.bfloat16).double().numpy())
     b = normal_bf16_bits((3, 5), seed=7)
     np.testing.assert_array_equal(b, normal_bf16_bits((3, 5), seed=7))
+
+
+# ---------------------------------------------------------------- block-sparse mask
+# Page "feat(attention): complete Flash Attention VJP implementation", "Sparse
+# Block Masks": one uint8 entry per (query tile, key tile); here 64 x 64.
+
+
+def _expand(bm, Lq, Lk, causal):
+    """Element mask from a block mask, written independently of the oracle."""
+    m = np.repeat(np.repeat(np.asarray(bm) != 0, 64, axis=0), 64, axis=1)[:Lq, :Lk]
+    if causal:
+        m &= np.arange(Lk)[None, :] <= np.arange(Lq)[:, None] + (Lk - Lq)
+    return m
+
+
+def _torch_masked(q, k, v, do, sc, elem):
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    m = torch.tensor(elem)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=sc, enable_gqa=True)
+    o.backward(torch.tensor(do))
+    G = q.shape[1] // k.shape[1]
+    s = torch.matmul(tq.detach(), tk.detach().repeat_interleave(G, dim=1).transpose(-1, -2)) * sc
+    lse = torch.logsumexp(s.masked_fill(~m, float("-inf")), dim=-1)
+    return {"o": o.detach().numpy(), "lse": lse.numpy(), "dq": tq.grad.numpy(),
+            "dk": tk.grad.numpy(), "dv": tv.grad.numpy()}
+
+
+def _random_block_mask(Lq, Lk, causal, seed, density=0.5):
+    """Seeded block mask in which every query row keeps at least one key:
+    the block holding each row's last visible key is always kept."""
+    r = np.random.default_rng(seed)
+    nq, nk = -(-Lq // 64), -(-Lk // 64)
+    bm = (r.random((nq, nk)) < density).astype(np.uint8)
+    for qb in range(nq):
+        last_row = min(Lq, 64 * qb + 64) - 1
+        first_row = 64 * qb
+        # keep the blocks of the diagonal keys of every row in the tile
+        for i in (first_row, last_row):
+            j = min(Lk - 1, i + (Lk - Lq)) if causal else Lk - 1
+            bm[qb, j // 64] = 1
+        if causal:
+            for i in range(first_row, last_row + 1):
+                bm[qb, min(Lk - 1, i + Lk - Lq) // 64] = 1
+    return bm
+
+
+def test_all_ones_block_mask_is_dense():
+    q, k, v, do = rnd(1, 2, 130, 16), rnd(1, 1, 150, 16), rnd(1, 1, 150, 16), rnd(1, 2, 130, 16)
+    for causal in (True, False):
+        ones = np.ones((3, 3), dtype=np.uint8)
+        a = oracle.backward(q, k, v, do, 0.25, causal, block=32)
+        b = oracle.backward(q, k, v, do, 0.25, causal, block=32, block_mask=ones)
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            assert np.array_equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Lq,Lk,D,causal,seed", [
+    (1, 2, 1, 200, 200, 16, True, 1),
+    (1, 4, 2, 130, 260, 8, True, 2),     # bottom-right causal, ragged tiles
+    (2, 2, 2, 190, 140, 8, False, 3),    # dense, Lq > Lk
+    (1, 2, 1, 256, 256, 8, False, 4),
+])
+def test_block_mask_matches_torch_float64(B, Hq, Hkv, Lq, Lk, D, causal, seed):
+    q, k, v, do = rnd(B, Hq, Lq, D), rnd(B, Hkv, Lk, D), rnd(B, Hkv, Lk, D), rnd(B, Hq, Lq, D)
+    bm = _random_block_mask(Lq, Lk, causal, seed)
+    assert 0 < bm.sum() < bm.size  # some tiles kept, some skipped
+    sc = 1.0 / math.sqrt(D)
+    g = oracle.backward(q, k, v, do, sc, causal, block=48, block_mask=bm)
+    t = _torch_masked(q, k, v, do, sc, _expand(bm, Lq, Lk, causal))
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        np.testing.assert_allclose(g[n], t[n], rtol=1e-10, atol=1e-12, err_msg=n)
+
+
+def test_block_mask_rows_without_keys():
+    """A query tile whose mask row is all zero: its rows get O = 0, LSE = -inf
+    and dQ = 0, and dK/dV equal those of the problem without those rows."""
+    Lq = Lk = 192
+    q, k, v, do = rnd(1, 2, Lq, 8), rnd(1, 1, Lk, 8), rnd(1, 1, Lk, 8), rnd(1, 2, Lq, 8)
+    bm = np.ones((3, 3), dtype=np.uint8)
+    bm[1, :] = 0
+    g = oracle.backward(q, k, v, do, 0.3, False, block=40, block_mask=bm)
+    empty = slice(64, 128)
+    assert np.all(g["o"][:, :, empty] == 0) and np.all(g["dq"][:, :, empty] == 0)
+    assert np.all(np.isneginf(g["lse"][:, :, empty]))
+    keep = np.r_[0:64, 128:192]
+    elem = np.ones((128, Lk), dtype=bool)
+    t = _torch_masked(q[:, :, keep], k, v, do[:, :, keep], 0.3, elem)
+    for n in ("o", "lse", "dq"):
+        np.testing.assert_allclose(g[n][:, :, keep], t[n], rtol=1e-10, atol=1e-12, err_msg=n)
+    for n in ("dk", "dv"):
+        np.testing.assert_allclose(g[n], t[n], rtol=1e-10, atol=1e-12, err_msg=n)
+
+
+def test_block_diagonal_mask_is_independent_blocks():
+    """Non-causal block-diagonal mask: each 64-row tile attends only its own
+    64 keys, i.e. independent attention per tile (closed-form split)."""
+    L = 192
+    q, k, v, do = rnd(1, 1, L, 8), rnd(1, 1, L, 8), rnd(1, 1, L, 8), rnd(1, 1, L, 8)
+    bm = np.eye(3, dtype=np.uint8)
+    g = oracle.backward(q, k, v, do, 0.5, False, block=64, block_mask=bm)
+    for b in range(3):
+        s = slice(64 * b, 64 * b + 64)
+        t = _torch_masked(q[:, :, s], k[:, :, s], v[:, :, s], do[:, :, s], 0.5, np.ones((64, 64), dtype=bool))
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            np.testing.assert_allclose(g[n][:, :, s], t[n], rtol=1e-10, atol=1e-12, err_msg=n)
