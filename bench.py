@@ -43,6 +43,13 @@ def model_flops(B, Hq, Lq, Lk, D, causal, backward=True):
     return fwd * (3.5 if backward else 1.0), fwd
 
 
+def masked_model_flops(B, Hq, D, pairs, backward=True):
+    """The same model counted over the pairs a block mask leaves visible:
+    forward 4*D per pair, backward 2.5x that."""
+    fwd = 4.0 * B * Hq * D * pairs
+    return fwd * (3.5 if backward else 1.0), fwd
+
+
 def visible_pairs(Lq, Lk, causal):
     """Exact number of (query, key) pairs inside the mask of one head."""
     if not causal:
@@ -50,6 +57,20 @@ def visible_pairs(Lq, Lk, causal):
     # causal needs Lq <= Lk; row i sees keys 0 .. i + (Lk - Lq), never past Lk - 1
     off = Lk - Lq
     return Lq * (off + 1) + Lq * (Lq - 1) // 2
+
+
+def visible_pairs_masked(Lq, Lk, causal, mask):
+    """Exact number of visible (query, key) pairs of one head under a 64 x 64
+    block mask (and the bottom-right causal diagonal, if any)."""
+    import numpy as np
+    blk = 64
+    nkb = mask.shape[1]
+    starts = np.arange(nkb) * blk
+    ends = np.minimum(starts + blk, Lk)
+    rows = np.arange(Lq)
+    lim = (rows + (Lk - Lq) + 1) if causal else np.full(Lq, Lk)  # keys < lim are seen
+    per = np.clip(np.minimum(ends[None, :], lim[:, None]) - starts[None, :], 0, None)
+    return int((per * (mask[rows // blk] != 0)).sum())
 
 
 def unfused_score_bytes(H, L, bytes_per=2):
@@ -143,10 +164,11 @@ def summarize_pmc(fetch_csv, write_csv, workload):
 
 # ------------------------------------------------------------ CPU oracle leg
 
-def cpu_baseline(w, bits, budget_s=30.0):
+def cpu_baseline(w, bits, budget_s=30.0, mask=None, pairs=None):
     """Time the fp64 oracle on one whole GQA group (its query heads, all rows,
     forward + backward) of the same inputs; report model TFLOP/s of that
-    sample.  The group is 1/(B*Hkv) of the workload's model FLOPs."""
+    sample.  The group is 1/(B*Hkv) of the workload's model FLOPs.  Under a
+    block mask the FLOPs are those of the visible pairs (`pairs` per head)."""
     import numpy as np
 
     import oracle
@@ -163,13 +185,17 @@ def cpu_baseline(w, bits, budget_s=30.0):
     for h in range(G):
         q = oracle.bf16_bits_to_f64(bits["q"][0, h])
         do = oracle.bf16_bits_to_f64(bits["do"][0, h])
-        oracle.head_backward(q, k, v, do, w.softmax_scale, w.causal)
+        oracle.head_backward(q, k, v, do, w.softmax_scale, w.causal, block_mask=mask)
         heads_done += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    total, _ = model_flops(1, heads_done, w.Lq, w.Lk, w.D, w.causal)
-    full, _ = model_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal)
+    if mask is None:
+        total, _ = model_flops(1, heads_done, w.Lq, w.Lk, w.D, w.causal)
+        full, _ = model_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal)
+    else:
+        total, _ = masked_model_flops(1, heads_done, w.D, pairs)
+        full, _ = masked_model_flops(w.B, w.Hq, w.D, pairs)
     del np
     return {"value": total / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{heads_done} query heads of key/value head 0 (one GQA group), all {w.Lq} rows, "
@@ -308,7 +334,7 @@ def main(argv=None):
     import torch
 
     import causal_gqa_flashattention_amd as fa
-    from fa_synth import WORKLOADS, make_inputs
+    from fa_synth import WORKLOADS, block_mask_of, make_inputs
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -327,20 +353,33 @@ def main(argv=None):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     sc, causal = w.softmax_scale, w.causal
     stream = torch.cuda.current_stream()
+    mask_np = block_mask_of(w)
+    mask = None if mask_np is None else torch.from_numpy(mask_np).to(dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fa.fa_fwd(q, k, v, o, lse, scale=sc, causal=causal, stream=stream)
+        if mask is None:
+            fa.fa_fwd(q, k, v, o, lse, scale=sc, causal=causal, stream=stream)
+        else:
+            fa.fa_fwd_block_sparse(q, k, v, mask, o, lse, scale=sc, causal=causal, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         fa.fa_bwd_delta(o, do, delta, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        fa.fa_bwd_dq(q, k, v, lse, delta, do, dq, scale=sc, causal=causal, stream=stream)
+        if mask is None:
+            fa.fa_bwd_dq(q, k, v, lse, delta, do, dq, scale=sc, causal=causal, stream=stream)
+        else:
+            fa.fa_bwd_dq_block_sparse(q, k, v, lse, delta, do, mask, dq, scale=sc, causal=causal,
+                                      stream=stream)
         if ev is not None:
             ev[3].record(stream)
-        fa.fa_bwd_dkv(q, k, v, lse, delta, do, dk, dv, scale=sc, causal=causal, stream=stream)
+        if mask is None:
+            fa.fa_bwd_dkv(q, k, v, lse, delta, do, dk, dv, scale=sc, causal=causal, stream=stream)
+        else:
+            fa.fa_bwd_dkv_block_sparse(q, k, v, lse, delta, do, mask, dk, dv, scale=sc, causal=causal,
+                                       stream=stream)
         if ev is not None:
             ev[4].record(stream)
 
@@ -378,10 +417,14 @@ def main(argv=None):
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
     step_ev = np.array([e[0].elapsed_time(e[4]) for e in evs])  # first launch to last, per step
     ms_step = wall * 1e3 / args.steps
-    total_flops, fwd_flops = model_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal)
+    if mask_np is None:
+        pairs = visible_pairs(w.Lq, w.Lk, w.causal)
+        total_flops, fwd_flops = model_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal)
+    else:
+        pairs = visible_pairs_masked(w.Lq, w.Lk, w.causal, mask_np)
+        total_flops, fwd_flops = masked_model_flops(w.B, w.Hq, w.D, pairs)
     value = total_flops / (ms_step * 1e-3) / 1e12
 
-    pairs = visible_pairs(w.Lq, w.Lk, w.causal)
     work = kernel_work(w, pairs)
     kernels = {}
     for n in names:
@@ -396,9 +439,15 @@ def main(argv=None):
                 "traffic": load_traffic(dom, w.name),
                 "flop_per_launch": work[dom], "avg_launch_ms": round(per[dom], 4)}
 
+    kind = "causal" if w.causal else "dense"
+    mask_desc = ""
+    if w.mask is not None:
+        recipe = (f"sliding window {w.mask[1]} keys" + (f" + {w.mask[2]} sink block(s)" if w.mask[2] else "")
+                  if w.mask[0] == "window" else f"random density {w.mask[1]}")
+        mask_desc = f", 64x64 block mask: {recipe}, {int(mask_np.sum())}/{mask_np.size} blocks kept"
     metric = METRIC if w.name == "train8k" else (
-        f"fwd+bwd TFLOP/s, {'causal' if w.causal else 'dense'} GQA bf16 attention D={w.D} "
-        f"Lq={w.Lq} Lk={w.Lk}; % of MFMA peak")
+        f"fwd+bwd TFLOP/s{' over visible pairs' if mask_np is not None else ''}, {kind} GQA bf16 "
+        f"attention D={w.D} Lq={w.Lq} Lk={w.Lk}{mask_desc}; % of MFMA peak")
     out = {
         "metric": metric,
         "value": round(value, 2),
@@ -412,9 +461,10 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {'causal' if w.causal else 'dense'} GQA fwd+bwd, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
-                               f"Lq={w.Lq} Lk={w.Lk} D={w.D}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "Lq": w.Lq, "Lk": w.Lk, "D": w.D, "causal": w.causal},
+        "config": {"workload": f"{w.name}: {kind} GQA fwd+bwd, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
+                               f"Lq={w.Lq} Lk={w.Lk} D={w.D}{mask_desc}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Lq": w.Lq, "Lk": w.Lk, "D": w.D, "causal": w.causal,
+                   "visible_pairs_per_head": int(pairs)},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "model_tflop_per_step": round(total_flops / 1e12, 4),
         "kernels": {n: {kk: round(vv, 4) for kk, vv in d.items()} for n, d in kernels.items()},
@@ -430,7 +480,7 @@ def main(argv=None):
         ceil["dominant_kernel_frac_of_random"] = round(achieved / ceil["random_operands"], 4)
         out["mfma_ceiling"] = ceil
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, bits)
+        out["cpu_baseline"] = cpu_baseline(w, bits, mask=mask_np, pairs=pairs)
     print(json.dumps(out), flush=True)
     return 0
 

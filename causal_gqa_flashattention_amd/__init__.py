@@ -6,15 +6,24 @@ library and marshals torch tensors into it.
 """
 from .binding import (  # noqa: F401
     FAError,
+    MASK_BLOCK,
     fa_bwd,
+    fa_bwd_block_sparse,
     fa_bwd_delta,
     fa_bwd_dkv,
+    fa_bwd_dkv_block_sparse,
     fa_bwd_dq,
+    fa_bwd_dq_block_sparse,
     fa_fwd,
+    fa_fwd_block_sparse,
     lib_path,
     load_library,
     status_str,
     version,
 )
 
-__all__ = ["FAError", "fa_fwd", "fa_bwd_delta", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkv", "lib_path", "load_library", "status_str", "version"]
+__all__ = [
+    "FAError", "MASK_BLOCK", "fa_fwd", "fa_bwd_delta", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkv",
+    "fa_fwd_block_sparse", "fa_bwd_block_sparse", "fa_bwd_dq_block_sparse",
+    "fa_bwd_dkv_block_sparse", "lib_path", "load_library", "status_str", "version",
+]

@@ -1,7 +1,7 @@
 """ctypes binding of libcgqa_fa.so (argument marshalling only).
 
 The names match the C ABI in ``include/fa.h``: ``fa_fwd``, ``fa_bwd_delta``,
-``fa_bwd``.  Each takes torch tensors that live on the GPU (torch is used
+``fa_bwd``, ``fa_bwd_dq``, ``fa_bwd_dkv`` and their ``*_block_sparse`` forms.  Each takes torch tensors that live on the GPU (torch is used
 for device memory and streams only), checks dtype/contiguity/device, derives
 the sizes from the shapes and calls the library on the current stream.  Every
 step of the computation runs in the HIP kernels; there is no other path.  If
@@ -32,6 +32,10 @@ _SIGS = {
     "fa_bwd": [_vp] * 10 + [_c_int] * 6 + [_c_float, _c_int, _vp],
     "fa_bwd_dq": [_vp] * 7 + [_c_int] * 6 + [_c_float, _c_int, _vp],
     "fa_bwd_dkv": [_vp] * 8 + [_c_int] * 6 + [_c_float, _c_int, _vp],
+    "fa_fwd_block_sparse": [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp, _vp],
+    "fa_bwd_block_sparse": [_vp] * 10 + [_c_int] * 6 + [_c_float, _c_int, _vp, _vp],
+    "fa_bwd_dq_block_sparse": [_vp] * 7 + [_c_int] * 6 + [_c_float, _c_int, _vp, _vp],
+    "fa_bwd_dkv_block_sparse": [_vp] * 8 + [_c_int] * 6 + [_c_float, _c_int, _vp, _vp],
     "fa_status_str": [_c_int],
     "fa_version": [],
 }
@@ -102,8 +106,34 @@ def _require(t, name, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+MASK_BLOCK = 64  # block-sparse mask granularity (FA_MASK_BLOCK)
+
+
+def _require_mask(m, Lq, Lk):
+    shape = (-(-Lq // MASK_BLOCK), -(-Lk // MASK_BLOCK))
+    if m.dtype not in (torch.uint8, torch.bool):
+        raise TypeError(f"block_mask must be uint8 or bool, got {m.dtype}")
+    if tuple(m.shape) != shape:
+        raise ValueError(f"block_mask must be {shape} for Lq={Lq}, Lk={Lk}, got {tuple(m.shape)}")
+    if not m.is_cuda:
+        raise ValueError("block_mask must be a GPU tensor")
+    if not m.is_contiguous():
+        raise ValueError("block_mask must be contiguous")
+
+
 def fa_fwd(q, k, v, o=None, lse=None, *, scale: float, causal: bool, stream=None):
     """O, LSE = attention(q, k, v).  q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] bf16."""
+    return _fwd(q, k, v, None, o, lse, scale, causal, stream)
+
+
+def fa_fwd_block_sparse(q, k, v, block_mask, o=None, lse=None, *, scale: float, causal: bool,
+                        stream=None):
+    """fa_fwd restricted to the 64 x 64 blocks where block_mask [ceil(Lq/64), ceil(Lk/64)]
+    is nonzero.  Rows that see no key get O = 0 and lse = -inf."""
+    return _fwd(q, k, v, block_mask, o, lse, scale, causal, stream)
+
+
+def _fwd(q, k, v, mask, o, lse, scale, causal, stream):
     _require(q, "q", torch.bfloat16, 4)
     _require(k, "k", torch.bfloat16, 4)
     _require(v, "v", torch.bfloat16, 4)
@@ -119,10 +149,16 @@ def fa_fwd(q, k, v, o=None, lse=None, *, scale: float, causal: bool, stream=None
     _require(lse, "lse", torch.float32, 3)
     if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Lq):
         raise ValueError("output shapes do not match q")
-    st = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                               B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)),
-                               _stream_ptr(stream))
-    _check(st, "fa_fwd")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+            B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)))
+    lib = load_library()
+    if mask is None:
+        st, name = lib.fa_fwd(*args, _stream_ptr(stream)), "fa_fwd"
+    else:
+        _require_mask(mask, Lq, Lk)
+        st = lib.fa_fwd_block_sparse(*args, _ptr(mask), _stream_ptr(stream))
+        name = "fa_fwd_block_sparse"
+    _check(st, name)
     return o, lse
 
 
@@ -146,6 +182,16 @@ def fa_bwd_delta(o, do, delta=None, *, stream=None):
 def fa_bwd(q, k, v, o, lse, delta, do, dq=None, dk=None, dv=None, *, scale: float, causal: bool,
            stream=None):
     """dQ, dK, dV of attention given the saved lse, the precomputed delta and dO."""
+    return _bwd(q, k, v, o, lse, delta, do, None, dq, dk, dv, scale, causal, stream)
+
+
+def fa_bwd_block_sparse(q, k, v, o, lse, delta, do, block_mask, dq=None, dk=None, dv=None, *,
+                        scale: float, causal: bool, stream=None):
+    """fa_bwd under the block mask the forward used."""
+    return _bwd(q, k, v, o, lse, delta, do, block_mask, dq, dk, dv, scale, causal, stream)
+
+
+def _bwd(q, k, v, o, lse, delta, do, mask, dq, dk, dv, scale, causal, stream):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (do, "do")):
         _require(t, n, torch.bfloat16, 4)
     _require(lse, "lse", torch.float32, 3)
@@ -165,15 +211,20 @@ def fa_bwd(q, k, v, o, lse, delta, do, dq=None, dk=None, dv=None, *, scale: floa
         _require(t, n, torch.bfloat16, 4)
         if tuple(t.shape) != tuple(ref.shape):
             raise ValueError(f"{n} has the wrong shape")
-    st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(delta), _ptr(do),
-                               _ptr(dq), _ptr(dk), _ptr(dv),
-                               B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)),
-                               _stream_ptr(stream))
-    _check(st, "fa_bwd")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(delta), _ptr(do),
+            _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)))
+    lib = load_library()
+    if mask is None:
+        st, name = lib.fa_bwd(*args, _stream_ptr(stream)), "fa_bwd"
+    else:
+        _require_mask(mask, Lq, Lk)
+        st = lib.fa_bwd_block_sparse(*args, _ptr(mask), _stream_ptr(stream))
+        name = "fa_bwd_block_sparse"
+    _check(st, name)
     return dq, dk, dv
 
 
-def _bwd_half(which, q, k, v, lse, delta, do, outs, scale, causal, stream):
+def _bwd_half(which, q, k, v, lse, delta, do, outs, scale, causal, stream, mask=None):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (do, "do")):
         _require(t, n, torch.bfloat16, 4)
     _require(lse, "lse", torch.float32, 3)
@@ -185,22 +236,29 @@ def _bwd_half(which, q, k, v, lse, delta, do, outs, scale, causal, stream):
     if tuple(lse.shape) != (B, Hq, Lq) or tuple(delta.shape) != (B, Hq, Lq):
         raise ValueError("lse/delta must be [B, Hq, Lq]")
     lib = load_library()
-    tail = (B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)), _stream_ptr(stream))
+    tail = (B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)))
+    suffix = ""
+    if mask is not None:
+        _require_mask(mask, Lq, Lk)
+        tail += (_ptr(mask),)
+        suffix = "_block_sparse"
+    tail += (_stream_ptr(stream),)
+    fn = getattr(lib, "fa_bwd_" + which + suffix)
     if which == "dq":
         (dq,) = outs
         _require(dq, "dq", torch.bfloat16, 4)
         if tuple(dq.shape) != tuple(q.shape):
             raise ValueError("dq has the wrong shape")
-        st = lib.fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(delta), _ptr(do), _ptr(dq), *tail)
+        st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(delta), _ptr(do), _ptr(dq), *tail)
     else:
         dk, dv = outs
         for t, n in ((dk, "dk"), (dv, "dv")):
             _require(t, n, torch.bfloat16, 4)
             if tuple(t.shape) != tuple(k.shape):
                 raise ValueError(f"{n} has the wrong shape")
-        st = lib.fa_bwd_dkv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(delta), _ptr(do),
-                            _ptr(dk), _ptr(dv), *tail)
-    _check(st, "fa_bwd_" + which)
+        st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(delta), _ptr(do),
+                _ptr(dk), _ptr(dv), *tail)
+    _check(st, "fa_bwd_" + which + suffix)
     return outs
 
 
@@ -215,3 +273,18 @@ def fa_bwd_dkv(q, k, v, lse, delta, do, dk=None, dv=None, *, scale: float, causa
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     return _bwd_half("dkv", q, k, v, lse, delta, do, (dk, dv), scale, causal, stream)
+
+
+def fa_bwd_dq_block_sparse(q, k, v, lse, delta, do, block_mask, dq=None, *, scale: float,
+                           causal: bool, stream=None):
+    """fa_bwd_dq under a block mask."""
+    dq = torch.empty_like(q) if dq is None else dq
+    return _bwd_half("dq", q, k, v, lse, delta, do, (dq,), scale, causal, stream, block_mask)[0]
+
+
+def fa_bwd_dkv_block_sparse(q, k, v, lse, delta, do, block_mask, dk=None, dv=None, *,
+                            scale: float, causal: bool, stream=None):
+    """fa_bwd_dkv under a block mask."""
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    return _bwd_half("dkv", q, k, v, lse, delta, do, (dk, dv), scale, causal, stream, block_mask)

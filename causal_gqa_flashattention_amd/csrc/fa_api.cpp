@@ -48,6 +48,7 @@ fa_status check_sizes(int B, int Hq, int Hkv, int Lq, int Lk, int D, bool causal
   const int64_t nq = (int64_t)B * Hq * (((int64_t)Lq + 63) / 64);
   const int64_t nk = (int64_t)B * Hkv * (((int64_t)Lk + 63) / 64);
   if (nq > INT32_MAX || nk > INT32_MAX) return FA_ERR_SHAPE;
+  static_assert(FA_MASK_BLOCK == cgqa::kMaskBlock, "mask granularity");
   return FA_OK;
 }
 
@@ -89,11 +90,16 @@ const char* fa_status_str(fa_status s) {
 
 const char* fa_version(void) { return "0.1.0 gfx950"; }
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                 int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
-                 int causal, void* stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                     int causal, const unsigned char* block_mask, void* stream) {
   if (!fwd_head_dim_ok(D)) return FA_ERR_HEAD_DIM;
   FA_TRY(check_sizes(B, Hq, Hkv, Lq, Lk, D, causal != 0));
+  if (block_mask && (Lq > FA_MASK_MAX_LEN || Lk > FA_MASK_MAX_LEN)) return FA_ERR_SHAPE;
   FA_TRY(check_scale(scale));
   if (B == 0 || Hq == 0 || Lq == 0) return FA_OK;
   for (const void* p : {q, k, v, (const void*)o, (const void*)lse}) FA_TRY(check_ptr(p));
@@ -108,8 +114,26 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   a.off = Lk - Lq;
   a.nqt = 0;  // set by the launcher from the kernel's tile height
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.mask = reinterpret_cast<const uint8_t*>(block_mask);
+  a.nkb = (Lk + cgqa::kMaskBlock - 1) / cgqa::kMaskBlock;
   const hipError_t e = cgqa::launch_fwd(a, D, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                 int causal, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, nullptr, stream);
+}
+
+fa_status fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                              int causal, const unsigned char* block_mask, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, block_mask, stream);
 }
 
 fa_status fa_bwd_delta(const void* o, const void* dO, float* delta,
@@ -138,9 +162,10 @@ namespace {
 fa_status bwd_common(const void* q, const void* k, const void* v, const float* lse,
                      const float* delta, const void* dO, void* dq, void* dk, void* dv,
                      int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
-                     int which, void* stream) {
+                     const unsigned char* block_mask, int which, void* stream) {
   if (!bwd_head_dim_ok(D)) return FA_ERR_HEAD_DIM;
   FA_TRY(check_sizes(B, Hq, Hkv, Lq, Lk, D, causal != 0));
+  if (block_mask && (Lq > FA_MASK_MAX_LEN || Lk > FA_MASK_MAX_LEN)) return FA_ERR_SHAPE;
   FA_TRY(check_scale(scale));
   if (B == 0 || Hq == 0) return FA_OK;
   // dk/dv are written whenever keys exist (zeros when there is no query row);
@@ -174,6 +199,8 @@ fa_status bwd_common(const void* q, const void* k, const void* v, const float* l
   a.nkt = 0;  // set by the launcher from the dK/dV kernel's key tile
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.mask = reinterpret_cast<const uint8_t*>(block_mask);
+  a.nkb = (Lk + cgqa::kMaskBlock - 1) / cgqa::kMaskBlock;
   const hipError_t e = cgqa::launch_bwd(a, D, causal != 0, which, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -188,8 +215,18 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                  int causal, void* stream) {
   (void)o;  // O enters the backward only through delta
-  return bwd_common(q, k, v, lse, delta, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal, 3,
-                    stream);
+  return bwd_common(q, k, v, lse, delta, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal,
+                    nullptr, 3, stream);
+}
+
+fa_status fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const float* delta, const void* dO,
+                              void* dq, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                              int causal, const unsigned char* block_mask, void* stream) {
+  (void)o;
+  return bwd_common(q, k, v, lse, delta, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal,
+                    block_mask, 3, stream);
 }
 
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
@@ -197,7 +234,15 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
                     int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                     int causal, void* stream) {
   return bwd_common(q, k, v, lse, delta, dO, dq, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, D, scale,
-                    causal, 1, stream);
+                    causal, nullptr, 1, stream);
+}
+
+fa_status fa_bwd_dq_block_sparse(const void* q, const void* k, const void* v,
+                                 const float* lse, const float* delta, const void* dO, void* dq,
+                                 int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                                 int causal, const unsigned char* block_mask, void* stream) {
+  return bwd_common(q, k, v, lse, delta, dO, dq, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, D, scale,
+                    causal, block_mask, 1, stream);
 }
 
 fa_status fa_bwd_dkv(const void* q, const void* k, const void* v,
@@ -206,7 +251,16 @@ fa_status fa_bwd_dkv(const void* q, const void* k, const void* v,
                      int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                      int causal, void* stream) {
   return bwd_common(q, k, v, lse, delta, dO, nullptr, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale,
-                    causal, 2, stream);
+                    causal, nullptr, 2, stream);
+}
+
+fa_status fa_bwd_dkv_block_sparse(const void* q, const void* k, const void* v,
+                                  const float* lse, const float* delta, const void* dO,
+                                  void* dk, void* dv,
+                                  int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                                  int causal, const unsigned char* block_mask, void* stream) {
+  return bwd_common(q, k, v, lse, delta, dO, nullptr, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale,
+                    causal, block_mask, 2, stream);
 }
 
 }  // extern "C"

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void fa_delta_kernel(DeltaArgs a) {
 //   dP^T = V dO^T       (A = V from LDS, B = dO^T in registers)
 //   dS^T = P^T * (dP^T - delta)
 //   dQ^T += K^T dS^T    (A = K^T by transposed LDS reads, B = dS^T)
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs a) {
   constexpr int BM = 128;
   constexpr int P = Tile<D>::P;
@@ -96,13 +96,35 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
   if (CAUSAL) n_full = min(n_full, (q0 + off + 1) / BN);
   n_full = max(0, min(n_full, nkt));
 
+  // ---- under a block mask: the key tiles some row of this workgroup needs
+  // (dynamic LDS: up to nkt entries, then the count)
+  extern __shared__ int tlist[];
+  int nt = nkt;
+  if constexpr (MASKED) {
+    const int qb0 = q0 / kMaskBlock, qb1 = (min(q0 + BM, Lq) - 1) / kMaskBlock;
+    if (w == 0) {
+      const int cnt = build_list(tlist, nkt, lane, [](int i) { return i; }, [&](int jj) {
+        bool any = false;
+        for (int qb = qb0; qb <= qb1; ++qb) any |= a.mask[qb * a.nkb + jj * BN / kMaskBlock] != 0;
+        return any;
+      });
+      if (lane == 0) tlist[nkt] = cnt;
+    }
+    __syncthreads();
+    nt = __builtin_amdgcn_readfirstlane(tlist[nkt]);
+  }
+  auto tile = [&](int ti) { return MASKED ? __builtin_amdgcn_readfirstlane(tlist[ti]) : ti; };
+  const int wqb = (q0 + 32 * w) / kMaskBlock;  // mask row of this wavefront's rows
+  const bool w_rows = q0 + 32 * w < Lq;
+
   const TileLoader<D> ld(w, lane);
-  auto issue = [&](int j) {
-    bf16_t* buf = smem + (j & 1) * BUF;
+  auto issue = [&](int ti) {
+    const int j = tile(ti);
+    bf16_t* buf = smem + (ti & 1) * BUF;
     ld.template load<BN>(buf, kp, j * BN, Lk, w);
     ld.template load<BN>(buf + BN * P, vp, j * BN, Lk, w);
   };
-  if (nkt > 0) issue(0);
+  if (nt > 0) issue(0);
 
   bf16x8 qf[NKD], dof[NKD];
   {
@@ -113,7 +135,9 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
       dof[kd] = as_bf16x8(ldg16(a.dO + (qh + qr) * D + 16 * kd + 8 * lg));
     }
   }
-  // rows past Lq: lse = +inf makes every P exactly 0
+  // rows past Lq: lse = +inf makes every P exactly 0.  (A row that sees no
+  // key under a block mask has LSE = -inf; it meets only diagonal tiles, whose
+  // mask zeroes its P.)
   const float lse2 = row_ok ? a.lse[qh + qrow] * kLog2e : INFINITY;
   const float dl = row_ok ? a.delta[qh + qrow] : 0.f;
 
@@ -125,9 +149,13 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
 
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j < nkt; ++j) {
-    if (j + 1 < nkt) issue(j + 1);
-    const bf16_t* Ks = smem;  // + (j & 1) * BUF through the reader's offsets
+  for (int ti = 0; ti < nt; ++ti) {
+    const int j = tile(ti);
+    if (ti + 1 < nt) issue(ti + 1);
+    bool skip = false;  // this wavefront's rows do not see tile j
+    if constexpr (MASKED) skip = !w_rows || a.mask[wqb * a.nkb + j * BN / kMaskBlock] == 0;
+    if (!skip) {
+    const bf16_t* Ks = smem;  // + (ti & 1) * BUF through the reader's offsets
     const bf16_t* Vs = smem + BN * P;
 
     f32x16 s[NNB], dp[NNB];
@@ -172,6 +200,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
       for (int db = 0; db < NDB; ++db) dq[db] = mfma32(rd.trA(Ks, 16 * ks, db), dsf[ks], dq[db]);
     read_ahead<NKS * NDB, 2>();
     prio_lo();
+    }
 
     rd.flip(BUF);
     wait_vmem();
@@ -207,7 +236,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
 //   dS = P * (dP - delta)
 //   dV^T += dO^T P      (A = dO^T by transposed LDS reads, B = P)
 //   dK^T += Q^T dS      (A = Q^T by transposed LDS reads, B = dS)
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   constexpr int BN = 128;   // keys per workgroup
   constexpr int BM = 64;    // query rows per tile (two halves of 32)
@@ -248,7 +277,27 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   // first and heads innermost, so the workgroups of one key/value head (placed
   // on one XCD) read the same Q/dO tile at about the same time and share it
   // in L2, whatever their first tile.
-  const int niter = G * nq;
+  // ---- under a block mask: the query tiles (last first) that some key of
+  // this workgroup sees (dynamic LDS: up to nq entries, then the count)
+  extern __shared__ int qlist[];
+  int nql = nq;
+  if constexpr (MASKED) {
+    const int kb0 = k0 / kMaskBlock, kb1 = (min(k0 + BN, Lk) - 1) / kMaskBlock;
+    if (w == 0) {
+      const int cnt = build_list(qlist, nq, lane, [&](int i) { return nqt - 1 - i; }, [&](int qtl) {
+        bool any = false;
+        for (int kbk = kb0; kbk <= kb1; ++kbk) any |= a.mask[qtl * a.nkb + kbk] != 0;
+        return any;
+      });
+      if (lane == 0) qlist[nq] = cnt;
+    }
+    __syncthreads();
+    nql = __builtin_amdgcn_readfirstlane(qlist[nq]);
+  }
+  const int niter = G * nql;
+  auto qtile_of = [&](int n) { return MASKED ? __builtin_amdgcn_readfirstlane(qlist[n / G]) : nqt - 1 - n / G; };
+  const int wkb = (k0 + 32 * kb) / kMaskBlock;  // mask column of this wavefront's keys
+  const bool w_keys = k0 + 32 * kb < Lk;
 
   // the 8 waves load as two groups of four: waves 0-3 fill Q, waves 4-7 fill dO
   const int wl = w & 3;
@@ -258,7 +307,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   auto issue = [&](int n) {
     bf16_t* qt_lds = smem + (n & 1) * BUF;
     bf16_t* dt_lds = qt_lds + BM * P;
-    const int hi = n % G, qtile = nqt - 1 - n / G;
+    const int hi = n % G, qtile = qtile_of(n);
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
     const int qbase = qtile * BM;
     if (w < 4)
@@ -289,11 +338,14 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   __syncthreads();
   for (int n = 0; n < niter; ++n) {
     const int buf = n & 1;
-    const int q0 = (nqt - 1 - n / G) * BM;
+    const int q0 = qtile_of(n) * BM;
+    bool skip = false;  // this wavefront's keys do not see query tile q0 / BM
+    if constexpr (MASKED) skip = !w_keys || a.mask[(q0 / BM) * a.nkb + wkb] == 0;
     if (n + 1 < niter) issue(n + 1);
     const bf16_t* Qs = smem;            // + buf * BUF through rq's flipped offsets
     const bf16_t* Ds = smem + BM * P;
     const int r0 = 32 * qhalf;  // this wave's rows within the tile
+    if (!skip) {
 
     f32x16 s = zero16(), dp = zero16();
     prio_hi();
@@ -338,6 +390,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
         dk[db] = mfma32(rq.trA(Qs, r0 + 16 * h, db), ds[h], dk[db]);
       }
     prio_lo();
+    }
 
     rq.flip(BUF);
     wait_vmem();
@@ -397,7 +450,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
 // the products are those of fa_dkv_kernel; the two row halves' dK/dV are
 // added through LDS at the end.  (64-key workgroups: at 8192 tokens and two
 // key/value heads that is 256 workgroups, one per CU.)
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   constexpr int BN = 64;    // keys per workgroup
   constexpr int BM = 64;    // query rows per tile (two halves of 32)
@@ -434,13 +487,31 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   // first and heads innermost, so the workgroups of one key/value head (placed
   // on one XCD) read the same Q/dO tile at about the same time and share it
   // in L2, whatever their first tile.
-  const int niter = G * nq;
+  // ---- under a block mask: the query tiles (last first) that some key of
+  // this workgroup sees (dynamic LDS: up to nq entries, then the count)
+  extern __shared__ int qlist[];
+  int nql = nq;
+  if constexpr (MASKED) {
+    const int kb0 = k0 / kMaskBlock, kb1 = (min(k0 + BN, Lk) - 1) / kMaskBlock;
+    if (w == 0) {
+      const int cnt = build_list(qlist, nq, lane, [&](int i) { return nqt - 1 - i; }, [&](int qtl) {
+        bool any = false;
+        for (int kbk = kb0; kbk <= kb1; ++kbk) any |= a.mask[qtl * a.nkb + kbk] != 0;
+        return any;
+      });
+      if (lane == 0) qlist[nq] = cnt;
+    }
+    __syncthreads();
+    nql = __builtin_amdgcn_readfirstlane(qlist[nq]);
+  }
+  const int niter = G * nql;
+  auto qtile_of = [&](int n) { return MASKED ? __builtin_amdgcn_readfirstlane(qlist[n / G]) : nqt - 1 - n / G; };
 
   const TileLoader<D> ld(w, lane);
   // Q, dO and the rows' LSE (wave 0) and delta (wave 1) by direct loads
   auto issue = [&](int n) {
     bf16_t* qt_lds = smem + (n & 1) * BUF;
-    const int hi = n % G, qtile = nqt - 1 - n / G;
+    const int hi = n % G, qtile = qtile_of(n);
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
     const int qbase = qtile * BM;
     // stats first: anything the compiler reloads for them then waits on
@@ -475,7 +546,7 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   __syncthreads();
   for (int n = 0; n < niter; ++n) {
     const int buf = n & 1;
-    const int q0 = (nqt - 1 - n / G) * BM;
+    const int q0 = qtile_of(n) * BM;
     if (n + 1 < niter) issue(n + 1);
     const bf16_t* Qs = smem;  // + buf * BUF through the reader's flipped offsets
     const bf16_t* Ds = smem + BM * P;
@@ -586,23 +657,33 @@ template <int D, int BN_Q>
 static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStream_t stream) {
   BwdArgs a = a0;
   a.nkt = (a.Lk + (D > 128 ? 63 : 127)) / (D > 128 ? 64 : 128);  // keys per dK/dV workgroup
+  const bool masked = a.mask != nullptr;
+  // dynamic LDS under a block mask: each workgroup's tile list and its count
+  const size_t dq_list = masked ? ((size_t)(a.Lk + BN_Q - 1) / BN_Q + 1) * sizeof(int) : 0;
+  const size_t dkv_list = masked ? ((size_t)(a.Lq + 63) / 64 + 1) * sizeof(int) : 0;
   const int ndq = (which & 1) ? a.B * a.Hq * a.nqt : 0;
   const int ndkv = (which & 2) ? a.B * a.Hkv * a.nkt : 0;
-  if (causal) {
-    if (ndq > 0) hipLaunchKernelGGL((fa_dq_kernel<D, BN_Q, true>), dim3(ndq), dim3(256), 0, stream, a);
-    if (ndkv > 0) {
-      if constexpr (D > 128)
-        hipLaunchKernelGGL((fa_dkv_reg_kernel<D, true>), dim3(ndkv), dim3(256), 0, stream, a);
+  auto dq = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(ndq), dim3(256), dq_list, stream, a); };
+  auto dkv = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(ndkv), dim3(D > 128 ? 256 : 512), dkv_list, stream, a);
+  };
+  if (ndq > 0) {
+    if (causal)
+      masked ? dq(fa_dq_kernel<D, BN_Q, true, true>) : dq(fa_dq_kernel<D, BN_Q, true, false>);
+    else
+      masked ? dq(fa_dq_kernel<D, BN_Q, false, true>) : dq(fa_dq_kernel<D, BN_Q, false, false>);
+  }
+  if (ndkv > 0) {
+    if constexpr (D > 128) {
+      if (causal)
+        masked ? dkv(fa_dkv_reg_kernel<D, true, true>) : dkv(fa_dkv_reg_kernel<D, true, false>);
       else
-        hipLaunchKernelGGL((fa_dkv_kernel<D, true>), dim3(ndkv), dim3(512), 0, stream, a);
-    }
-  } else {
-    if (ndq > 0) hipLaunchKernelGGL((fa_dq_kernel<D, BN_Q, false>), dim3(ndq), dim3(256), 0, stream, a);
-    if (ndkv > 0) {
-      if constexpr (D > 128)
-        hipLaunchKernelGGL((fa_dkv_reg_kernel<D, false>), dim3(ndkv), dim3(256), 0, stream, a);
+        masked ? dkv(fa_dkv_reg_kernel<D, false, true>) : dkv(fa_dkv_reg_kernel<D, false, false>);
+    } else {
+      if (causal)
+        masked ? dkv(fa_dkv_kernel<D, true, true>) : dkv(fa_dkv_kernel<D, true, false>);
       else
-        hipLaunchKernelGGL((fa_dkv_kernel<D, false>), dim3(ndkv), dim3(512), 0, stream, a);
+        masked ? dkv(fa_dkv_kernel<D, false, true>) : dkv(fa_dkv_kernel<D, false, false>);
     }
   }
   return hipGetLastError();

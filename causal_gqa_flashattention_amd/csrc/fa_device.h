@@ -332,6 +332,27 @@ __device__ __forceinline__ void read_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x008, NM - MID, 0);
 }
 
+// ------------------------------------------------------------ block-sparse lists
+// Under a block mask (one byte per 64 query rows x 64 keys, nonzero = kept) a
+// workgroup visits only the tiles that some of its rows need.  One wavefront
+// builds that list in LDS: for i = 0 .. n-1 it takes candidate c = order(i)
+// and keeps it when covers(c) (some mask entry the tile touches is nonzero),
+// preserving the order.  Returns the number kept (the same in every lane).
+template <class Order, class Covers>
+__device__ __forceinline__ int build_list(int* list, int n, int lane, Order order, Covers covers) {
+  int count = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    const int c = i < n ? order(i) : 0;
+    const bool keep = i < n && covers(c);
+    const uint64_t bal = __ballot(keep);
+    const int pos = count + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+    if (keep) list[pos] = c;
+    count += __popcll(bal);
+  }
+  return count;
+}
+
 // s_waitcnt vmcnt(0), leaving expcnt/lgkmcnt unconstrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

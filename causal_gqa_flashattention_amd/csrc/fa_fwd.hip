@@ -34,7 +34,7 @@ namespace cgqa {
 // LDS reads kept this many fragments ahead of the MFMAs that use them
 constexpr int kLookahead = 6;
 
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs a) {
   constexpr int BM = 128;
   constexpr int P = Tile<D>::P;
@@ -79,13 +79,36 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
   if (CAUSAL) n_full = min(n_full, (q0 + off + 1) / BN);
   n_full = max(0, min(n_full, nkt));
 
+  // ---- under a block mask: the key tiles some row of this workgroup needs
+  // (dynamic LDS: up to nkt entries, then the count)
+  extern __shared__ int tlist[];
+  int nt = nkt;
+  if constexpr (MASKED) {
+    const int qb0 = q0 / kMaskBlock, qb1 = (min(q0 + BM, Lq) - 1) / kMaskBlock;
+    if (w == 0) {
+      const int cnt = build_list(tlist, nkt, lane, [](int i) { return i; }, [&](int jj) {
+        bool any = false;
+        for (int qb = qb0; qb <= qb1; ++qb) any |= a.mask[qb * a.nkb + jj * BN / kMaskBlock] != 0;
+        return any;
+      });
+      if (lane == 0) tlist[nkt] = cnt;
+    }
+    __syncthreads();
+    nt = __builtin_amdgcn_readfirstlane(tlist[nkt]);
+  }
+  auto tile = [&](int ti) { return MASKED ? __builtin_amdgcn_readfirstlane(tlist[ti]) : ti; };
+  // mask row of this wavefront's 32 rows (rows past Lq: none, the wave idles)
+  const int wqb = (q0 + 32 * w) / kMaskBlock;
+  const bool w_rows = q0 + 32 * w < Lq;
+
   const TileLoader<D> ld(w, lane);
-  auto issue = [&](int j) {
-    bf16_t* buf = smem + (j & 1) * BUF;
+  auto issue = [&](int ti) {
+    const int j = tile(ti);
+    bf16_t* buf = smem + (ti & 1) * BUF;
     ld.template load<BN>(buf, kp, j * BN, Lk, w);
     ld.template load<BN>(buf + BN * P, vp, j * BN, Lk, w);
   };
-  if (nkt > 0) issue(0);
+  if (nt > 0) issue(0);
 
   // ---- Q^T operand (B): lane holds query qrow, head-dim slots 16*kd + 8*lg + s
   bf16x8 qf[NKD];
@@ -95,7 +118,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
     for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qr * D + 16 * kd + 8 * lg));
   }
 
-  TileReader<D> rd(lane);  // offsets point into buffer (j & 1); flipped every tile
+  TileReader<D> rd(lane);  // offsets point into buffer (ti & 1); flipped every tile
   const float c2 = a.scale_log2;
   float m_run = -INFINITY;  // max (exp2 units) the accumulator is scaled with
   float l_run = 0.f;        // this lane's share of the running denominator
@@ -105,11 +128,14 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
 
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j < nkt; ++j) {
-    if (j + 1 < nkt) issue(j + 1);
-    const bf16_t* Ks = smem;           // + (j & 1) * BUF through the reader's offsets
+  for (int ti = 0; ti < nt; ++ti) {
+    const int j = tile(ti);
+    if (ti + 1 < nt) issue(ti + 1);
+    const bf16_t* Ks = smem;           // + (ti & 1) * BUF through the reader's offsets
     const bf16_t* Vs = smem + BN * P;
-
+    bool skip = false;  // this wavefront's rows do not see tile j
+    if constexpr (MASKED) skip = !w_rows || a.mask[wqb * a.nkb + j * BN / kMaskBlock] == 0;
+    if (!skip) {
     f32x16 s[NNB];
     prio_hi();
 #pragma unroll
@@ -175,16 +201,18 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) acc[db] = mfma32(rd.trA(Vs, 16 * ks, db), pf[ks], acc[db]);
     prio_lo();
+    }
 
     rd.flip(BUF);
     wait_vmem();
     __syncthreads();
   }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; a row that saw no
+  // key (possible only under a block mask) gets O = 0, LSE = -inf
   const float l_tot = l_run + xor32(l_run);
   if (qrow < Lq) {
-    const float inv = 1.f / l_tot;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     bf16_t* op = a.o + ((int64_t)(b * a.Hq + hq) * Lq + qrow) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -195,7 +223,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
         for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[db][4 * q4 + e] * inv);
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * q4 + 4 * lg) = v4;
       }
-    if (lg == 0) a.lse[(int64_t)(b * a.Hq + hq) * Lq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    if (lg == 0)
+      a.lse[(int64_t)(b * a.Hq + hq) * Lq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -218,7 +247,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
 // previous batch, so a tile is resident at least one phase before it is read.
 // A vector step also reads the next matrix step's K fragments into registers,
 // so that step's S products start on register operands.
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   constexpr int BM = 256;
   constexpr int P = Tile<D>::P;
@@ -270,12 +299,40 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   if (CAUSAL) n_full = min(n_full, (r0 + off + 1) / BN);
   n_full = max(0, min(n_full, wnkt));
 
+  // ---- under a block mask: the key tiles some row of this workgroup needs
+  // (dynamic LDS: up to nkt entries, then the count).  The loop runs over
+  // list positions x; tile(x) is the key tile.
+  extern __shared__ int tlist[];
+  int nt = nkt;
+  if constexpr (MASKED) {
+    const int qb0 = q0 / kMaskBlock, qb1 = (min(q0 + BM, Lq) - 1) / kMaskBlock;
+    if (w == 0) {
+      const int cnt = build_list(tlist, nkt, lane, [](int i) { return i; }, [&](int jj) {
+        bool any = false;
+        for (int qb = qb0; qb <= qb1; ++qb) any |= a.mask[qb * a.nkb + jj * BN / kMaskBlock] != 0;
+        return any;
+      });
+      if (lane == 0) tlist[nkt] = cnt;
+    }
+    __syncthreads();
+    nt = __builtin_amdgcn_readfirstlane(tlist[nkt]);
+  }
+  auto tile = [&](int x) { return MASKED ? __builtin_amdgcn_readfirstlane(tlist[x]) : x; };
+  // does this wavefront's work include list position x?
+  const int wqb = r0 / kMaskBlock;
+  auto need = [&](int x) {
+    if (x < 0 || x >= nt) return false;
+    const int jj = tile(x);
+    if (jj >= wnkt) return false;
+    return !MASKED || a.mask[wqb * a.nkb + jj * BN / kMaskBlock] != 0;
+  };
+
   const TileLoader<D> ld(w & 3, lane);
   if (w < 4) {
-    if (nkt > 0) ld.template load<BN>(sK, kp, 0, Lk, w);
-    if (nkt > 1) ld.template load<BN>(sK + TILE, kp, BN, Lk, w);
+    if (nt > 0) ld.template load<BN>(sK, kp, tile(0) * BN, Lk, w);
+    if (nt > 1) ld.template load<BN>(sK + TILE, kp, tile(1) * BN, Lk, w);
   } else {
-    if (nkt > 0) ld.template load<BN>(sV, vp, 0, Lk, w & 3);
+    if (nt > 0) ld.template load<BN>(sV, vp, tile(0) * BN, Lk, w & 3);
   }
 
   bf16x8 qf[NKD];
@@ -285,9 +342,10 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
     for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qr * D + 16 * kd + 8 * lg));
   }
 
-  // row reads (K) follow tile j of the matrix step, transposed reads (V) tile
-  // j - 1; buffer b sits b * TILE elements in, so moving from buffer j & 3 to
-  // (j + 1) & 3 is an XOR of the offsets with (j odd ? 3 : 1) * TILE
+  // row reads (K) follow list position x of the matrix step, transposed reads
+  // (V) position x - 1; buffer b sits b * TILE elements in, so moving from
+  // buffer x & 3 to (x + 1) & 3 is an XOR of the offsets with
+  // (x odd ? 3 : 1) * TILE
   TileReaderX<D> rd(lane);
   const float c2 = a.scale_log2;
   float m_run = -INFINITY;
@@ -300,14 +358,15 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   for (int nb = 0; nb < NNB; ++nb) s[nb] = zero16();
   bf16x8 pf[NKS];
 
-  // loads issued in phase 2j; returns whether this wavefront issued any
-  auto loads = [&](int j) -> bool {
+  // loads issued by matrix step x: K of position x + 2 (waves 0-3) or V of
+  // position x + 1 (waves 4-7); returns whether this wavefront issued any
+  auto loads = [&](int x) -> bool {
     if (w < 4) {
-      if (j + 2 >= nkt) return false;
-      ld.template load<BN>(sK + ((j + 2) & 3) * TILE, kp, (j + 2) * BN, Lk, w);
+      if (x + 2 >= nt) return false;
+      ld.template load<BN>(sK + ((x + 2) & 3) * TILE, kp, tile(x + 2) * BN, Lk, w);
     } else {
-      if (j + 1 >= nkt) return false;
-      ld.template load<BN>(sV + ((j + 1) & 3) * TILE, vp, (j + 1) * BN, Lk, w & 3);
+      if (x + 1 >= nt) return false;
+      ld.template load<BN>(sV + ((x + 1) & 3) * TILE, vp, tile(x + 1) * BN, Lk, w & 3);
     }
     return true;
   };
@@ -333,9 +392,9 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   // step also issues this wavefront's tile loads, so that the wavefronts in
   // their vector step never wait on a load issue, and ends with the wait for
   // its previous batch.
-  auto mstep = [&](int j) {
-    const bool issued = loads(j);
-    if (j < wnkt) {
+  auto mstep = [&](int x) {
+    const bool issued = loads(x);
+    if (need(x)) {
 #pragma unroll
       for (int nb = 0; nb < NNB; ++nb) s[nb] = zero16();
 #pragma unroll
@@ -343,7 +402,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
         for (int nb = 0; nb < NNB; ++nb) s[nb] = mfma32(kf[nb * NKD + kd], qf[kd], s[nb]);
     }
-    if (j >= 1 && j <= wnkt) {
+    if (need(x - 1)) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -360,13 +419,14 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - LA) / 2, 0);
     }
-    rd.flip_ra(((j & 1) ? 3 : 1) * TILE);
-    if (j >= 1) rd.flip_tr((((j - 1) & 1) ? 3 : 1) * TILE);
+    rd.flip_ra(((x & 1) ? 3 : 1) * TILE);
+    if (x >= 1) rd.flip_tr((((x - 1) & 1) ? 3 : 1) * TILE);
     wait_loads(issued);
   };
-  // vector step j: softmax of S(j) into P(j)
-  auto vstep = [&](int j) {
-    if (j < 0 || j >= wnkt) return;
+  // vector step x: softmax of S(tile(x)) into P
+  auto vstep = [&](int x) {
+    if (!need(x)) return;
+    const int j = tile(x);
     if (j >= n_full) {  // diagonal or ragged tile
       __asm__ volatile("");
       const int last = CAUSAL ? min(qrow + off, Lk - 1) : Lk - 1;
@@ -413,27 +473,27 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   __syncthreads();
   // 2 * (nkt + 1) phases; every wavefront passes the same barriers
   if (!grp_b) {
-    if (wnkt > 0) prefetch_k();
-    for (int j = 0; j <= nkt; ++j) {
-      mstep(j);
+    if (need(0)) prefetch_k();
+    for (int x = 0; x <= nt; ++x) {
+      mstep(x);
       __syncthreads();
-      if (j + 1 < wnkt) prefetch_k();
-      vstep(j);
+      if (need(x + 1)) prefetch_k();
+      vstep(x);
       __syncthreads();
     }
   } else {
-    for (int j = 0; j <= nkt; ++j) {
-      if (j < wnkt) prefetch_k();
-      vstep(j - 1);
+    for (int x = 0; x <= nt; ++x) {
+      if (need(x)) prefetch_k();
+      vstep(x - 1);
       __syncthreads();
-      mstep(j);
+      mstep(x);
       __syncthreads();
     }
   }
 
   const float l_tot = l_run + xor32(l_run);
   if (qrow < Lq) {
-    const float inv = 1.f / l_tot;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;  // no key seen (block mask): O = 0
     bf16_t* op = a.o + ((int64_t)(b * a.Hq + hq) * Lq + qrow) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -444,29 +504,34 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
         for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[db][4 * q4 + e] * inv);
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * q4 + 4 * lg) = v4;
       }
-    if (lg == 0) a.lse[(int64_t)(b * a.Hq + hq) * Lq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    if (lg == 0)
+      a.lse[(int64_t)(b * a.Hq + hq) * Lq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
 template <int D, int BN>
 static hipError_t launch_fwd_d(const FwdArgs& a0, bool causal, hipStream_t stream) {
   FwdArgs a = a0;
+  const bool masked = a.mask != nullptr;
+  // dynamic LDS under a block mask: the workgroup's key-tile list and its count
+  const size_t list_bytes = masked ? ((size_t)(a.Lk + BN - 1) / BN + 1) * sizeof(int) : 0;
+  auto go = [&](auto kern, int threads) {
+    hipLaunchKernelGGL(kern, dim3(a.B * a.Hq * a.nqt), dim3(threads), list_bytes, stream, a);
+  };
   // ping-pong for D = 96 and 128; at D = 64 the 4-wavefront kernel runs four
   // wavefronts per SIMD, which hides latency better (measured faster)
   if constexpr (D == 96 || D == 128) {
     a.nqt = (a.Lq + 255) / 256;
-    const int nblocks = a.B * a.Hq * a.nqt;
     if (causal)
-      hipLaunchKernelGGL((fa_fwd_pp_kernel<D, BN, true>), dim3(nblocks), dim3(512), 0, stream, a);
+      masked ? go(fa_fwd_pp_kernel<D, BN, true, true>, 512) : go(fa_fwd_pp_kernel<D, BN, true, false>, 512);
     else
-      hipLaunchKernelGGL((fa_fwd_pp_kernel<D, BN, false>), dim3(nblocks), dim3(512), 0, stream, a);
+      masked ? go(fa_fwd_pp_kernel<D, BN, false, true>, 512) : go(fa_fwd_pp_kernel<D, BN, false, false>, 512);
   } else {
     a.nqt = (a.Lq + 127) / 128;
-    const int nblocks = a.B * a.Hq * a.nqt;
     if (causal)
-      hipLaunchKernelGGL((fa_fwd_kernel<D, BN, true>), dim3(nblocks), dim3(256), 0, stream, a);
+      masked ? go(fa_fwd_kernel<D, BN, true, true>, 256) : go(fa_fwd_kernel<D, BN, true, false>, 256);
     else
-      hipLaunchKernelGGL((fa_fwd_kernel<D, BN, false>), dim3(nblocks), dim3(256), 0, stream, a);
+      masked ? go(fa_fwd_kernel<D, BN, false, true>, 256) : go(fa_fwd_kernel<D, BN, false, false>, 256);
   }
   return hipGetLastError();
 }

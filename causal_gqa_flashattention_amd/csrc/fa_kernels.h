@@ -6,6 +6,9 @@
 
 namespace cgqa {
 
+// Block-sparse mask granularity: one entry per 64 query rows x 64 keys.
+constexpr int kMaskBlock = 64;
+
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -16,6 +19,8 @@ struct FwdArgs {
   int off;          // Lk - Lq: causal diagonal offset
   int nqt;          // number of query tiles (set by launch_fwd)
   float scale_log2; // scale * log2(e)
+  const uint8_t* mask;  // block mask [ceil(Lq/64)][nkb], nonzero = kept; null: dense
+  int nkb;              // ceil(Lk / 64)
 };
 
 struct DeltaArgs {
@@ -41,6 +46,8 @@ struct BwdArgs {
   int nkt;          // key tiles (dK/dV kernel)
   float scale;
   float scale_log2;
+  const uint8_t* mask;  // block mask [ceil(Lq/64)][nkb], nonzero = kept; null: dense
+  int nkb;              // ceil(Lk / 64)
 };
 
 // Each launcher enqueues on `stream` and returns hipGetLastError().

@@ -8,6 +8,14 @@ Recipe (the same for every workload): numpy ``Generator(PCG64(seed))``
 standard normals drawn in float32, multiplied by ``sigma``, rounded to
 bfloat16 with round-to-nearest-even on the bit pattern.  Tensors are
 contiguous ``[B, H, L, D]`` with D innermost.
+
+Block masks (inputs of the block-sparse calls) are uint8
+``[ceil(Lq/64), ceil(Lk/64)]`` arrays, 1 = the 64 x 64 block is kept:
+``random_block_mask`` draws each entry Bernoulli(density) from its own
+seeded generator; ``window_block_mask`` keeps, for every query block, the
+key blocks that overlap a band of ``window`` keys ending at the block's last
+query row (bottom-right aligned, as the causal diagonal), plus the first
+``sink_blocks`` key blocks.
 """
 from __future__ import annotations
 
@@ -22,7 +30,13 @@ __all__ = [
     "AttnShape",
     "WORKLOADS",
     "make_inputs",
+    "MASK_BLOCK",
+    "random_block_mask",
+    "window_block_mask",
+    "block_mask_of",
 ]
+
+MASK_BLOCK = 64
 
 
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
@@ -62,6 +76,9 @@ class AttnShape:
     scale: float | None = None  # None -> float32(1/sqrt(D))
     backward: bool = True
     q_sigma_mult: float = 1.0  # extra factor on Q only (peaked-softmax variant)
+    # block mask recipe: None (dense), ("window", keys, sink_blocks) or
+    # ("random", density, seed)
+    mask: tuple | None = None
 
     @property
     def softmax_scale(self) -> float:
@@ -85,6 +102,11 @@ WORKLOADS = {
     "d256_8200": AttnShape("d256_8200", 1, 16, 2, 8200, 8200, 256, True, seed=4200, scale=1.0 / 16, backward=False),
     "long23k": AttnShape("long23k", 1, 32, 8, 23040, 23040, 128, True, seed=5000),
     "d256_train8k": AttnShape("d256_train8k", 1, 16, 2, 8192, 8192, 256, True, seed=6000, scale=1.0 / 16),
+    # the 8192-token training shape under a sliding-window block mask: each
+    # query block keeps the key blocks that meet the 1024 keys before its
+    # last row
+    "train8k_window": AttnShape("train8k_window", 1, 32, 8, 8192, 8192, 128, True, seed=2100,
+                                mask=("window", 1024, 0)),
 }
 
 
@@ -101,3 +123,37 @@ def make_inputs(shape: AttnShape, with_grad: bool | None = None) -> dict:
     if with_grad:
         out["do"] = normal_bf16_bits((shape.B, shape.Hq, shape.Lq, shape.D), s + 3, shape.sigma)
     return out
+
+
+def random_block_mask(Lq: int, Lk: int, density: float, seed: int) -> np.ndarray:
+    """uint8 [ceil(Lq/64), ceil(Lk/64)], each entry 1 with probability `density`."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (-(-Lq // MASK_BLOCK), -(-Lk // MASK_BLOCK))
+    return (rng.random(shape) < density).astype(np.uint8)
+
+
+def window_block_mask(Lq: int, Lk: int, window: int, sink_blocks: int = 0) -> np.ndarray:
+    """Local-attention band: query block i keeps key block j when keys
+    [64j, 64j+63] meet [last - window + 1, last], last = 64i + 63 + (Lk - Lq)
+    (the last key its last row may see under the bottom-right diagonal);
+    the first `sink_blocks` key blocks are always kept."""
+    nqb, nkb = -(-Lq // MASK_BLOCK), -(-Lk // MASK_BLOCK)
+    i = np.arange(nqb)[:, None]
+    j = np.arange(nkb)[None, :]
+    last = np.minimum(i * MASK_BLOCK + MASK_BLOCK - 1, Lq - 1) + (Lk - Lq)
+    lo = last - window + 1
+    keep = (j * MASK_BLOCK + MASK_BLOCK - 1 >= lo) & (j * MASK_BLOCK <= last)
+    keep |= j < sink_blocks
+    return keep.astype(np.uint8)
+
+
+def block_mask_of(shape: AttnShape):
+    """The workload's block mask (uint8 [ceil(Lq/64), ceil(Lk/64)]) or None."""
+    if shape.mask is None:
+        return None
+    kind = shape.mask[0]
+    if kind == "window":
+        return window_block_mask(shape.Lq, shape.Lk, shape.mask[1], shape.mask[2])
+    if kind == "random":
+        return random_block_mask(shape.Lq, shape.Lk, shape.mask[1], shape.mask[2])
+    raise ValueError(f"unknown mask recipe {shape.mask}")

@@ -118,6 +118,50 @@ fa_status fa_bwd_dkv(const void* q, const void* k, const void* v,
                      int causal, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
+/*
+ * Block-sparse variants (page "feat(attention): complete Flash Attention VJP
+ * implementation", "Sparse Block Masks": an optional uint8 mask with one
+ * entry per (query tile, key tile) pair; a zero entry skips the pair).
+ *
+ * block_mask: DEVICE pointer, owned by the caller, uint8 row-major
+ *   [ceil(Lq / FA_MASK_BLOCK)][ceil(Lk / FA_MASK_BLOCK)], one mask for every
+ *   batch entry and head.  Query i may attend key j iff
+ *   block_mask[(i / 64) * ceil(Lk / 64) + j / 64] != 0 and (when causal)
+ *   j <= i + (Lk - Lq).  Pass the same mask to the forward and backward.
+ *   NULL means no mask: the call is the plain one.  The library reads the
+ *   mask on the device; its contents are not checked.
+ * Tiles whose entries are all zero for a workgroup are not loaded or
+ * computed.  A query row that sees no key at all gets O = 0 and
+ * lse = -inf from the forward, dq = 0, and no share in dk and dv.
+ * Other arguments, checks and errors are those of the plain calls; dq, dk
+ * and dv are written in full (zeros where nothing is seen).  With a mask,
+ * Lq and Lk may not exceed FA_MASK_MAX_LEN (each workgroup keeps its list of
+ * tiles in LDS): FA_ERR_SHAPE otherwise.
+ */
+#define FA_MASK_BLOCK 64
+#define FA_MASK_MAX_LEN 262144
+
+fa_status fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                              int causal, const unsigned char* block_mask, void* stream);
+
+fa_status fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const float* delta, const void* dO,
+                              void* dq, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                              int causal, const unsigned char* block_mask, void* stream);
+
+fa_status fa_bwd_dq_block_sparse(const void* q, const void* k, const void* v,
+                                 const float* lse, const float* delta, const void* dO, void* dq,
+                                 int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                                 int causal, const unsigned char* block_mask, void* stream);
+
+fa_status fa_bwd_dkv_block_sparse(const void* q, const void* k, const void* v,
+                                  const float* lse, const float* delta, const void* dO,
+                                  void* dk, void* dv,
+                                  int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                                  int causal, const unsigned char* block_mask, void* stream);
+
 const char* fa_status_str(fa_status s);
 
 /* Library version string, e.g. "0.1.0 gfx950". */

@@ -28,14 +28,22 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_library(q, k, v, do, scale, causal, backward=True):
-    """Run fa_fwd (+ fa_bwd_delta + fa_bwd) on GPU tensors; return GPU tensors."""
+def run_library(q, k, v, do, scale, causal, backward=True, block_mask=None):
+    """Run fa_fwd (+ fa_bwd_delta + fa_bwd) on GPU tensors; return GPU tensors.
+    With a (GPU uint8) block mask the *_block_sparse calls are used."""
     import causal_gqa_flashattention_amd as fa
-    o, lse = fa.fa_fwd(q, k, v, scale=scale, causal=causal)
+    if block_mask is None:
+        o, lse = fa.fa_fwd(q, k, v, scale=scale, causal=causal)
+    else:
+        o, lse = fa.fa_fwd_block_sparse(q, k, v, block_mask, scale=scale, causal=causal)
     out = {"o": o, "lse": lse}
     if backward:
         delta = fa.fa_bwd_delta(o, do)
-        dq, dk, dv = fa.fa_bwd(q, k, v, o, lse, delta, do, scale=scale, causal=causal)
+        if block_mask is None:
+            dq, dk, dv = fa.fa_bwd(q, k, v, o, lse, delta, do, scale=scale, causal=causal)
+        else:
+            dq, dk, dv = fa.fa_bwd_block_sparse(q, k, v, o, lse, delta, do, block_mask,
+                                                scale=scale, causal=causal)
         out.update(delta=delta, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return out
@@ -64,12 +72,34 @@ def check(name: str, got: np.ndarray, ref: np.ndarray, label: str = "", atol: fl
     return st
 
 
-def oracle_full(bits: dict, scale: float, causal: bool, backward=True) -> dict:
+def oracle_full(bits: dict, scale: float, causal: bool, backward=True, block_mask=None) -> dict:
     q = oracle.bf16_bits_to_f64(bits["q"])
     k = oracle.bf16_bits_to_f64(bits["k"])
     v = oracle.bf16_bits_to_f64(bits["v"])
     if not backward:
-        o, lse = oracle.forward(q, k, v, scale, causal)
+        o, lse = oracle.forward(q, k, v, scale, causal, block_mask=block_mask)
         return {"o": o, "lse": lse}
     do = oracle.bf16_bits_to_f64(bits["do"])
-    return oracle.backward(q, k, v, do, scale, causal)
+    return oracle.backward(q, k, v, do, scale, causal, block_mask=block_mask)
+
+
+def check_masked(name: str, got: np.ndarray, ref: np.ndarray, label: str = "", empty=None) -> dict:
+    """`check` for block-masked results.  `empty` (bool over the sequence
+    axis: query rows for o, lse, dq; keys for dk, dv) marks the rows that see
+    no key / keys that no row sees: there the GPU must give exactly what the
+    oracle gives (LSE = -inf, zeros); the tolerance of `check` applies to the
+    rest."""
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    if name == "lse":
+        e = np.isneginf(ref)
+        assert np.array_equal(np.isneginf(got), e), f"{label} lse: -inf rows differ"
+        if empty is not None:
+            assert np.array_equal(e, np.broadcast_to(empty, e.shape)), f"{label}: oracle -inf rows"
+        return check(name, got[~e], ref[~e], label) if (~e).any() else {}
+    if empty is not None and np.any(empty):
+        sel = np.broadcast_to(np.asarray(empty)[:, None], got.shape[-2:])
+        sel = np.broadcast_to(sel, got.shape)
+        assert np.all(ref[sel] == 0.0), f"{label} {name}: oracle not zero where nothing is seen"
+        assert np.all(got[sel] == 0.0), f"{label} {name}: not zero where nothing is seen"
+        print(f"[parity] {label} {name}: {int(np.sum(empty))} empty rows exactly zero", flush=True)
+    return check(name, got, ref, label)

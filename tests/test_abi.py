@@ -27,7 +27,9 @@ def lib():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_bwd_delta", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkv", "fa_status_str", "fa_version"):
+    for n in ("fa_fwd", "fa_bwd_delta", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkv", "fa_status_str", "fa_version",
+              "fa_fwd_block_sparse", "fa_bwd_block_sparse", "fa_bwd_dq_block_sparse",
+              "fa_bwd_dkv_block_sparse"):
         assert n in names
 
 
@@ -82,3 +84,37 @@ def test_bwd_validation(lib):
     assert lib.fa_bwd_delta(P, P, P, 1, 2, 8, 80, None) == 4
     assert lib.fa_bwd_delta(P, 0, P, 1, 2, 8, 64, None) == 1
     assert lib.fa_bwd_delta(0, 0, 0, 1, 2, 0, 64, None) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((P, P, P, P, P, 1, 2, 1, 8, 8, 48, 0.1, 1), 4),
+    ((P, P, P, P, P, 1, 3, 2, 8, 8, 64, 0.1, 1), 5),
+    ((P, P, P, P, P, 1, 2, 1, 9, 8, 64, 0.1, 1), 6),
+    ((0, P, P, P, P, 1, 2, 1, 8, 8, 64, 0.1, 1), 1),
+    ((P, P, P + 2, P, P, 1, 2, 1, 8, 8, 64, 0.1, 1), 2),
+])
+def test_block_sparse_validation_matches_dense(lib, args, status):
+    # the mask pointer (here a fake one, or NULL) changes none of the checks
+    for m in (None, P + 1):
+        assert lib.fa_fwd_block_sparse(*args, m, None) == status
+    a = list(args[:3]) + [P] * 7
+    if args[0] == 0:
+        a[0] = 0
+    if args[2] == P + 2:
+        a[2] = P + 2
+    tail = list(args[5:])
+    assert lib.fa_bwd_block_sparse(*a, *tail, P + 1, None) == status
+    assert lib.fa_bwd_dq_block_sparse(*a[:7], *tail, P + 1, None) == status
+    assert lib.fa_bwd_dkv_block_sparse(*a[:8], *tail, P + 1, None) == status
+
+
+def test_block_sparse_empty_is_ok(lib):
+    assert lib.fa_fwd_block_sparse(0, 0, 0, 0, 0, 0, 2, 1, 8, 8, 64, 0.1, 1, 0, None) == 0
+    assert lib.fa_bwd_block_sparse(*([0] * 10), 0, 2, 1, 8, 8, 64, 0.1, 1, 0, None) == 0
+
+
+def test_block_sparse_length_limit(lib):
+    # tile lists live in LDS: Lq, Lk <= FA_MASK_MAX_LEN under a mask (plain calls are not limited)
+    big = 262144 + 64
+    assert lib.fa_fwd_block_sparse(P, P, P, P, P, 1, 1, 1, big, big, 128, 0.1, 1, P, None) == 3
+    assert lib.fa_bwd_block_sparse(*([P] * 10), 1, 1, 1, 64, big, 128, 0.1, 1, P, None) == 3

@@ -60,3 +60,23 @@ def test_executed_mfma_counts():
                 assert ratio == 1.0, (name, k, ratio)
             else:
                 assert 1.0 <= ratio < 1.05, (name, k, ratio)
+
+
+def test_visible_pairs_under_a_block_mask():
+    """The bench's pair count under a block mask is the number of True entries
+    of the oracle's visibility matrix, and reduces to the plain count for an
+    all-ones mask."""
+    import numpy as np
+
+    import bench
+    import oracle
+    from fa_synth import random_block_mask, window_block_mask
+    for Lq, Lk, causal, m in [
+        (300, 300, True, random_block_mask(300, 300, 0.5, 1)),
+        (200, 333, True, window_block_mask(200, 333, 100, 1)),
+        (333, 200, False, random_block_mask(333, 200, 0.3, 2)),
+        (257, 257, True, np.ones((5, 5), np.uint8)),
+    ]:
+        want = int(oracle.visible_mask(Lq, Lk, causal, block_mask=m).sum())
+        assert bench.visible_pairs_masked(Lq, Lk, causal, m) == want
+    assert bench.visible_pairs_masked(257, 257, True, np.ones((5, 5), np.uint8)) == bench.visible_pairs(257, 257, True)

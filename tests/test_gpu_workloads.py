@@ -17,6 +17,8 @@ checked against the fp64 oracle on what it can compute in seconds:
   library allocates nothing; a materialised fp32 score matrix would need
   63 GiB).
 """
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -106,8 +108,9 @@ def test_long23k_sampled_and_identities():
     delta = torch.empty_like(lse)
     dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
     torch.cuda.synchronize()
-    resident = torch.cuda.memory_allocated()
+    gc.collect()  # garbage of earlier tests must not be freed inside the window
     torch.cuda.reset_peak_memory_stats()
+    resident = torch.cuda.memory_allocated()
     fa.fa_fwd(g["q"], g["k"], g["v"], o, lse, scale=w.softmax_scale, causal=True)
     fa.fa_bwd_delta(o, g["do"], delta)
     fa.fa_bwd(g["q"], g["k"], g["v"], o, lse, delta, g["do"], dq, dk, dv, scale=w.softmax_scale, causal=True)
@@ -191,8 +194,9 @@ def test_memory_linear_in_length(L):
     delta = torch.empty_like(lse)
     dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
     torch.cuda.synchronize()
-    resident = torch.cuda.memory_allocated()
+    gc.collect()  # garbage of earlier tests must not be freed inside the window
     torch.cuda.reset_peak_memory_stats()
+    resident = torch.cuda.memory_allocated()
     fa.fa_fwd(g["q"], g["k"], g["v"], o, lse, scale=w.softmax_scale, causal=True)
     fa.fa_bwd_delta(o, g["do"], delta)
     fa.fa_bwd(g["q"], g["k"], g["v"], o, lse, delta, g["do"], dq, dk, dv, scale=w.softmax_scale, causal=True)
