@@ -178,13 +178,13 @@ def cpu_baseline(w, bits, budget_s=30.0, mask=None, pairs=None):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     G = w.Hq // w.Hkv
-    k = oracle.bf16_bits_to_f64(bits["k"][0, 0])
-    v = oracle.bf16_bits_to_f64(bits["v"][0, 0])
+    k = oracle.bits_to_f64(bits["k"][0, 0], w.dtype)
+    v = oracle.bits_to_f64(bits["v"][0, 0], w.dtype)
     t0 = time.perf_counter()
     heads_done = 0
     for h in range(G):
-        q = oracle.bf16_bits_to_f64(bits["q"][0, h])
-        do = oracle.bf16_bits_to_f64(bits["do"][0, h])
+        q = oracle.bits_to_f64(bits["q"][0, h], w.dtype)
+        do = oracle.bits_to_f64(bits["do"][0, h], w.dtype)
         oracle.head_backward(q, k, v, do, w.softmax_scale, w.causal, block_mask=mask)
         heads_done += 1
         if time.perf_counter() - t0 > budget_s:
@@ -345,7 +345,10 @@ def main(argv=None):
         return 0
     fa.load_library()
     bits = make_inputs(w, with_grad=True)
-    g = {n: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for n, b in bits.items()}
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+    g = {n: torch.from_numpy(b.view(np.int16)).view(tdt).to(dev) for n, b in bits.items()}
+    if w.layout == "bshd":  # [B, L, H, D] buffers seen as [B, H, L, D]; outputs follow (empty_like)
+        g = {n: t.transpose(1, 2).contiguous().transpose(1, 2) for n, t in g.items()}
     q, k, v, do = g["q"], g["k"], g["v"], g["do"]
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=dev)
@@ -356,7 +359,29 @@ def main(argv=None):
     mask_np = block_mask_of(w)
     mask = None if mask_np is None else torch.from_numpy(mask_np).to(dev)
 
+    general = w.dtype != "bf16" or w.layout != "bhld"  # fp16 or strided: the fa_*_ex calls
+
+    def step_ex(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd_ex(q, k, v, o, lse, scale=sc, causal=causal, block_mask=mask, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fa_bwd_delta_ex(o, do, delta, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fa.fa_bwd_ex(q, k, v, lse, delta, do, dq, None, None, scale=sc, causal=causal, block_mask=mask,
+                     grads="dq", stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        fa.fa_bwd_ex(q, k, v, lse, delta, do, None, dk, dv, scale=sc, causal=causal, block_mask=mask,
+                     grads="dkv", stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
     def step(ev=None):
+        if general:
+            return step_ex(ev)
         if ev is not None:
             ev[0].record(stream)
         if mask is None:
@@ -445,8 +470,10 @@ def main(argv=None):
         recipe = (f"sliding window {w.mask[1]} keys" + (f" + {w.mask[2]} sink block(s)" if w.mask[2] else "")
                   if w.mask[0] == "window" else f"random density {w.mask[1]}")
         mask_desc = f", 64x64 block mask: {recipe}, {int(mask_np.sum())}/{mask_np.size} blocks kept"
+    if w.layout == "bshd":
+        mask_desc += ", every tensor a [B, L, H, D] buffer passed as a strided view"
     metric = METRIC if w.name == "train8k" else (
-        f"fwd+bwd TFLOP/s{' over visible pairs' if mask_np is not None else ''}, {kind} GQA bf16 "
+        f"fwd+bwd TFLOP/s{' over visible pairs' if mask_np is not None else ''}, {kind} GQA {w.dtype} "
         f"attention D={w.D} Lq={w.Lq} Lk={w.Lk}{mask_desc}; % of MFMA peak")
     out = {
         "metric": metric,
@@ -459,7 +486,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {kind} GQA fwd+bwd, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
                                f"Lq={w.Lq} Lk={w.Lk} D={w.D}{mask_desc}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,

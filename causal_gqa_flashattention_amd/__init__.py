@@ -6,8 +6,13 @@ library and marshals torch tensors into it.
 """
 from .binding import (  # noqa: F401
     FAError,
+    FA_BF16,
+    FA_F16,
     MASK_BLOCK,
+    FaTensor,
     fa_bwd,
+    fa_bwd_delta_ex,
+    fa_bwd_ex,
     fa_bwd_block_sparse,
     fa_bwd_delta,
     fa_bwd_dkv,
@@ -16,6 +21,7 @@ from .binding import (  # noqa: F401
     fa_bwd_dq_block_sparse,
     fa_fwd,
     fa_fwd_block_sparse,
+    fa_fwd_ex,
     lib_path,
     load_library,
     status_str,
@@ -25,5 +31,6 @@ from .binding import (  # noqa: F401
 __all__ = [
     "FAError", "MASK_BLOCK", "fa_fwd", "fa_bwd_delta", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkv",
     "fa_fwd_block_sparse", "fa_bwd_block_sparse", "fa_bwd_dq_block_sparse",
-    "fa_bwd_dkv_block_sparse", "lib_path", "load_library", "status_str", "version",
+    "fa_bwd_dkv_block_sparse", "fa_fwd_ex", "fa_bwd_delta_ex", "fa_bwd_ex", "FaTensor", "FA_BF16",
+    "FA_F16", "lib_path", "load_library", "status_str", "version",
 ]

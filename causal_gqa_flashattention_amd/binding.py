@@ -21,10 +21,21 @@ FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_ALIGN", 3: "FA_ERR_SHAPE",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_GQA", 6: "FA_ERR_CAUSAL_LQ_GT_LK",
-    7: "FA_ERR_SCALE", 8: "FA_ERR_LAUNCH",
+    7: "FA_ERR_SCALE", 8: "FA_ERR_LAUNCH", 9: "FA_ERR_STRIDE", 10: "FA_ERR_DTYPE",
 }
 
 _c_int, _c_float, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+
+
+class FaTensor(ctypes.Structure):
+    """fa_tensor: a strided [B, H, L, D] view (element strides; D contiguous)."""
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_l", ctypes.c_int64)]
+
+
+_T = FaTensor
+FA_BF16, FA_F16 = 0, 1
+FA_GRAD_DQ, FA_GRAD_DKV = 1, 2
 
 _SIGS = {
     "fa_fwd": [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6 + [_c_float, _c_int, _vp],
@@ -32,6 +43,10 @@ _SIGS = {
     "fa_bwd": [_vp] * 10 + [_c_int] * 6 + [_c_float, _c_int, _vp],
     "fa_bwd_dq": [_vp] * 7 + [_c_int] * 6 + [_c_float, _c_int, _vp],
     "fa_bwd_dkv": [_vp] * 8 + [_c_int] * 6 + [_c_float, _c_int, _vp],
+    "fa_fwd_ex": [_T] * 4 + [_vp] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _vp, _vp],
+    "fa_bwd_delta_ex": [_T, _T, _vp] + [_c_int] * 4 + [_c_int, _vp],
+    "fa_bwd_ex": [_T] * 3 + [_vp, _vp] + [_T] * 4 + [_c_int] * 6
+                 + [_c_float, _c_int, _c_int, _vp, ctypes.c_uint, _vp],
     "fa_fwd_block_sparse": [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp, _vp],
     "fa_bwd_block_sparse": [_vp] * 10 + [_c_int] * 6 + [_c_float, _c_int, _vp, _vp],
     "fa_bwd_dq_block_sparse": [_vp] * 7 + [_c_int] * 6 + [_c_float, _c_int, _vp, _vp],
@@ -288,3 +303,122 @@ def fa_bwd_dkv_block_sparse(q, k, v, lse, delta, do, block_mask, dk=None, dv=Non
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     return _bwd_half("dkv", q, k, v, lse, delta, do, (dk, dv), scale, causal, stream, block_mask)
+
+
+# ---------------------------------------------------------------- general calls
+# fp16 or bf16, any strided [B, H, L, D] views whose last dimension is
+# contiguous (for instance [B, L, H, D] buffers seen through .transpose(1, 2),
+# or the first Lk rows of a longer K/V cache).
+
+_DTYPES = {torch.bfloat16: FA_BF16, torch.float16: FA_F16}
+
+
+def _view(t, name, dtype=None):
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"{name} must be bfloat16 or float16, got {t.dtype}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have the dtype of q ({dtype}), got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must have 4 dims [B, H, L, D], got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError(f"{name}: the head dimension must be contiguous (stride 1)")
+    return FaTensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _null_view():
+    return FaTensor(None, 0, 0, 0)
+
+
+def _out_like(ref, shape=None):
+    """A new output for `ref`'s [B, H, L, D] view: the same layout when ref is
+    a permutation of a dense buffer, else contiguous."""
+    return torch.empty_like(ref) if shape is None else torch.empty(shape, dtype=ref.dtype, device=ref.device)
+
+
+def fa_fwd_ex(q, k, v, o=None, lse=None, *, scale: float, causal: bool, block_mask=None, stream=None):
+    """fa_fwd for bf16 or fp16 strided views (and an optional block mask)."""
+    qt = _view(q, "q")
+    kt, vt = _view(k, "k", q.dtype), _view(v, "v", q.dtype)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k/v shapes do not match q")
+    o = _out_like(q) if o is None else o
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have the shape of q")
+    ot = _view(o, "o", q.dtype)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    _require(lse, "lse", torch.float32, 3)
+    if tuple(lse.shape) != (B, Hq, Lq):
+        raise ValueError("lse must be [B, Hq, Lq]")
+    mask = 0
+    if block_mask is not None:
+        _require_mask(block_mask, Lq, Lk)
+        mask = _ptr(block_mask)
+    st = load_library().fa_fwd_ex(qt, kt, vt, ot, _ptr(lse), B, Hq, Hkv, Lq, Lk, D, float(scale),
+                                  int(bool(causal)), _DTYPES[q.dtype], mask, _stream_ptr(stream))
+    _check(st, "fa_fwd_ex")
+    return o, lse
+
+
+def fa_bwd_delta_ex(o, do, delta=None, *, stream=None):
+    """fa_bwd_delta for bf16 or fp16 strided views."""
+    ot = _view(o, "o")
+    dt = _view(do, "do", o.dtype)
+    if tuple(do.shape) != tuple(o.shape):
+        raise ValueError("do must have the shape of o")
+    B, H, Lq, D = o.shape
+    if delta is None:
+        delta = torch.empty((B, H, Lq), dtype=torch.float32, device=o.device)
+    _require(delta, "delta", torch.float32, 3)
+    if tuple(delta.shape) != (B, H, Lq):
+        raise ValueError("delta must be [B, H, Lq]")
+    st = load_library().fa_bwd_delta_ex(ot, dt, _ptr(delta), B, H, Lq, D, _DTYPES[o.dtype],
+                                        _stream_ptr(stream))
+    _check(st, "fa_bwd_delta_ex")
+    return delta
+
+
+def fa_bwd_ex(q, k, v, lse, delta, do, dq=None, dk=None, dv=None, *, scale: float, causal: bool,
+              block_mask=None, grads: str = "all", stream=None):
+    """fa_bwd for bf16 or fp16 strided views.  grads: "all", "dq" or "dkv";
+    returns (dq, dk, dv) with None for what was not asked for."""
+    want = {"all": FA_GRAD_DQ | FA_GRAD_DKV, "dq": FA_GRAD_DQ, "dkv": FA_GRAD_DKV}[grads]
+    qt = _view(q, "q")
+    kt, vt, dot = _view(k, "k", q.dtype), _view(v, "v", q.dtype), _view(do, "do", q.dtype)
+    _require(lse, "lse", torch.float32, 3)
+    _require(delta, "delta", torch.float32, 3)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or tuple(do.shape) != tuple(q.shape) or k.shape[0] != B \
+            or k.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if tuple(lse.shape) != (B, Hq, Lq) or tuple(delta.shape) != (B, Hq, Lq):
+        raise ValueError("lse/delta must be [B, Hq, Lq]")
+    dqt = dkt = dvt = _null_view()
+    if want & FA_GRAD_DQ:
+        dq = _out_like(q) if dq is None else dq
+        if tuple(dq.shape) != tuple(q.shape):
+            raise ValueError("dq has the wrong shape")
+        dqt = _view(dq, "dq", q.dtype)
+    if want & FA_GRAD_DKV:
+        dk = _out_like(k) if dk is None else dk
+        dv = _out_like(v) if dv is None else dv
+        for t, n in ((dk, "dk"), (dv, "dv")):
+            if tuple(t.shape) != tuple(k.shape):
+                raise ValueError(f"{n} has the wrong shape")
+        dkt, dvt = _view(dk, "dk", q.dtype), _view(dv, "dv", q.dtype)
+    mask = 0
+    if block_mask is not None:
+        _require_mask(block_mask, Lq, Lk)
+        mask = _ptr(block_mask)
+    st = load_library().fa_bwd_ex(qt, kt, vt, _ptr(lse), _ptr(delta), dot, dqt, dkt, dvt,
+                                  B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)),
+                                  _DTYPES[q.dtype], mask, want, _stream_ptr(stream))
+    _check(st, "fa_bwd_ex")
+    return (dq if want & FA_GRAD_DQ else None,
+            dk if want & FA_GRAD_DKV else None,
+            dv if want & FA_GRAD_DKV else None)

@@ -69,6 +69,62 @@ fa_status check_scale(float scale) {
     if (st_ != FA_OK) return st_;      \
   } while (0)
 
+// A strided [B, H, L, D] operand: pointer checks, then strides.  Strides of
+// dimensions of extent 1 are never used and are ignored.  Every used stride
+// is >= 0 and a multiple of 8 elements (16-byte rows and heads), the row
+// stride is below 2^24 (tile offsets are 32-bit), and the last element's
+// offset fits in int64.  An output must not overlap itself: taken in order
+// of increasing stride, each dimension's stride is at least the span of the
+// dimensions inside it (the D elements of a row first).
+fa_status check_tensor(const fa_tensor& t, int B, int H, int L, int D, bool output) {
+  FA_TRY(check_ptr(t.data));
+  struct Dim { int64_t stride, extent; } dims[3] = {{t.stride_b, B}, {t.stride_h, H}, {t.stride_l, L}};
+  int64_t last = D;
+  for (Dim& d : dims) {
+    if (d.extent <= 1) {
+      d.stride = 0;
+      continue;
+    }
+    if (d.stride < 0 || d.stride % 8 != 0) return FA_ERR_STRIDE;
+    if (d.stride > (INT64_MAX / 4 - last) / (d.extent - 1)) return FA_ERR_SHAPE;
+    last += d.stride * (d.extent - 1);
+  }
+  if (L > 1 && t.stride_l >= (int64_t{1} << 24)) return FA_ERR_STRIDE;
+  if (output) {
+    // insertion sort of the used dimensions by stride
+    Dim used[3];
+    int n = 0;
+    for (const Dim& d : dims)
+      if (d.extent > 1) {
+        int j = n++;
+        while (j > 0 && used[j - 1].stride > d.stride) {
+          used[j] = used[j - 1];
+          --j;
+        }
+        used[j] = d;
+      }
+    int64_t span = D;  // elements covered by the dimensions inside
+    for (int j = 0; j < n; ++j) {
+      if (used[j].stride < span) return FA_ERR_STRIDE;
+      span = used[j].stride * used[j].extent;
+    }
+  }
+  return FA_OK;
+}
+
+fa_tensor dense(const void* p, int H, int L, int D) {
+  return fa_tensor{const_cast<void*>(p), (int64_t)H * L * D, (int64_t)L * D, (int64_t)D};
+}
+
+// (a row stride that check_tensor did not bound belongs to a dimension of
+// extent <= 1 and is never used)
+cgqa::Tensor to_kernel(const fa_tensor& t) {
+  const int64_t sl = t.stride_l >= 0 && t.stride_l < (int64_t{1} << 24) ? t.stride_l : 0;
+  return cgqa::Tensor{static_cast<uint16_t*>(t.data), t.stride_b, t.stride_h, (int)sl};
+}
+
+bool dtype_ok(fa_dtype d) { return d == FA_BF16 || d == FA_F16; }
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +140,9 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_CAUSAL_LQ_GT_LK: return "causal attention needs Lq <= Lk";
     case FA_ERR_SCALE: return "scale must be finite and positive";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_STRIDE:
+      return "a stride is negative, not a multiple of 8 elements or too large, or makes an output overlap itself";
+    case FA_ERR_DTYPE: return "unknown element type";
   }
   return "unknown status";
 }
@@ -94,21 +153,27 @@ const char* fa_version(void) { return "0.1.0 gfx950"; }
 
 namespace {
 
-fa_status fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
-                     int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
-                     int causal, const unsigned char* block_mask, void* stream) {
+fa_status fwd_common(const fa_tensor& q, const fa_tensor& k, const fa_tensor& v, const fa_tensor& o,
+                     float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                     int causal, fa_dtype dtype, const unsigned char* block_mask, void* stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
   if (!fwd_head_dim_ok(D)) return FA_ERR_HEAD_DIM;
   FA_TRY(check_sizes(B, Hq, Hkv, Lq, Lk, D, causal != 0));
   if (block_mask && (Lq > FA_MASK_MAX_LEN || Lk > FA_MASK_MAX_LEN)) return FA_ERR_SHAPE;
   FA_TRY(check_scale(scale));
   if (B == 0 || Hq == 0 || Lq == 0) return FA_OK;
-  for (const void* p : {q, k, v, (const void*)o, (const void*)lse}) FA_TRY(check_ptr(p));
+  for (const void* p : {(const void*)q.data, (const void*)k.data, (const void*)v.data, (const void*)o.data,
+                        (const void*)lse}) FA_TRY(check_ptr(p));
+  FA_TRY(check_tensor(q, B, Hq, Lq, D, false));
+  FA_TRY(check_tensor(k, B, Hkv, Lk, D, false));
+  FA_TRY(check_tensor(v, B, Hkv, Lk, D, false));
+  FA_TRY(check_tensor(o, B, Hq, Lq, D, true));
 
   cgqa::FwdArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<uint16_t*>(o);
+  a.q = to_kernel(q);
+  a.k = to_kernel(k);
+  a.v = to_kernel(v);
+  a.o = to_kernel(o);
   a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.G = Hq / Hkv;
   a.off = Lk - Lq;
@@ -116,83 +181,82 @@ fa_status fwd_common(const void* q, const void* k, const void* v, void* o, float
   a.scale_log2 = scale * 1.4426950408889634f;
   a.mask = reinterpret_cast<const uint8_t*>(block_mask);
   a.nkb = (Lk + cgqa::kMaskBlock - 1) / cgqa::kMaskBlock;
-  const hipError_t e = cgqa::launch_fwd(a, D, causal != 0, static_cast<hipStream_t>(stream));
+  const hipError_t e = cgqa::launch_fwd(a, D, causal != 0, dtype == FA_F16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-}  // namespace
-
-extern "C" {
-
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                 int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
-                 int causal, void* stream) {
-  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, nullptr, stream);
-}
-
-fa_status fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
-                              int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
-                              int causal, const unsigned char* block_mask, void* stream) {
-  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, block_mask, stream);
-}
-
-fa_status fa_bwd_delta(const void* o, const void* dO, float* delta,
-                       int B, int H, int Lq, int D, void* stream) {
+fa_status delta_common(const fa_tensor& o, const fa_tensor& dO, float* delta, int B, int H, int Lq,
+                       int D, fa_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
   if (!fwd_head_dim_ok(D)) return FA_ERR_HEAD_DIM;
   if (B < 0 || H < 0 || Lq < 0) return FA_ERR_SHAPE;
   const int64_t n = elems(B, H, Lq, D);
   if (n < 0) return FA_ERR_SHAPE;
   if (n == 0) return FA_OK;
-  for (const void* p : {o, dO, (const void*)delta}) FA_TRY(check_ptr(p));
+  for (const void* p : {(const void*)o.data, (const void*)dO.data, (const void*)delta}) FA_TRY(check_ptr(p));
+  FA_TRY(check_tensor(o, B, H, Lq, D, false));
+  FA_TRY(check_tensor(dO, B, H, Lq, D, false));
   cgqa::DeltaArgs a;
-  a.o = static_cast<const uint16_t*>(o);
-  a.dO = static_cast<const uint16_t*>(dO);
+  a.o = to_kernel(o);
+  a.dO = to_kernel(dO);
   a.delta = delta;
+  a.H = H;
+  a.Lq = Lq;
   a.rows = (int64_t)B * H * Lq;
-  if (a.rows / 8 > INT32_MAX) return FA_ERR_SHAPE;
-  const hipError_t e = cgqa::launch_delta(a, D, static_cast<hipStream_t>(stream));
+  if (a.rows / 8 > INT32_MAX || (int64_t)B * H > INT32_MAX) return FA_ERR_SHAPE;
+  const hipError_t e = cgqa::launch_delta(a, D, dtype == FA_F16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-}  // extern "C"
-
-namespace {
-
-// Shared body of fa_bwd / fa_bwd_dq / fa_bwd_dkv.  which: 1 = dQ, 2 = dK/dV.
-fa_status bwd_common(const void* q, const void* k, const void* v, const float* lse,
-                     const float* delta, const void* dO, void* dq, void* dk, void* dv,
-                     int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
-                     const unsigned char* block_mask, int which, void* stream) {
+// Shared body of every backward call.  which: FA_GRAD_DQ and/or FA_GRAD_DKV.
+fa_status bwd_common(const fa_tensor& q, const fa_tensor& k, const fa_tensor& v, const float* lse,
+                     const float* delta, const fa_tensor& dO, const fa_tensor& dq, const fa_tensor& dk,
+                     const fa_tensor& dv, int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                     int causal, fa_dtype dtype, const unsigned char* block_mask, unsigned which,
+                     void* stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
   if (!bwd_head_dim_ok(D)) return FA_ERR_HEAD_DIM;
   FA_TRY(check_sizes(B, Hq, Hkv, Lq, Lk, D, causal != 0));
   if (block_mask && (Lq > FA_MASK_MAX_LEN || Lk > FA_MASK_MAX_LEN)) return FA_ERR_SHAPE;
   FA_TRY(check_scale(scale));
+  which &= FA_GRAD_DQ | FA_GRAD_DKV;
   if (B == 0 || Hq == 0) return FA_OK;
   // dk/dv are written whenever keys exist (zeros when there is no query row);
   // dq only when there are query rows.
-  if (Lq == 0) which &= 2;
-  if (Lk == 0) which &= 1;
+  if (Lq == 0) which &= FA_GRAD_DKV;
+  if (Lk == 0) which &= FA_GRAD_DQ;
   if (which == 0) return FA_OK;
-  FA_TRY(check_ptr(k));
-  FA_TRY(check_ptr(v));
+  FA_TRY(check_ptr(k.data));
+  FA_TRY(check_ptr(v.data));
   if (Lq > 0)
-    for (const void* p : {q, (const void*)lse, (const void*)delta, dO}) FA_TRY(check_ptr(p));
-  if (which & 1) FA_TRY(check_ptr(dq));
-  if (which & 2) {
-    FA_TRY(check_ptr(dk));
-    FA_TRY(check_ptr(dv));
+    for (const void* p : {(const void*)q.data, (const void*)lse, (const void*)delta, (const void*)dO.data}) FA_TRY(check_ptr(p));
+  if (which & FA_GRAD_DQ) FA_TRY(check_ptr(dq.data));
+  if (which & FA_GRAD_DKV) {
+    FA_TRY(check_ptr(dk.data));
+    FA_TRY(check_ptr(dv.data));
+  }
+  FA_TRY(check_tensor(k, B, Hkv, Lk, D, false));
+  FA_TRY(check_tensor(v, B, Hkv, Lk, D, false));
+  if (Lq > 0) {
+    FA_TRY(check_tensor(q, B, Hq, Lq, D, false));
+    FA_TRY(check_tensor(dO, B, Hq, Lq, D, false));
+  }
+  if (which & FA_GRAD_DQ) FA_TRY(check_tensor(dq, B, Hq, Lq, D, true));
+  if (which & FA_GRAD_DKV) {
+    FA_TRY(check_tensor(dk, B, Hkv, Lk, D, true));
+    FA_TRY(check_tensor(dv, B, Hkv, Lk, D, true));
   }
 
   cgqa::BwdArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
+  a.q = to_kernel(q);
+  a.k = to_kernel(k);
+  a.v = to_kernel(v);
+  a.dO = to_kernel(dO);
+  a.dq = to_kernel(dq);
+  a.dk = to_kernel(dk);
+  a.dv = to_kernel(dv);
   a.lse = lse;
   a.delta = delta;
-  a.dO = static_cast<const uint16_t*>(dO);
-  a.dq = static_cast<uint16_t*>(dq);
-  a.dk = static_cast<uint16_t*>(dk);
-  a.dv = static_cast<uint16_t*>(dv);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.G = Hq / Hkv;
   a.off = Lk - Lq;
   a.nqt = (Lq + kDqBM - 1) / kDqBM;
@@ -201,13 +265,53 @@ fa_status bwd_common(const void* q, const void* k, const void* v, const float* l
   a.scale_log2 = scale * 1.4426950408889634f;
   a.mask = reinterpret_cast<const uint8_t*>(block_mask);
   a.nkb = (Lk + cgqa::kMaskBlock - 1) / cgqa::kMaskBlock;
-  const hipError_t e = cgqa::launch_bwd(a, D, causal != 0, which, static_cast<hipStream_t>(stream));
+  const hipError_t e = cgqa::launch_bwd(a, D, causal != 0, (int)which, dtype == FA_F16,
+                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
+
+// Contiguous bf16 tensors of the plain calls.
+struct Dense {
+  int B, Hq, Hkv, Lq, Lk, D;
+  fa_tensor q(const void* p) const { return dense(p, Hq, Lq, D); }
+  fa_tensor kv(const void* p) const { return dense(p, Hkv, Lk, D); }
+};
 
 }  // namespace
 
 extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                 int causal, void* stream) {
+  const Dense t{B, Hq, Hkv, Lq, Lk, D};
+  return fwd_common(t.q(q), t.kv(k), t.kv(v), t.q(o), lse, B, Hq, Hkv, Lq, Lk, D, scale, causal,
+                    FA_BF16, nullptr, stream);
+}
+
+fa_status fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
+                              int causal, const unsigned char* block_mask, void* stream) {
+  const Dense t{B, Hq, Hkv, Lq, Lk, D};
+  return fwd_common(t.q(q), t.kv(k), t.kv(v), t.q(o), lse, B, Hq, Hkv, Lq, Lk, D, scale, causal,
+                    FA_BF16, block_mask, stream);
+}
+
+fa_status fa_fwd_ex(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                    fa_dtype dtype, const unsigned char* block_mask, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, dtype, block_mask, stream);
+}
+
+fa_status fa_bwd_delta(const void* o, const void* dO, float* delta,
+                       int B, int H, int Lq, int D, void* stream) {
+  return delta_common(dense(o, H, Lq, D), dense(dO, H, Lq, D), delta, B, H, Lq, D, FA_BF16, stream);
+}
+
+fa_status fa_bwd_delta_ex(fa_tensor o, fa_tensor dO, float* delta, int B, int H, int Lq, int D,
+                          fa_dtype dtype, void* stream) {
+  return delta_common(o, dO, delta, B, H, Lq, D, dtype, stream);
+}
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const float* delta, const void* dO,
@@ -215,8 +319,10 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                  int causal, void* stream) {
   (void)o;  // O enters the backward only through delta
-  return bwd_common(q, k, v, lse, delta, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal,
-                    nullptr, 3, stream);
+  const Dense t{B, Hq, Hkv, Lq, Lk, D};
+  return bwd_common(t.q(q), t.kv(k), t.kv(v), lse, delta, t.q(dO), t.q(dq), t.kv(dk), t.kv(dv),
+                    B, Hq, Hkv, Lq, Lk, D, scale, causal, FA_BF16, nullptr, FA_GRAD_DQ | FA_GRAD_DKV,
+                    stream);
 }
 
 fa_status fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
@@ -225,24 +331,30 @@ fa_status fa_bwd_block_sparse(const void* q, const void* k, const void* v, const
                               int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                               int causal, const unsigned char* block_mask, void* stream) {
   (void)o;
-  return bwd_common(q, k, v, lse, delta, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal,
-                    block_mask, 3, stream);
+  const Dense t{B, Hq, Hkv, Lq, Lk, D};
+  return bwd_common(t.q(q), t.kv(k), t.kv(v), lse, delta, t.q(dO), t.q(dq), t.kv(dk), t.kv(dv),
+                    B, Hq, Hkv, Lq, Lk, D, scale, causal, FA_BF16, block_mask,
+                    FA_GRAD_DQ | FA_GRAD_DKV, stream);
 }
 
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
                     const float* lse, const float* delta, const void* dO, void* dq,
                     int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                     int causal, void* stream) {
-  return bwd_common(q, k, v, lse, delta, dO, dq, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, D, scale,
-                    causal, nullptr, 1, stream);
+  const Dense t{B, Hq, Hkv, Lq, Lk, D};
+  return bwd_common(t.q(q), t.kv(k), t.kv(v), lse, delta, t.q(dO), t.q(dq), t.kv(nullptr),
+                    t.kv(nullptr), B, Hq, Hkv, Lq, Lk, D, scale, causal, FA_BF16, nullptr, FA_GRAD_DQ,
+                    stream);
 }
 
 fa_status fa_bwd_dq_block_sparse(const void* q, const void* k, const void* v,
                                  const float* lse, const float* delta, const void* dO, void* dq,
                                  int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                                  int causal, const unsigned char* block_mask, void* stream) {
-  return bwd_common(q, k, v, lse, delta, dO, dq, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, D, scale,
-                    causal, block_mask, 1, stream);
+  const Dense t{B, Hq, Hkv, Lq, Lk, D};
+  return bwd_common(t.q(q), t.kv(k), t.kv(v), lse, delta, t.q(dO), t.q(dq), t.kv(nullptr),
+                    t.kv(nullptr), B, Hq, Hkv, Lq, Lk, D, scale, causal, FA_BF16, block_mask,
+                    FA_GRAD_DQ, stream);
 }
 
 fa_status fa_bwd_dkv(const void* q, const void* k, const void* v,
@@ -250,8 +362,9 @@ fa_status fa_bwd_dkv(const void* q, const void* k, const void* v,
                      void* dk, void* dv,
                      int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                      int causal, void* stream) {
-  return bwd_common(q, k, v, lse, delta, dO, nullptr, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale,
-                    causal, nullptr, 2, stream);
+  const Dense t{B, Hq, Hkv, Lq, Lk, D};
+  return bwd_common(t.q(q), t.kv(k), t.kv(v), lse, delta, t.q(dO), t.q(nullptr), t.kv(dk), t.kv(dv),
+                    B, Hq, Hkv, Lq, Lk, D, scale, causal, FA_BF16, nullptr, FA_GRAD_DKV, stream);
 }
 
 fa_status fa_bwd_dkv_block_sparse(const void* q, const void* k, const void* v,
@@ -259,8 +372,17 @@ fa_status fa_bwd_dkv_block_sparse(const void* q, const void* k, const void* v,
                                   void* dk, void* dv,
                                   int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                                   int causal, const unsigned char* block_mask, void* stream) {
-  return bwd_common(q, k, v, lse, delta, dO, nullptr, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale,
-                    causal, block_mask, 2, stream);
+  const Dense t{B, Hq, Hkv, Lq, Lk, D};
+  return bwd_common(t.q(q), t.kv(k), t.kv(v), lse, delta, t.q(dO), t.q(nullptr), t.kv(dk), t.kv(dv),
+                    B, Hq, Hkv, Lq, Lk, D, scale, causal, FA_BF16, block_mask, FA_GRAD_DKV, stream);
+}
+
+fa_status fa_bwd_ex(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, const float* delta,
+                    fa_tensor dO, fa_tensor dq, fa_tensor dk, fa_tensor dv,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                    fa_dtype dtype, const unsigned char* block_mask, unsigned grads, void* stream) {
+  return bwd_common(q, k, v, lse, delta, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal, dtype,
+                    block_mask, grads, stream);
 }
 
 }  // extern "C"

@@ -23,8 +23,9 @@ namespace cgqa {
 
 // ---------------------------------------------------------------- delta
 // delta[row] = sum_d f32(O[row, d]) * f32(dO[row, d]).  HBM-bound: each
-// thread reads 16 bytes of O and of dO; TPR threads share one row.
-template <int D>
+// thread reads 16 bytes of O and of dO; TPR threads share one row.  Rows are
+// numbered (b * H + h) * Lq + i; delta is contiguous in that order.
+template <class E, int D>
 __global__ __launch_bounds__(256) void fa_delta_kernel(DeltaArgs a) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per row
   constexpr int TPR = CPR <= 8 ? 8 : (CPR <= 16 ? 16 : 32);  // power of two >= CPR
@@ -34,11 +35,19 @@ __global__ __launch_bounds__(256) void fa_delta_kernel(DeltaArgs a) {
   const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
   float acc = 0.f;
   if (row < a.rows && sub < CPR) {
-    const uint4 uo = ldg16(a.o + row * D + sub * 8);
-    const uint4 ud = ldg16(a.dO + row * D + sub * 8);
-    const bf16x8 vo = as_bf16x8(uo), vd = as_bf16x8(ud);
+    int bh, i;  // b * H + h < 2^31 (checked on the host); i < Lq
+    if (a.rows <= INT_MAX) {  // 32-bit division where it suffices
+      bh = (int)row / a.Lq;
+      i = (int)row - bh * a.Lq;
+    } else {
+      bh = (int)(row / a.Lq);
+      i = (int)(row - (int64_t)bh * a.Lq);
+    }
+    const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+    const uint4 uo = ldg16(a.o.head(b, h) + (int64_t)i * a.o.sl + sub * 8);
+    const uint4 ud = ldg16(a.dO.head(b, h) + (int64_t)i * a.dO.sl + sub * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)vo[e], (float)vd[e], acc);
+    for (int e = 0; e < 8; ++e) acc = fmaf(E::get(uo, e), E::get(ud, e), acc);
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
@@ -54,7 +63,7 @@ __global__ __launch_bounds__(256) void fa_delta_kernel(DeltaArgs a) {
 //   dP^T = V dO^T       (A = V from LDS, B = dO^T in registers)
 //   dS^T = P^T * (dP^T - delta)
 //   dQ^T += K^T dS^T    (A = K^T by transposed LDS reads, B = dS^T)
-template <int D, int BN, bool CAUSAL, bool MASKED>
+template <class E, int D, int BN, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs a) {
   constexpr int BM = 128;
   constexpr int P = Tile<D>::P;
@@ -81,9 +90,10 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
   const int hq = hk * G + hi;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
-  const int64_t qh = (int64_t)(b * a.Hq + hq) * Lq;
-  const bf16_t* kp = a.k + ((int64_t)(b * a.Hkv + hk) * Lk) * D;
-  const bf16_t* vp = a.v + ((int64_t)(b * a.Hkv + hk) * Lk) * D;
+  const int64_t qh = (int64_t)(b * a.Hq + hq) * Lq;  // LSE and delta rows
+  const bf16_t* kp = a.k.head(b, hk);
+  const bf16_t* vp = a.v.head(b, hk);
+  const int ks = a.k.sl, vs = a.v.sl;
 
   const int q0 = qt * BM;
   const int qrow = q0 + 32 * w + lr;
@@ -117,12 +127,12 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
   const int wqb = (q0 + 32 * w) / kMaskBlock;  // mask row of this wavefront's rows
   const bool w_rows = q0 + 32 * w < Lq;
 
-  const TileLoader<D> ld(w, lane);
+  const TileLoader<D> ldk(w, lane, ks), ldv(w, lane, vs);
   auto issue = [&](int ti) {
     const int j = tile(ti);
     bf16_t* buf = smem + (ti & 1) * BUF;
-    ld.template load<BN>(buf, kp, j * BN, Lk, w);
-    ld.template load<BN>(buf + BN * P, vp, j * BN, Lk, w);
+    ldk.template load<BN>(buf, kp, j * BN, Lk, w);
+    ldv.template load<BN>(buf + BN * P, vp, j * BN, Lk, w);
   };
   if (nt > 0) issue(0);
 
@@ -131,8 +141,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
     const int qr = min(qrow, Lq - 1);
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
-      qf[kd] = as_bf16x8(ldg16(a.q + (qh + qr) * D + 16 * kd + 8 * lg));
-      dof[kd] = as_bf16x8(ldg16(a.dO + (qh + qr) * D + 16 * kd + 8 * lg));
+      qf[kd] = as_bf16x8(ldg16(a.q.head(b, hq) + (int64_t)qr * a.q.sl + 16 * kd + 8 * lg));
+      dof[kd] = as_bf16x8(ldg16(a.dO.head(b, hq) + (int64_t)qr * a.dO.sl + 16 * kd + 8 * lg));
     }
   }
   // rows past Lq: lse = +inf makes every P exactly 0.  (A row that sees no
@@ -166,8 +176,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
       dp[nb] = zero16();
 #pragma unroll
       for (int kd = 0; kd < NKD; ++kd) {
-        s[nb] = mfma32(rd.row16(Ks, nb * 32, kd), qf[kd], s[nb]);
-        dp[nb] = mfma32(rd.row16(Vs, nb * 32, kd), dof[kd], dp[nb]);
+        s[nb] = E::mma(rd.row16(Ks, nb * 32, kd), qf[kd], s[nb]);
+        dp[nb] = E::mma(rd.row16(Vs, nb * 32, kd), dof[kd], dp[nb]);
       }
     }
     read_ahead<2 * NNB * NKD, 1>();
@@ -192,12 +202,12 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
       for (int i = 0; i < 16; ++i) s[nb][i] = s[nb][i] * (dp[nb][i] - dl);  // dS^T
     bf16x8 dsf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) dsf[ks] = pack8(s[ks / 2], ks % 2);
+    for (int ks = 0; ks < NKS; ++ks) dsf[ks] = E::pack8(s[ks / 2], ks % 2);
     prio_hi();
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) dq[db] = mfma32(rd.trA(Ks, 16 * ks, db), dsf[ks], dq[db]);
+      for (int db = 0; db < NDB; ++db) dq[db] = E::mma(rd.trA(Ks, 16 * ks, db), dsf[ks], dq[db]);
     read_ahead<NKS * NDB, 2>();
     prio_lo();
     }
@@ -208,16 +218,15 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
   }
 
   if (row_ok) {
-    bf16_t* out = a.dq + (qh + qrow) * D;
+    bf16_t* out = a.dq.head(b, hq) + (int64_t)qrow * a.dq.sl;
     const float sc = a.scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(dq[db][4 * q4 + e] * sc);
-        *reinterpret_cast<bf16x4*>(out + 32 * db + 8 * q4 + 4 * lg) = v4;
+        const f32x16& c = dq[db];
+        *reinterpret_cast<uint2*>(out + 32 * db + 8 * q4 + 4 * lg) =
+            E::pack4(c[4 * q4] * sc, c[4 * q4 + 1] * sc, c[4 * q4 + 2] * sc, c[4 * q4 + 3] * sc);
       }
   }
 }
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
 //   dS = P * (dP - delta)
 //   dV^T += dO^T P      (A = dO^T by transposed LDS reads, B = P)
 //   dK^T += Q^T dS      (A = Q^T by transposed LDS reads, B = dS)
-template <int D, bool CAUSAL, bool MASKED>
+template <class E, int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   constexpr int BN = 128;   // keys per workgroup
   constexpr int BM = 64;    // query rows per tile (two halves of 32)
@@ -263,7 +272,6 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
-  const int64_t kvh = (int64_t)(b * a.Hkv + hk) * Lk;
   const int k0 = kt * BN;
   const int krow = k0 + 32 * kb + lr;
   const bool key_ok = krow < Lk;
@@ -301,27 +309,29 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
 
   // the 8 waves load as two groups of four: waves 0-3 fill Q, waves 4-7 fill dO
   const int wl = w & 3;
-  const TileLoader<D> ld(wl, lane);
+  const TileLoader<D> ld(wl, lane, w < 4 ? a.q.sl : a.dO.sl);
+  const bf16_t* const qsrc = a.q.head(b, hk * G);
+  const bf16_t* const osrc = a.dO.head(b, hk * G);
   // every load of the loop is a direct global->LDS load: Q, dO and the rows'
   // LSE (wave 0) and delta (wave 4), rows past Lq repeating the last row
   auto issue = [&](int n) {
     bf16_t* qt_lds = smem + (n & 1) * BUF;
     bf16_t* dt_lds = qt_lds + BM * P;
     const int hi = n % G, qtile = qtile_of(n);
-    const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
+    const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;  // LSE and delta rows
     const int qbase = qtile * BM;
     if (w < 4)
-      ld.template load<BM>(qt_lds, a.q + qh * D, qbase, Lq, wl);
+      ld.template load<BM>(qt_lds, qsrc + hi * a.q.sh, qbase, Lq, wl);
     else
-      ld.template load<BM>(dt_lds, a.dO + qh * D, qbase, Lq, wl);
+      ld.template load<BM>(dt_lds, osrc + hi * a.dO.sh, qbase, Lq, wl);
     if (w == 0) load_row_stat(&stat[n & 1][0][0], a.lse + qh, qbase, Lq, lane);
     if (w == 4) load_row_stat(&stat[n & 1][1][0], a.delta + qh, qbase, Lq, lane);
   };
   // K and V of this key tile, once (rows past Lk repeat the last key)
-  if (w < 4)
-    ld.template load<BN>(sK, a.k + kvh * D, k0, Lk, wl);
-  else
-    ld.template load<BN>(sV, a.v + kvh * D, k0, Lk, wl);
+  {
+    const TileLoader<D> lkv(wl, lane, w < 4 ? a.k.sl : a.v.sl);
+    lkv.template load<BN>(w < 4 ? sK : sV, w < 4 ? a.k.head(b, hk) : a.v.head(b, hk), k0, Lk, wl);
+  }
   if (niter > 0) issue(0);
 
   TileReaderX<D> rq(lane);  // Q and dO tiles: offsets flip with the buffer
@@ -351,8 +361,8 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     prio_hi();
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
-      s = mfma32(rq.row16(Qs, r0, kd), rk.row16(sK, 32 * kb, kd), s);
-      dp = mfma32(rq.row16(Ds, r0, kd), rk.row16(sV, 32 * kb, kd), dp);
+      s = E::mma(rq.row16(Qs, r0, kd), rk.row16(sK, 32 * kb, kd), s);
+      dp = E::mma(rq.row16(Ds, r0, kd), rk.row16(sV, 32 * kb, kd), dp);
     }
     // (no read-ahead pattern here: with eight wavefronts in step it only
     // bunches the LDS reads, measured slower)
@@ -379,15 +389,15 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = s[4 * i4 + e] * (dp[4 * i4 + e] - d4[e]);
     }
-    const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
-    const bf16x8 ds[2] = {pack8(dp, 0), pack8(dp, 1)};
+    const bf16x8 pf[2] = {E::pack8(s, 0), E::pack8(s, 1)};
+    const bf16x8 ds[2] = {E::pack8(dp, 0), E::pack8(dp, 1)};
     prio_hi();
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        dv[db] = mfma32(rq.trA(Ds, r0 + 16 * h, db), pf[h], dv[db]);
-        dk[db] = mfma32(rq.trA(Qs, r0 + 16 * h, db), ds[h], dk[db]);
+        dv[db] = E::mma(rq.trA(Ds, r0 + 16 * h, db), pf[h], dv[db]);
+        dk[db] = E::mma(rq.trA(Qs, r0 + 16 * h, db), ds[h], dk[db]);
       }
     prio_lo();
     }
@@ -421,21 +431,18 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   }
 
   if (w < 4 && key_ok) {
-    bf16_t* dkp = a.dk + (kvh + krow) * D;
-    bf16_t* dvp = a.dv + (kvh + krow) * D;
+    bf16_t* dkp = a.dk.head(b, hk) + (int64_t)krow * a.dk.sl;
+    bf16_t* dvp = a.dv.head(b, hk) + (int64_t)krow * a.dv.sl;
     const float sc = a.scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 k4, v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k4[e] = (__bf16)(dk[db][4 * q4 + e] * sc);
-          v4[e] = (__bf16)(dv[db][4 * q4 + e]);
-        }
-        *reinterpret_cast<bf16x4*>(dkp + 32 * db + 8 * q4 + 4 * lg) = k4;
-        *reinterpret_cast<bf16x4*>(dvp + 32 * db + 8 * q4 + 4 * lg) = v4;
+        const f32x16 &ck = dk[db], &cv = dv[db];
+        *reinterpret_cast<uint2*>(dkp + 32 * db + 8 * q4 + 4 * lg) =
+            E::pack4(ck[4 * q4] * sc, ck[4 * q4 + 1] * sc, ck[4 * q4 + 2] * sc, ck[4 * q4 + 3] * sc);
+        *reinterpret_cast<uint2*>(dvp + 32 * db + 8 * q4 + 4 * lg) =
+            E::pack4(cv[4 * q4], cv[4 * q4 + 1], cv[4 * q4 + 2], cv[4 * q4 + 3]);
       }
   }
 }
@@ -450,7 +457,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
 // the products are those of fa_dkv_kernel; the two row halves' dK/dV are
 // added through LDS at the end.  (64-key workgroups: at 8192 tokens and two
 // key/value heads that is 256 workgroups, one per CU.)
-template <int D, bool CAUSAL, bool MASKED>
+template <class E, int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   constexpr int BN = 64;    // keys per workgroup
   constexpr int BM = 64;    // query rows per tile (two halves of 32)
@@ -474,7 +481,6 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
-  const int64_t kvh = (int64_t)(b * a.Hkv + hk) * Lk;
   const int k0 = kt * BN;
   const int krow = k0 + 32 * kb + lr;
   const bool key_ok = krow < Lk;
@@ -507,7 +513,9 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   const int niter = G * nql;
   auto qtile_of = [&](int n) { return MASKED ? __builtin_amdgcn_readfirstlane(qlist[n / G]) : nqt - 1 - n / G; };
 
-  const TileLoader<D> ld(w, lane);
+  const TileLoader<D> ldq(w, lane, a.q.sl), ldo(w, lane, a.dO.sl);
+  const bf16_t* const qsrc = a.q.head(b, hk * G);
+  const bf16_t* const osrc = a.dO.head(b, hk * G);
   // Q, dO and the rows' LSE (wave 0) and delta (wave 1) by direct loads
   auto issue = [&](int n) {
     bf16_t* qt_lds = smem + (n & 1) * BUF;
@@ -518,8 +526,8 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     // nothing but its own load
     if (w == 0) load_row_stat(&stat[n & 1][0][0], a.lse + qh, qbase, Lq, lane);
     if (w == 1) load_row_stat(&stat[n & 1][1][0], a.delta + qh, qbase, Lq, lane);
-    ld.template load<BM>(qt_lds, a.q + qh * D, qbase, Lq, w);
-    ld.template load<BM>(qt_lds + BM * P, a.dO + qh * D, qbase, Lq, w);
+    ldq.template load<BM>(qt_lds, qsrc + hi * a.q.sh, qbase, Lq, w);
+    ldo.template load<BM>(qt_lds + BM * P, osrc + hi * a.dO.sh, qbase, Lq, w);
   };
   if (niter > 0) issue(0);
 
@@ -528,8 +536,8 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     const int kr = min(krow, Lk - 1);  // keys past Lk: a copy, never stored
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
-      kf[kd] = as_bf16x8(ldg16(a.k + (kvh + kr) * D + 16 * kd + 8 * lg));
-      vf[kd] = as_bf16x8(ldg16(a.v + (kvh + kr) * D + 16 * kd + 8 * lg));
+      kf[kd] = as_bf16x8(ldg16(a.k.head(b, hk) + (int64_t)kr * a.k.sl + 16 * kd + 8 * lg));
+      vf[kd] = as_bf16x8(ldg16(a.v.head(b, hk) + (int64_t)kr * a.v.sl + 16 * kd + 8 * lg));
     }
   }
 
@@ -554,8 +562,8 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     f32x16 s = zero16(), dp = zero16();
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
-      s = mfma32(rd.row16(Qs, r0, kd), kf[kd], s);
-      dp = mfma32(rd.row16(Ds, r0, kd), vf[kd], dp);
+      s = E::mma(rd.row16(Qs, r0, kd), kf[kd], s);
+      dp = E::mma(rd.row16(Ds, r0, kd), vf[kd], dp);
     }
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
@@ -577,14 +585,14 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = s[4 * i4 + e] * (dp[4 * i4 + e] - d4[e]);
     }
-    const bf16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 1);
-    const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 1);
+    const bf16x8 pf0 = E::pack8(s, 0), pf1 = E::pack8(s, 1);
+    const bf16x8 ds0 = E::pack8(dp, 0), ds1 = E::pack8(dp, 1);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      dv[db] = mfma32(rd.trA(Ds, r0, db), pf0, dv[db]);
-      dv[db] = mfma32(rd.trA(Ds, r0 + 16, db), pf1, dv[db]);
-      dk[db] = mfma32(rd.trA(Qs, r0, db), ds0, dk[db]);
-      dk[db] = mfma32(rd.trA(Qs, r0 + 16, db), ds1, dk[db]);
+      dv[db] = E::mma(rd.trA(Ds, r0, db), pf0, dv[db]);
+      dv[db] = E::mma(rd.trA(Ds, r0 + 16, db), pf1, dv[db]);
+      dk[db] = E::mma(rd.trA(Qs, r0, db), ds0, dk[db]);
+      dk[db] = E::mma(rd.trA(Qs, r0 + 16, db), ds1, dk[db]);
     }
 
     rd.flip(BUF);
@@ -616,44 +624,46 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   }
 
   if (qhalf == 0 && key_ok) {
-    bf16_t* dkp = a.dk + (kvh + krow) * D;
-    bf16_t* dvp = a.dv + (kvh + krow) * D;
+    bf16_t* dkp = a.dk.head(b, hk) + (int64_t)krow * a.dk.sl;
+    bf16_t* dvp = a.dv.head(b, hk) + (int64_t)krow * a.dv.sl;
     const float sc = a.scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 k4, v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k4[e] = (__bf16)(dk[db][4 * q4 + e] * sc);
-          v4[e] = (__bf16)(dv[db][4 * q4 + e]);
-        }
-        *reinterpret_cast<bf16x4*>(dkp + 32 * db + 8 * q4 + 4 * lg) = k4;
-        *reinterpret_cast<bf16x4*>(dvp + 32 * db + 8 * q4 + 4 * lg) = v4;
+        const f32x16 &ck = dk[db], &cv = dv[db];
+        *reinterpret_cast<uint2*>(dkp + 32 * db + 8 * q4 + 4 * lg) =
+            E::pack4(ck[4 * q4] * sc, ck[4 * q4 + 1] * sc, ck[4 * q4 + 2] * sc, ck[4 * q4 + 3] * sc);
+        *reinterpret_cast<uint2*>(dvp + 32 * db + 8 * q4 + 4 * lg) =
+            E::pack4(cv[4 * q4], cv[4 * q4 + 1], cv[4 * q4 + 2], cv[4 * q4 + 3]);
       }
   }
 }
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t stream) {
+template <class E>
+static hipError_t launch_delta_e(const DeltaArgs& a, int D, hipStream_t stream) {
   auto go = [&](auto kern, int tpr) {
     const int rpb = 256 / tpr;
     const int64_t nblocks = (a.rows + rpb - 1) / rpb;
     hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(256), 0, stream, a);
   };
   switch (D) {
-    case 64: go(fa_delta_kernel<64>, 8); break;
-    case 96: go(fa_delta_kernel<96>, 16); break;
-    case 128: go(fa_delta_kernel<128>, 16); break;
-    case 256: go(fa_delta_kernel<256>, 32); break;
+    case 64: go(fa_delta_kernel<E, 64>, 8); break;
+    case 96: go(fa_delta_kernel<E, 96>, 16); break;
+    case 128: go(fa_delta_kernel<E, 128>, 16); break;
+    case 256: go(fa_delta_kernel<E, 256>, 32); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int D, int BN_Q>
+hipError_t launch_delta(const DeltaArgs& a, int D, bool f16, hipStream_t stream) {
+  return f16 ? launch_delta_e<FP16>(a, D, stream) : launch_delta_e<BF16>(a, D, stream);
+}
+
+template <class E, int D, int BN_Q>
 static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStream_t stream) {
   BwdArgs a = a0;
   a.nkt = (a.Lk + (D > 128 ? 63 : 127)) / (D > 128 ? 64 : 128);  // keys per dK/dV workgroup
@@ -669,34 +679,39 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
   };
   if (ndq > 0) {
     if (causal)
-      masked ? dq(fa_dq_kernel<D, BN_Q, true, true>) : dq(fa_dq_kernel<D, BN_Q, true, false>);
+      masked ? dq(fa_dq_kernel<E, D, BN_Q, true, true>) : dq(fa_dq_kernel<E, D, BN_Q, true, false>);
     else
-      masked ? dq(fa_dq_kernel<D, BN_Q, false, true>) : dq(fa_dq_kernel<D, BN_Q, false, false>);
+      masked ? dq(fa_dq_kernel<E, D, BN_Q, false, true>) : dq(fa_dq_kernel<E, D, BN_Q, false, false>);
   }
   if (ndkv > 0) {
     if constexpr (D > 128) {
       if (causal)
-        masked ? dkv(fa_dkv_reg_kernel<D, true, true>) : dkv(fa_dkv_reg_kernel<D, true, false>);
+        masked ? dkv(fa_dkv_reg_kernel<E, D, true, true>) : dkv(fa_dkv_reg_kernel<E, D, true, false>);
       else
-        masked ? dkv(fa_dkv_reg_kernel<D, false, true>) : dkv(fa_dkv_reg_kernel<D, false, false>);
+        masked ? dkv(fa_dkv_reg_kernel<E, D, false, true>) : dkv(fa_dkv_reg_kernel<E, D, false, false>);
     } else {
       if (causal)
-        masked ? dkv(fa_dkv_kernel<D, true, true>) : dkv(fa_dkv_kernel<D, true, false>);
+        masked ? dkv(fa_dkv_kernel<E, D, true, true>) : dkv(fa_dkv_kernel<E, D, true, false>);
       else
-        masked ? dkv(fa_dkv_kernel<D, false, true>) : dkv(fa_dkv_kernel<D, false, false>);
+        masked ? dkv(fa_dkv_kernel<E, D, false, true>) : dkv(fa_dkv_kernel<E, D, false, false>);
     }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, hipStream_t stream) {
+template <class E>
+static hipError_t launch_bwd_e(const BwdArgs& a, int D, bool causal, int which, hipStream_t stream) {
   switch (D) {
-    case 64: return launch_bwd_d<64, 64>(a, causal, which, stream);
-    case 96: return launch_bwd_d<96, 64>(a, causal, which, stream);
-    case 128: return launch_bwd_d<128, 64>(a, causal, which, stream);
-    case 256: return launch_bwd_d<256, 32>(a, causal, which, stream);
+    case 64: return launch_bwd_d<E, 64, 64>(a, causal, which, stream);
+    case 96: return launch_bwd_d<E, 96, 64>(a, causal, which, stream);
+    case 128: return launch_bwd_d<E, 128, 64>(a, causal, which, stream);
+    case 256: return launch_bwd_d<E, 256, 32>(a, causal, which, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, bool f16, hipStream_t stream) {
+  return f16 ? launch_bwd_e<FP16>(a, D, causal, which, stream) : launch_bwd_e<BF16>(a, D, causal, which, stream);
 }
 
 }  // namespace cgqa

@@ -1,7 +1,7 @@
 // Device-side building blocks shared by the attention kernels (gfx950 only).
 //
-// Matrix-core contraction: v_mfma_f32_32x32x16_bf16, one 64-lane wavefront
-// computes C[32x32] += A[32x16] * B[16x32] in fp32.  Lane layout (checked on
+// Matrix-core contraction: v_mfma_f32_32x32x16_bf16 (or _f16), one 64-lane
+// wavefront computes C[32x32] += A[32x16] * B[16x32] in fp32.  Lane layout (checked on
 // the device):
 //   A operand: lane l holds row (l % 32), k = 8*(l / 32) + s, s = 0..7
 //   B operand: lane l holds column (l % 32), the same k slots
@@ -27,16 +27,60 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint16_t bf16_t;  // storage type of a bfloat16 in global memory
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // storage type of a 16-bit element in global memory and LDS
 
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+// ------------------------------------------------------------ element formats
+// Q, K, V, O, dO and the gradients are bfloat16 (BF16) or IEEE half (FP16).
+// Operand fragments travel as 16-bit payloads in bf16x8 registers in either
+// case; only the matrix instruction (v_mfma_f32_32x32x16_bf16 / _f16, same
+// lane layout) and the conversions from and to fp32 read them as numbers.
+// Conversions from fp32 round to nearest even.
+struct BF16 {
+  __device__ __forceinline__ static f32x16 mma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // registers 8*half .. 8*half+7 of a C-layout result as an operand fragment
+  __device__ __forceinline__ static bf16x8 pack8(const f32x16& c, int half) {
+    bf16x8 r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r[s] = (__bf16)c[8 * half + s];
+    return r;
+  }
+  __device__ __forceinline__ static uint2 pack4(float x0, float x1, float x2, float x3) {
+    const bf16x4 r = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+    return __builtin_bit_cast(uint2, r);
+  }
+  __device__ __forceinline__ static float get(const uint4& u, int e) {
+    return (float)__builtin_bit_cast(bf16x8, u)[e];
+  }
+};
+
+struct FP16 {
+  __device__ __forceinline__ static f32x16 mma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                  c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static bf16x8 pack8(const f32x16& c, int half) {
+    f16x8 r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r[s] = (_Float16)c[8 * half + s];
+    return __builtin_bit_cast(bf16x8, r);
+  }
+  __device__ __forceinline__ static uint2 pack4(float x0, float x1, float x2, float x3) {
+    const f16x4 r = {(_Float16)x0, (_Float16)x1, (_Float16)x2, (_Float16)x3};
+    return __builtin_bit_cast(uint2, r);
+  }
+  __device__ __forceinline__ static float get(const uint4& u, int e) {
+    return (float)__builtin_bit_cast(f16x8, u)[e];
+  }
+};
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -47,15 +91,6 @@ __device__ __forceinline__ f32x16 zero16() {
 
 // Row of the C/D layout held by register i of lane group g = lane / 32.
 __device__ __forceinline__ constexpr int crow(int i, int g) { return 8 * (i / 4) + 4 * g + (i % 4); }
-
-// Eight consecutive fp32 registers (C-layout rows of one 16-wide k step) to a
-// bf16 operand fragment, round-to-nearest-even.
-__device__ __forceinline__ bf16x8 pack8(const f32x16& c, int half) {
-  bf16x8 r;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) r[s] = (__bf16)c[8 * half + s];
-  return r;
-}
 
 // Wave priority around matrix-core phases: a wave about to issue a run of
 // MFMAs asks the sequencer to prefer it, so a co-resident wave's vector work
@@ -228,7 +263,8 @@ struct TileReaderX {
   }
 };
 
-// Direct global->LDS copy of a ROWS x D bf16 tile into the swizzled layout.
+// Direct global->LDS copy of a ROWS x D tile of 16-bit elements into the
+// swizzled layout.
 // Load round i of wave w fills the 1 KiB block 4*i + w of the tile, i.e. tile
 // rows 4*RW*i + RW*w + lane / PC (RW = 64 / PC rows per block), physical
 // chunk lane % PC; the lane's source chunk follows from the row's swizzle.
@@ -239,13 +275,19 @@ struct TileLoader {
   static constexpr int RW = 64 / PC;  // tile rows per wave block
   int rl;    // this lane's row within a round's rows
   int x;     // physical chunk this lane fills
-  __device__ __forceinline__ TileLoader(int w, int lane) : rl(RW * w + lane / PC), x(lane % PC) {}
+  int rs;     // row stride of the source in elements (wave-uniform; rs * 128 < 2^31)
+  int rstep;  // 4 * RW * rs: source elements between two load rounds
+  int lro;    // rl * rs
+  __device__ __forceinline__ TileLoader(int w, int lane, int row_stride)
+      : rl(RW * w + lane / PC), x(lane % PC), rs(row_stride), rstep(4 * RW * row_stride),
+        lro(rl * row_stride) {}
   __device__ __forceinline__ int src_off(int r) const {  // element offset within the source row
     int c = x ^ T::swz(r);
     return (c < CPR ? c : 0) * 8;  // padding slots (D = 96): any in-bounds data
   }
-  // Rows row0 .. row0+ROWS-1 of `g` (row stride D).  Rows at or past `nrows`
-  // repeat row nrows-1, which keeps every value finite; kernels mask them.
+  // Rows row0 .. row0+ROWS-1 of `g`, whose rows sit rs elements apart (the
+  // D elements of a row contiguous).  Rows at or past `nrows` repeat row
+  // nrows-1, which keeps every value finite; kernels mask them.
   // Each wave issues ROWS*PC/256 loads of 64 x 16 bytes; the caller waits on
   // vmcnt and synchronises before reading.  ASM issues them as inline
   // assembly (see lds_dma16); without it they go through the compiler's
@@ -254,17 +296,18 @@ struct TileLoader {
   __device__ __forceinline__ void load(bf16_t* tile, const bf16_t* g, int row0, int nrows, int w) const {
     constexpr int ROUNDS = ROWS * PC / 256;
     static_assert(ROWS * PC % 256 == 0, "tile must split evenly over four waves");
+    const bf16_t* const g0 = g + (int64_t)row0 * rs;  // wave-uniform
     if (row0 + ROWS <= nrows) {
       // whole tile: the per-lane offsets do not depend on the tile, so they
       // stay in registers across the loop; the row step goes in the scalar base
 #pragma unroll
       for (int i = 0; i < ROUNDS; ++i) {
         const int r = 4 * RW * i + rl;
-        const bf16_t* base = g + (int64_t)(row0 + 4 * RW * i) * D;  // wave-uniform
+        const bf16_t* base = g0 + i * rstep;  // wave-uniform
         if constexpr (ASM)
-          lds_dma16(tile + (4 * i + w) * 512, base, (uint32_t)(rl * D + src_off(r)) * 2u);
+          lds_dma16(tile + (4 * i + w) * 512, base, (uint32_t)(lro + src_off(r)) * 2u);
         else
-          __builtin_amdgcn_global_load_lds((const void*)(base + rl * D + src_off(r)),
+          __builtin_amdgcn_global_load_lds((const void*)(base + lro + src_off(r)),
                                            (LDS_AS void*)(tile + (4 * i + w) * 512), 16, 0, 0);
       }
     } else {
@@ -273,11 +316,10 @@ struct TileLoader {
         const int r = 4 * RW * i + rl;
         if constexpr (ASM) {
           const int last = nrows - 1 - row0;  // last tile row that exists
-          lds_dma16(tile + (4 * i + w) * 512, g + (int64_t)row0 * D,
-                    (uint32_t)(min(r, last) * D + src_off(r)) * 2u);
+          lds_dma16(tile + (4 * i + w) * 512, g0, (uint32_t)(min(r, last) * rs + src_off(r)) * 2u);
         } else {
           const int gr = min(row0 + r, nrows - 1);
-          __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)gr * D + src_off(r)),
+          __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)gr * rs + src_off(r)),
                                            (LDS_AS void*)(tile + (4 * i + w) * 512), 16, 0, 0);
         }
       }

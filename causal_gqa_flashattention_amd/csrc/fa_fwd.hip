@@ -34,7 +34,7 @@ namespace cgqa {
 // LDS reads kept this many fragments ahead of the MFMAs that use them
 constexpr int kLookahead = 6;
 
-template <int D, int BN, bool CAUSAL, bool MASKED>
+template <class E, int D, int BN, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs a) {
   constexpr int BM = 128;
   constexpr int P = Tile<D>::P;
@@ -64,9 +64,10 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
   const int hq = hk * G + hi;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
-  const bf16_t* qp = a.q + ((int64_t)(b * a.Hq + hq) * Lq) * D;
-  const bf16_t* kp = a.k + ((int64_t)(b * a.Hkv + hk) * Lk) * D;
-  const bf16_t* vp = a.v + ((int64_t)(b * a.Hkv + hk) * Lk) * D;
+  const bf16_t* qp = a.q.head(b, hq);
+  const bf16_t* kp = a.k.head(b, hk);
+  const bf16_t* vp = a.v.head(b, hk);
+  const int qs = a.q.sl, ks = a.k.sl, vs = a.v.sl;
 
   const int q0 = qt * BM;
   const int qrow = q0 + 32 * w + lr;
@@ -101,12 +102,12 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
   const int wqb = (q0 + 32 * w) / kMaskBlock;
   const bool w_rows = q0 + 32 * w < Lq;
 
-  const TileLoader<D> ld(w, lane);
+  const TileLoader<D> ldk(w, lane, ks), ldv(w, lane, vs);
   auto issue = [&](int ti) {
     const int j = tile(ti);
     bf16_t* buf = smem + (ti & 1) * BUF;
-    ld.template load<BN>(buf, kp, j * BN, Lk, w);
-    ld.template load<BN>(buf + BN * P, vp, j * BN, Lk, w);
+    ldk.template load<BN>(buf, kp, j * BN, Lk, w);
+    ldv.template load<BN>(buf + BN * P, vp, j * BN, Lk, w);
   };
   if (nt > 0) issue(0);
 
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
   {
     const int qr = min(qrow, Lq - 1);  // rows past Lq compute on a copy; never stored
 #pragma unroll
-    for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qr * D + 16 * kd + 8 * lg));
+    for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qr * qs + 16 * kd + 8 * lg));
   }
 
   TileReader<D> rd(lane);  // offsets point into buffer (ti & 1); flipped every tile
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
     for (int nb = 0; nb < NNB; ++nb) {
       s[nb] = zero16();
 #pragma unroll
-      for (int kd = 0; kd < NKD; ++kd) s[nb] = mfma32(rd.row16(Ks, nb * 32, kd), qf[kd], s[nb]);
+      for (int kd = 0; kd < NKD; ++kd) s[nb] = E::mma(rd.row16(Ks, nb * 32, kd), qf[kd], s[nb]);
     }
     // keep LDS reads kLookahead fragments ahead of the products that use them
     __builtin_amdgcn_sched_group_barrier(0x100, kLookahead, 0);
@@ -194,12 +195,12 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
     l_run += rs;
     bf16x8 pf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) pf[ks] = pack8(s[ks / 2], ks % 2);
+    for (int ks = 0; ks < NKS; ++ks) pf[ks] = E::pack8(s[ks / 2], ks % 2);
     prio_hi();
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) acc[db] = mfma32(rd.trA(Vs, 16 * ks, db), pf[ks], acc[db]);
+      for (int ks = 0; ks < NKS; ++ks) acc[db] = E::mma(rd.trA(Vs, 16 * ks, db), pf[ks], acc[db]);
     prio_lo();
     }
 
@@ -213,15 +214,14 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
   const float l_tot = l_run + xor32(l_run);
   if (qrow < Lq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16_t* op = a.o + ((int64_t)(b * a.Hq + hq) * Lq + qrow) * D;
+    bf16_t* op = a.o.head(b, hq) + (int64_t)qrow * a.o.sl;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[db][4 * q4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * q4 + 4 * lg) = v4;
+        const f32x16& c = acc[db];
+        *reinterpret_cast<uint2*>(op + 32 * db + 8 * q4 + 4 * lg) =
+            E::pack4(c[4 * q4] * inv, c[4 * q4 + 1] * inv, c[4 * q4 + 2] * inv, c[4 * q4 + 3] * inv);
       }
     if (lg == 0)
       a.lse[(int64_t)(b * a.Hq + hq) * Lq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
 // previous batch, so a tile is resident at least one phase before it is read.
 // A vector step also reads the next matrix step's K fragments into registers,
 // so that step's S products start on register operands.
-template <int D, int BN, bool CAUSAL, bool MASKED>
+template <class E, int D, int BN, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   constexpr int BM = 256;
   constexpr int P = Tile<D>::P;
@@ -280,9 +280,10 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   const int hq = hk * G + hi;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
-  const bf16_t* qp = a.q + ((int64_t)(b * a.Hq + hq) * Lq) * D;
-  const bf16_t* kp = a.k + ((int64_t)(b * a.Hkv + hk) * Lk) * D;
-  const bf16_t* vp = a.v + ((int64_t)(b * a.Hkv + hk) * Lk) * D;
+  const bf16_t* qp = a.q.head(b, hq);
+  const bf16_t* kp = a.k.head(b, hk);
+  const bf16_t* vp = a.v.head(b, hk);
+  const int qs = a.q.sl, ks = a.k.sl, vs = a.v.sl;
 
   const int q0 = qt * BM;
   const int r0 = q0 + 32 * w;  // this wavefront's first row
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
     return !MASKED || a.mask[wqb * a.nkb + jj * BN / kMaskBlock] != 0;
   };
 
-  const TileLoader<D> ld(w & 3, lane);
+  const TileLoader<D> ld(w & 3, lane, w < 4 ? ks : vs);  // waves 0-3 load K, 4-7 load V
   if (w < 4) {
     if (nt > 0) ld.template load<BN>(sK, kp, tile(0) * BN, Lk, w);
     if (nt > 1) ld.template load<BN>(sK + TILE, kp, tile(1) * BN, Lk, w);
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   {
     const int qr = min(qrow, Lq - 1);  // rows past Lq compute on a copy; never stored
 #pragma unroll
-    for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qr * D + 16 * kd + 8 * lg));
+    for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qr * qs + 16 * kd + 8 * lg));
   }
 
   // row reads (K) follow list position x of the matrix step, transposed reads
@@ -400,13 +401,13 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
       for (int kd = 0; kd < NKD; ++kd)
 #pragma unroll
-        for (int nb = 0; nb < NNB; ++nb) s[nb] = mfma32(kf[nb * NKD + kd], qf[kd], s[nb]);
+        for (int nb = 0; nb < NNB; ++nb) s[nb] = E::mma(kf[nb * NKD + kd], qf[kd], s[nb]);
     }
     if (need(x - 1)) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db] = mfma32(rd.trA(sV, 16 * ks, db), pf[ks], acc[db]);
+        for (int db = 0; db < NDB; ++db) acc[db] = E::mma(rd.trA(sV, 16 * ks, db), pf[ks], acc[db]);
       // the transposed reads run kLookahead ahead of the products (the K
       // fragments' registers are free by now)
       constexpr int NM = NKS * NDB, NR = 2 * NM, LA = kLookahead < NR ? kLookahead : NR;
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
       }
     l_run += rs;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) pf[ks] = pack8(s[ks / 2], ks % 2);
+    for (int ks = 0; ks < NKS; ++ks) pf[ks] = E::pack8(s[ks / 2], ks % 2);
   };
 
   wait_vmem();
@@ -494,22 +495,21 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   const float l_tot = l_run + xor32(l_run);
   if (qrow < Lq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;  // no key seen (block mask): O = 0
-    bf16_t* op = a.o + ((int64_t)(b * a.Hq + hq) * Lq + qrow) * D;
+    bf16_t* op = a.o.head(b, hq) + (int64_t)qrow * a.o.sl;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[db][4 * q4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * q4 + 4 * lg) = v4;
+        const f32x16& c = acc[db];
+        *reinterpret_cast<uint2*>(op + 32 * db + 8 * q4 + 4 * lg) =
+            E::pack4(c[4 * q4] * inv, c[4 * q4 + 1] * inv, c[4 * q4 + 2] * inv, c[4 * q4 + 3] * inv);
       }
     if (lg == 0)
       a.lse[(int64_t)(b * a.Hq + hq) * Lq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
-template <int D, int BN>
+template <class E, int D, int BN>
 static hipError_t launch_fwd_d(const FwdArgs& a0, bool causal, hipStream_t stream) {
   FwdArgs a = a0;
   const bool masked = a.mask != nullptr;
@@ -523,27 +523,32 @@ static hipError_t launch_fwd_d(const FwdArgs& a0, bool causal, hipStream_t strea
   if constexpr (D == 96 || D == 128) {
     a.nqt = (a.Lq + 255) / 256;
     if (causal)
-      masked ? go(fa_fwd_pp_kernel<D, BN, true, true>, 512) : go(fa_fwd_pp_kernel<D, BN, true, false>, 512);
+      masked ? go(fa_fwd_pp_kernel<E, D, BN, true, true>, 512) : go(fa_fwd_pp_kernel<E, D, BN, true, false>, 512);
     else
-      masked ? go(fa_fwd_pp_kernel<D, BN, false, true>, 512) : go(fa_fwd_pp_kernel<D, BN, false, false>, 512);
+      masked ? go(fa_fwd_pp_kernel<E, D, BN, false, true>, 512) : go(fa_fwd_pp_kernel<E, D, BN, false, false>, 512);
   } else {
     a.nqt = (a.Lq + 127) / 128;
     if (causal)
-      masked ? go(fa_fwd_kernel<D, BN, true, true>, 256) : go(fa_fwd_kernel<D, BN, true, false>, 256);
+      masked ? go(fa_fwd_kernel<E, D, BN, true, true>, 256) : go(fa_fwd_kernel<E, D, BN, true, false>, 256);
     else
-      masked ? go(fa_fwd_kernel<D, BN, false, true>, 256) : go(fa_fwd_kernel<D, BN, false, false>, 256);
+      masked ? go(fa_fwd_kernel<E, D, BN, false, true>, 256) : go(fa_fwd_kernel<E, D, BN, false, false>, 256);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, hipStream_t stream) {
+template <class E>
+static hipError_t launch_fwd_e(const FwdArgs& a, int D, bool causal, hipStream_t stream) {
   switch (D) {
-    case 64: return launch_fwd_d<64, 64>(a, causal, stream);
-    case 96: return launch_fwd_d<96, 64>(a, causal, stream);
-    case 128: return launch_fwd_d<128, 64>(a, causal, stream);
-    case 256: return launch_fwd_d<256, 32>(a, causal, stream);
+    case 64: return launch_fwd_d<E, 64, 64>(a, causal, stream);
+    case 96: return launch_fwd_d<E, 96, 64>(a, causal, stream);
+    case 128: return launch_fwd_d<E, 128, 64>(a, causal, stream);
+    case 256: return launch_fwd_d<E, 256, 32>(a, causal, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, bool f16, hipStream_t stream) {
+  return f16 ? launch_fwd_e<FP16>(a, D, causal, stream) : launch_fwd_e<BF16>(a, D, causal, stream);
 }
 
 }  // namespace cgqa

@@ -9,11 +9,17 @@ namespace cgqa {
 // Block-sparse mask granularity: one entry per 64 query rows x 64 keys.
 constexpr int kMaskBlock = 64;
 
+// A strided [B, H, L, D] tensor of 16-bit elements: element (b, h, i, d) is
+// at p + b * sb + h * sh + i * sl + d (the D elements of a row contiguous).
+struct Tensor {
+  uint16_t* p;
+  int64_t sb, sh;
+  int sl;  // row stride (checked: sl * 128 < 2^31)
+  __host__ __device__ uint16_t* head(int b, int h) const { return p + b * sb + h * sh; }
+};
+
 struct FwdArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* o;
+  Tensor q, k, v, o;
   float* lse;
   int B, Hq, Hkv, Lq, Lk, G;
   int off;          // Lk - Lq: causal diagonal offset
@@ -24,22 +30,16 @@ struct FwdArgs {
 };
 
 struct DeltaArgs {
-  const uint16_t* o;
-  const uint16_t* dO;
-  float* delta;
-  int64_t rows;
+  Tensor o, dO;
+  float* delta;  // [H rows of Lq] per batch entry, contiguous
+  int H, Lq;
+  int64_t rows;  // B * H * Lq
 };
 
 struct BwdArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
+  Tensor q, k, v, dO, dq, dk, dv;
   const float* lse;
   const float* delta;
-  const uint16_t* dO;
-  uint16_t* dq;
-  uint16_t* dk;
-  uint16_t* dv;
   int B, Hq, Hkv, Lq, Lk, G;
   int off;
   int nqt;          // query tiles (dQ kernel)
@@ -50,10 +50,11 @@ struct BwdArgs {
   int nkb;              // ceil(Lk / 64)
 };
 
-// Each launcher enqueues on `stream` and returns hipGetLastError().
-hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, hipStream_t stream);
-hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t stream);
+// Each launcher enqueues on `stream` and returns hipGetLastError().  f16:
+// the elements are IEEE half instead of bfloat16.
+hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, bool f16, hipStream_t stream);
+hipError_t launch_delta(const DeltaArgs& a, int D, bool f16, hipStream_t stream);
 // which: 1 = dQ kernel, 2 = dK/dV kernel, 3 = both (dQ first).
-hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, bool f16, hipStream_t stream);
 
 }  // namespace cgqa

@@ -1,13 +1,15 @@
 """Seeded synthetic inputs shared by the HIP path's tests/bench and the oracle.
 
 This module holds no attention arithmetic.  It only draws i.i.d. normal
-values and rounds them to bfloat16 bit patterns, so that the GPU path and the
-CPU oracle see exactly the same input bits.
+values and rounds them to bfloat16 (or IEEE half) bit patterns, so that the
+GPU path and the CPU oracle see exactly the same input bits.
 
 Recipe (the same for every workload): numpy ``Generator(PCG64(seed))``
 standard normals drawn in float32, multiplied by ``sigma``, rounded to
-bfloat16 with round-to-nearest-even on the bit pattern.  Tensors are
-contiguous ``[B, H, L, D]`` with D innermost.
+bfloat16 with round-to-nearest-even on the bit pattern (or to binary16 by
+numpy's round-to-nearest-even cast).  Tensors are contiguous
+``[B, H, L, D]`` with D innermost; a workload's ``layout`` only says how the
+GPU side places them.
 
 Block masks (inputs of the block-sparse calls) are uint8
 ``[ceil(Lq/64), ceil(Lk/64)]`` arrays, 1 = the 64 x 64 block is kept:
@@ -27,6 +29,9 @@ import numpy as np
 __all__ = [
     "bf16_bits_from_f32",
     "normal_bf16_bits",
+    "normal_f16_bits",
+    "f16_bits_from_f32",
+    "normal_bits",
     "AttnShape",
     "WORKLOADS",
     "make_inputs",
@@ -49,6 +54,30 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     lsb = (u >> np.uint64(16)) & np.uint64(1)
     r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
     return r.astype(np.uint16)
+
+
+def f16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (numpy's cast: round to nearest
+    even); return uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def normal_f16_bits(shape, seed: int, sigma: float = 1.0) -> np.ndarray:
+    """The draws of normal_bf16_bits rounded to binary16 instead."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        x = x * np.float32(sigma)
+    return f16_bits_from_f32(x)
+
+
+def normal_bits(shape, seed: int, sigma: float = 1.0, dtype: str = "bf16") -> np.ndarray:
+    """normal_bf16_bits or normal_f16_bits by element type name."""
+    if dtype == "bf16":
+        return normal_bf16_bits(shape, seed, sigma)
+    if dtype == "f16":
+        return normal_f16_bits(shape, seed, sigma)
+    raise ValueError(f"unknown element type {dtype}")
 
 
 def normal_bf16_bits(shape, seed: int, sigma: float = 1.0) -> np.ndarray:
@@ -79,6 +108,8 @@ class AttnShape:
     # block mask recipe: None (dense), ("window", keys, sink_blocks) or
     # ("random", density, seed)
     mask: tuple | None = None
+    dtype: str = "bf16"    # element type of q, k, v, dO and the outputs: "bf16" or "f16"
+    layout: str = "bhld"   # "bhld" (contiguous [B, H, L, D]) or "bshd" ([B, L, H, D] buffers)
 
     @property
     def softmax_scale(self) -> float:
@@ -105,6 +136,10 @@ WORKLOADS = {
     # the 8192-token training shape under a sliding-window block mask: each
     # query block keeps the key blocks that meet the 1024 keys before its
     # last row
+    # the 8192-token training shape in IEEE half, and in bf16 with every
+    # tensor a [B, L, H, D] buffer (sequence-major) passed as a strided view
+    "train8k_f16": AttnShape("train8k_f16", 1, 32, 8, 8192, 8192, 128, True, seed=2200, dtype="f16"),
+    "train8k_bshd": AttnShape("train8k_bshd", 1, 32, 8, 8192, 8192, 128, True, seed=2300, layout="bshd"),
     "train8k_window": AttnShape("train8k_window", 1, 32, 8, 8192, 8192, 128, True, seed=2100,
                                 mask=("window", 1024, 0)),
 }
@@ -114,14 +149,14 @@ def make_inputs(shape: AttnShape, with_grad: bool | None = None) -> dict:
     """Return uint16 bf16 bit arrays q, k, v (and dO when a backward is wanted)."""
     if with_grad is None:
         with_grad = shape.backward
-    s = shape.seed
+    s, dt = shape.seed, shape.dtype
     out = {
-        "q": normal_bf16_bits((shape.B, shape.Hq, shape.Lq, shape.D), s + 0, shape.sigma * shape.q_sigma_mult),
-        "k": normal_bf16_bits((shape.B, shape.Hkv, shape.Lk, shape.D), s + 1, shape.sigma),
-        "v": normal_bf16_bits((shape.B, shape.Hkv, shape.Lk, shape.D), s + 2, shape.sigma),
+        "q": normal_bits((shape.B, shape.Hq, shape.Lq, shape.D), s + 0, shape.sigma * shape.q_sigma_mult, dt),
+        "k": normal_bits((shape.B, shape.Hkv, shape.Lk, shape.D), s + 1, shape.sigma, dt),
+        "v": normal_bits((shape.B, shape.Hkv, shape.Lk, shape.D), s + 2, shape.sigma, dt),
     }
     if with_grad:
-        out["do"] = normal_bf16_bits((shape.B, shape.Hq, shape.Lq, shape.D), s + 3, shape.sigma)
+        out["do"] = normal_bits((shape.B, shape.Hq, shape.Lq, shape.D), s + 3, shape.sigma, dt)
     return out
 
 

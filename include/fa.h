@@ -16,7 +16,8 @@
  *     then over query blocks), both recomputing P from the saved log-sum-exp,
  *     no atomics (VJP page, Architecture / Two-Kernel Design).
  *
- * Tensor layout (all calls): contiguous [B, H, L, D], D innermost.
+ * Tensor layout (plain calls): contiguous [B, H, L, D], D innermost; the
+ * *_ex calls below take strided views and float16 as well.
  *   q, o, dO, dq : [B, Hq,  Lq, D]   bfloat16 (passed as raw 16-bit words)
  *   k, v, dk, dv : [B, Hkv, Lk, D]   bfloat16
  *   lse, delta   : [B, Hq,  Lq]      float32
@@ -54,6 +55,8 @@
 #ifndef CGQA_FA_H
 #define CGQA_FA_H
 
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -67,7 +70,9 @@ typedef enum {
   FA_ERR_GQA = 5,               /* Hq not a multiple of Hkv                   */
   FA_ERR_CAUSAL_LQ_GT_LK = 6,   /* causal with Lq > Lk                        */
   FA_ERR_SCALE = 7,             /* scale not finite or not positive           */
-  FA_ERR_LAUNCH = 8             /* the HIP runtime refused a kernel launch    */
+  FA_ERR_LAUNCH = 8,            /* the HIP runtime refused a kernel launch    */
+  FA_ERR_STRIDE = 9,            /* bad stride, or an output overlaps itself   */
+  FA_ERR_DTYPE = 10             /* unknown element type                       */
 } fa_status;
 
 /*
@@ -117,7 +122,6 @@ fa_status fa_bwd_dkv(const void* q, const void* k, const void* v,
                      int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                      int causal, void* stream);
 
-/* Human-readable name of a status code (static string, never NULL). */
 /*
  * Block-sparse variants (page "feat(attention): complete Flash Attention VJP
  * implementation", "Sparse Block Masks": an optional uint8 mask with one
@@ -162,6 +166,66 @@ fa_status fa_bwd_dkv_block_sparse(const void* q, const void* k, const void* v,
                                   int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                                   int causal, const unsigned char* block_mask, void* stream);
 
+/*
+ * General calls: element type and strided operands.
+ *
+ * Element type (page "feat(attention): complete Flash Attention VJP
+ * implementation", summary: float16 and bfloat16 are supported): one fa_dtype
+ * for q, k, v, o, dO, dq, dk and dv.  FA_F16 is IEEE binary16; the products
+ * then run on the half-precision matrix instructions with fp32 accumulation,
+ * and P and dS are rounded to half (RNE) as operands.  lse and delta stay
+ * float32.
+ *
+ * Strided operands (same page, summary of params.h: the backward takes
+ * gradient and input strides; review-comment resolutions: strides are
+ * checked at run time): an fa_tensor is a [B, H, L, D] view whose element
+ * (b, h, i, d) sits at element offset b*stride_b + h*stride_h + i*stride_l + d
+ * from data.  The D elements of a row are contiguous.  This covers
+ * [B, L, H, D] ("sequence-major") buffers, K/V that are the first Lk rows of
+ * a longer cache ([B, Hkv, capacity, D] with stride_h = capacity * D: rows at
+ * and past Lk are never read), and padded rows.  Requirements, checked
+ * before any launch:
+ *   data 16-byte aligned (FA_ERR_ALIGN) and non-NULL when non-empty;
+ *   strides of dimensions with extent > 1 are >= 0 and multiples of 8
+ *   elements, stride_l < 2^24 (FA_ERR_STRIDE); a stride of an extent-1
+ *   dimension is ignored;
+ *   inputs may overlap one another or themselves (stride 0 broadcasts);
+ *   an output (o, dq, dk, dv) must not overlap itself: in order of
+ *   increasing stride each dimension's stride is at least the span of the
+ *   dimensions inside it, the D elements first (FA_ERR_STRIDE).
+ *   Outputs must not overlap inputs or other outputs (not checked).
+ * lse and delta are contiguous [B, Hq, Lq] float32 as in the plain calls.
+ * All other arguments, checks and errors are those of the plain calls, of
+ * which these are the general form: fa_fwd(...) is fa_fwd_ex with dense
+ * [B, H, L, D] tensors, FA_BF16 and no mask.
+ */
+typedef enum { FA_BF16 = 0, FA_F16 = 1 } fa_dtype;
+
+typedef struct fa_tensor {
+  void* data;        /* DEVICE pointer owned by the caller (const for inputs) */
+  int64_t stride_b;  /* element strides of batch, head and row            */
+  int64_t stride_h;
+  int64_t stride_l;
+} fa_tensor;
+
+fa_status fa_fwd_ex(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                    fa_dtype dtype, const unsigned char* block_mask, void* stream);
+
+fa_status fa_bwd_delta_ex(fa_tensor o, fa_tensor dO, float* delta, int B, int H, int Lq, int D,
+                          fa_dtype dtype, void* stream);
+
+/* grads: FA_GRAD_DQ (writes dq), FA_GRAD_DKV (writes dk and dv), or both
+ * (fa_bwd); the tensors of a gradient not asked for may be NULL. */
+#define FA_GRAD_DQ 1u
+#define FA_GRAD_DKV 2u
+
+fa_status fa_bwd_ex(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, const float* delta,
+                    fa_tensor dO, fa_tensor dq, fa_tensor dk, fa_tensor dv,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                    fa_dtype dtype, const unsigned char* block_mask, unsigned grads, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_str(fa_status s);
 
 /* Library version string, e.g. "0.1.0 gfx950". */

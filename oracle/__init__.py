@@ -41,6 +41,8 @@ from __future__ import annotations
 from .attention import (  # noqa: F401
     MASK_BLOCK,
     bf16_bits_to_f64,
+    f16_bits_to_f64,
+    bits_to_f64,
     visible_mask,
     head_forward,
     head_forward_online,

@@ -21,6 +21,22 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of IEEE binary16 bit patterns (uint16/int16) to float64
+    (the float16 element type of "feat(attention): complete Flash Attention
+    VJP implementation", summary)."""
+    return np.ascontiguousarray(bits).view(np.float16).astype(np.float64)
+
+
+def bits_to_f64(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """bf16_bits_to_f64 or f16_bits_to_f64 by element type name."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(bits)
+    if dtype == "f16":
+        return f16_bits_to_f64(bits)
+    raise ValueError(f"unknown element type {dtype}")
+
+
 def visible_mask(Lq: int, Lk: int, causal: bool, rows=None, block_mask=None) -> np.ndarray:
     """Boolean [len(rows), Lk]: may query row i attend to key j?
 

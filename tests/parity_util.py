@@ -20,8 +20,9 @@ TOL = {"lse": ("abs", 1e-3), "o": ("rel_max", 1e-2), "dq": ("rel_max", 2e-2),
        "dk": ("rel_max", 2e-2), "dv": ("rel_max", 2e-2), "delta": ("rel_max", 1e-2)}
 
 
-def to_gpu(bits: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+def to_gpu(bits: np.ndarray, dtype: str = "bf16") -> torch.Tensor:
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).cuda()
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
@@ -72,14 +73,15 @@ def check(name: str, got: np.ndarray, ref: np.ndarray, label: str = "", atol: fl
     return st
 
 
-def oracle_full(bits: dict, scale: float, causal: bool, backward=True, block_mask=None) -> dict:
-    q = oracle.bf16_bits_to_f64(bits["q"])
-    k = oracle.bf16_bits_to_f64(bits["k"])
-    v = oracle.bf16_bits_to_f64(bits["v"])
+def oracle_full(bits: dict, scale: float, causal: bool, backward=True, block_mask=None,
+                dtype: str = "bf16") -> dict:
+    q = oracle.bits_to_f64(bits["q"], dtype)
+    k = oracle.bits_to_f64(bits["k"], dtype)
+    v = oracle.bits_to_f64(bits["v"], dtype)
     if not backward:
         o, lse = oracle.forward(q, k, v, scale, causal, block_mask=block_mask)
         return {"o": o, "lse": lse}
-    do = oracle.bf16_bits_to_f64(bits["do"])
+    do = oracle.bits_to_f64(bits["do"], dtype)
     return oracle.backward(q, k, v, do, scale, causal, block_mask=block_mask)
 
 

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(9):
+    for s in range(11):
         assert lib.fa_status_str(s)
     assert b"Lq <= Lk" in lib.fa_status_str(6)
 
@@ -118,3 +118,66 @@ def test_block_sparse_length_limit(lib):
     big = 262144 + 64
     assert lib.fa_fwd_block_sparse(P, P, P, P, P, 1, 1, 1, big, big, 128, 0.1, 1, P, None) == 3
     assert lib.fa_bwd_block_sparse(*([P] * 10), 1, 1, 1, 64, big, 128, 0.1, 1, P, None) == 3
+
+
+# ---------------------------------------------------------------- general calls
+
+def _t(lib, data, sb, sh, sl):
+    import causal_gqa_flashattention_amd as fa
+    return fa.FaTensor(data, sb, sh, sl)
+
+
+def _dense(lib, H, L, D, data=P):
+    return _t(lib, data, H * L * D, L * D, D)
+
+
+def test_ex_symbols_and_status_strings(lib):
+    assert b"stride" in lib.fa_status_str(9)
+    assert b"element type" in lib.fa_status_str(10)
+
+
+@pytest.mark.parametrize("q_strides,o_strides,status", [
+    ((2 * 128 * 64, 128 * 64, 60), (2 * 128 * 64, 128 * 64, 64), 9),    # row stride not a multiple of 8
+    ((2 * 128 * 64, -128 * 64, 64), (2 * 128 * 64, 128 * 64, 64), 9),   # negative head stride
+    ((2 * 128 * 64, 128 * 64, 1 << 24), (2 * 128 * 64, 128 * 64, 64), 9),  # row stride too large
+    ((2 * 128 * 64, 128 * 64, 64), (2 * 128 * 64, 128 * 64, 32), 9),    # output rows overlap
+    ((2 * 128 * 64, 128 * 64, 64), (2 * 128 * 64, 8, 128), 9),          # output heads overlap
+    ((2 * 128 * 64, 128 * 64, 64), (2 * 128 * 64, 64, 64), 9),          # heads and rows collide
+    ((2 * 128 * 64, 128 * 64, 64), (128 * 64, 128 * 64, 64), 9),       # batches overlap heads
+])
+def test_fwd_ex_stride_validation(lib, q_strides, o_strides, status):
+    # B=2, Hq=2, Hkv=1, Lq=Lk=128, D=64
+    q = _t(lib, P, *q_strides)
+    kv = _dense(lib, 1, 128, 64)
+    o = _t(lib, P, *o_strides)
+    assert lib.fa_fwd_ex(q, kv, kv, o, P, 2, 2, 1, 128, 128, 64, 0.1, 1, 0, None, None) == status
+
+
+def test_ex_dtype_and_empty(lib):
+    q = _dense(lib, 2, 128, 64)
+    kv = _dense(lib, 1, 128, 64)
+    assert lib.fa_fwd_ex(q, kv, kv, q, P, 1, 2, 1, 128, 128, 64, 0.1, 1, 2, None, None) == 10
+    assert lib.fa_bwd_delta_ex(q, q, P, 1, 2, 128, 64, 7, None) == 10
+    z = _t(lib, None, 0, 0, 0)
+    assert lib.fa_fwd_ex(z, z, z, z, None, 0, 2, 1, 128, 128, 64, 0.1, 1, 1, None, None) == 0
+    assert lib.fa_bwd_ex(z, z, z, None, None, z, z, z, z, 0, 2, 1, 8, 8, 64, 0.1, 1, 1, None, 3, None) == 0
+    # no gradient asked for: nothing to do
+    assert lib.fa_bwd_ex(z, z, z, None, None, z, z, z, z, 1, 2, 1, 8, 8, 64, 0.1, 1, 0, None, 0, None) == 0
+
+
+def test_bwd_ex_validation(lib):
+    q = _dense(lib, 2, 128, 64)
+    kv = _dense(lib, 1, 128, 64)
+    z = _t(lib, None, 0, 0, 0)
+    bad = _t(lib, P, 2 * 128 * 64, 128 * 64, 32)  # rows overlap
+    # dq only: the dK/dV tensors may be NULL; an overlapping dq is refused
+    assert lib.fa_bwd_ex(q, kv, kv, P, P, q, bad, z, z, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 1, None) == 9
+    # dK/dV only: dq may be NULL, dk must be given
+    assert lib.fa_bwd_ex(q, kv, kv, P, P, q, z, z, kv, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 2, None) == 1
+    # an overlapping dv (stride 0 rows) is refused, a stride-0 input is not looked at as an output
+    zero_rows = _t(lib, P, 128 * 64, 128 * 64, 0)
+    assert lib.fa_bwd_ex(q, kv, kv, P, P, q, z, kv, zero_rows, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 2,
+                         None) == 9
+    # misaligned data pointer in a strided view
+    mis = _t(lib, P + 8, 2 * 128 * 64, 128 * 64, 64)
+    assert lib.fa_bwd_ex(mis, kv, kv, P, P, q, q, kv, kv, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 3, None) == 2

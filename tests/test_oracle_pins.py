@@ -288,6 +288,24 @@ def test_bf16_widening_is_exact():
     np.testing.assert_array_equal(b, normal_bf16_bits((3, 5), seed=7))
 
 
+def test_f16_widening_is_exact():
+    # IEEE binary16 values by their definition: sign, 5-bit exponent (bias
+    # 15), 10-bit fraction; subnormals scale the fraction by 2^-24
+    bits = np.array([0x3C00, 0xC000, 0x7BFF, 0x0001, 0x03FF, 0x0400, 0x3555, 0x8000], dtype=np.uint16)
+    want = np.array([1.0, -2.0, 65504.0, 2.0 ** -24, 1023 * 2.0 ** -24, 2.0 ** -14,
+                     (1 + 0x155 / 1024) * 2.0 ** -2, -0.0])
+    got = oracle.f16_bits_to_f64(bits)
+    np.testing.assert_array_equal(got, want)
+    assert np.signbit(got[-1])
+    # the input rounding agrees with torch's cast (round to nearest even)
+    from fa_synth import f16_bits_from_f32, normal_f16_bits
+    x = np.array([1.0, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, -3.14159, 65519.0], dtype=np.float32)
+    tb = torch.tensor(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(f16_bits_from_f32(x), tb)
+    np.testing.assert_array_equal(normal_f16_bits((3, 5), seed=7), normal_f16_bits((3, 5), seed=7))
+    np.testing.assert_array_equal(oracle.bits_to_f64(bits, "f16"), want)
+
+
 # ---------------------------------------------------------------- block-sparse mask
 # Page "feat(attention): complete Flash Attention VJP implementation", "Sparse
 # Block Masks": one uint8 entry per (query tile, key tile); here 64 x 64.
