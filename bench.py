@@ -91,6 +91,18 @@ def kernel_work(w, pairs):
     return work
 
 
+def short_bytes(w):
+    """Algorithmic HBM bytes per kernel of the short-query path (each tensor
+    read or written once; the fp32 partials in the workspace are the
+    implementation's, not the algorithm's)."""
+    e = 2  # bytes per element
+    kv = w.B * w.Hkv * w.Lk * w.D * e          # one of K, V, dK, dV
+    qrow = w.B * w.Hq * w.Lq * w.D * e         # one of Q, O, dO, dQ
+    stat = w.B * w.Hq * w.Lq * 4               # LSE or delta
+    return {"fwd": 2 * kv + 2 * qrow + stat, "dq": 2 * kv + 3 * qrow + 2 * stat,
+            "dkv": 4 * kv + 2 * qrow + 2 * stat, "delta": 2 * qrow + stat}
+
+
 # ------------------------------------------------------------ traffic record
 
 def source_digest():
@@ -197,6 +209,13 @@ def cpu_baseline(w, bits, budget_s=30.0, mask=None, pairs=None):
         total, _ = masked_model_flops(1, heads_done, w.D, pairs)
         full, _ = masked_model_flops(w.B, w.Hq, w.D, pairs)
     del np
+    if w.Lq <= 8:  # the short-query workloads are measured in algorithmic HBM bytes
+        share = sum(short_bytes(w).values()) / (w.B * w.Hkv) * heads_done / G
+        full_s = dt * (w.B * w.Hkv) * G / heads_done
+        return {"value": share / dt / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+                "sample": f"{heads_done} query heads of key/value head 0 (one GQA group), all {w.Lq} rows, "
+                          f"fp64 forward+backward, {dt:.2f} s",
+                "full_workload_s_extrapolated": round(full_s, 1)}
     return {"value": total / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{heads_done} query heads of key/value head 0 (one GQA group), all {w.Lq} rows, "
                       f"fp64 forward+backward, {dt:.2f} s",
@@ -301,10 +320,29 @@ def mfma_ceiling(dev, cus):
             "kernel": "v_mfma_f32_32x32x16_bf16, 2 wavefronts/SIMD, 4 accumulators each, operands in registers"}
 
 
+def gemm_canary(dev, n=4096, reps=10):
+    """A plain bf16 n^3 library GEMM timed after the step: a clock and
+    contention sanity check for the box (its value is context, not a target)."""
+    import torch
+    a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return {"shape": f"{n}x{n}x{n} bf16", "ms": round(ms, 4), "TFLOP/s": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="train8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -360,6 +398,29 @@ def main(argv=None):
     mask = None if mask_np is None else torch.from_numpy(mask_np).to(dev)
 
     general = w.dtype != "bf16" or w.layout != "bhld"  # fp16 or strided: the fa_*_ex calls
+    short = w.Lq <= fa.SHORT_MAX_LQ                      # decode-style: the short-query calls
+    ws = None
+    if short:
+        ws = torch.empty(fa.fa_short_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D), dtype=torch.uint8,
+                         device=dev)
+
+    def step_short(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd_short(q, k, v, o, lse, scale=sc, causal=causal, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fa_bwd_delta_ex(o, do, delta, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fa.fa_bwd_short(q, k, v, lse, delta, do, dq, None, None, scale=sc, causal=causal, grads="dq",
+                        workspace=ws, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        fa.fa_bwd_short(q, k, v, lse, delta, do, None, dk, dv, scale=sc, causal=causal, grads="dkv",
+                        stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
 
     def step_ex(ev=None):
         if ev is not None:
@@ -380,6 +441,8 @@ def main(argv=None):
             ev[4].record(stream)
 
     def step(ev=None):
+        if short:
+            return step_short(ev)
         if general:
             return step_ex(ev)
         if ev is not None:
@@ -424,6 +487,8 @@ def main(argv=None):
         return 0
 
     resident = torch.cuda.memory_allocated()
+    torch.cuda.synchronize()
+    free_before = torch.cuda.mem_get_info(dev)[0]  # device-wide: sees allocations outside torch too
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -437,6 +502,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     peak = torch.cuda.max_memory_allocated()
+    free_after = torch.cuda.mem_get_info(dev)[0]
 
     names = ["fwd", "delta", "dq", "dkv"]
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
@@ -463,6 +529,14 @@ def main(argv=None):
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic(dom, w.name),
                 "flop_per_launch": work[dom], "avg_launch_ms": round(per[dom], 4)}
+    if short:  # a handful of query rows: every kernel is bound by HBM, not by the matrix cores
+        sb = short_bytes(w)
+        for n in names:
+            kernels[n] = {"ms": per[n], "GB/s": sb[n] / (per[n] * 1e-3) / 1e9}
+        gbs = sb[dom] / (per[dom] * 1e-3) / 1e9
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic(dom, w.name),
+                    "bytes_per_launch": sb[dom], "avg_launch_ms": round(per[dom], 4)}
 
     kind = "causal" if w.causal else "dense"
     mask_desc = ""
@@ -475,10 +549,17 @@ def main(argv=None):
     metric = METRIC if w.name == "train8k" else (
         f"fwd+bwd TFLOP/s{' over visible pairs' if mask_np is not None else ''}, {kind} GQA {w.dtype} "
         f"attention D={w.D} Lq={w.Lq} Lk={w.Lk}{mask_desc}; % of MFMA peak")
+    unit = "TFLOP/s"
+    if short:
+        total_bytes = sum(short_bytes(w).values())
+        value = total_bytes / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+        metric = (f"fwd+bwd algorithmic HBM GB/s (short-query path), {kind} GQA {w.dtype} attention "
+                  f"D={w.D} Lq={w.Lq} Lk={w.Lk}; % of HBM peak")
     out = {
         "metric": metric,
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -492,7 +573,7 @@ def main(argv=None):
                                f"Lq={w.Lq} Lk={w.Lk} D={w.D}{mask_desc}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Lq": w.Lq, "Lk": w.Lk, "D": w.D, "causal": w.causal,
                    "visible_pairs_per_head": int(pairs)},
-        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "frac_of_peak": round(value / (PEAK_HBM_GBS if short else PEAK_BF16_TFLOPS), 4),
         "model_tflop_per_step": round(total_flops / 1e12, 4),
         "kernels": {n: {kk: round(vv, 4) for kk, vv in d.items()} for n, d in kernels.items()},
         "step_events_ms": {"median": round(float(np.median(step_ev)), 4), "min": round(float(step_ev.min()), 4),
@@ -500,8 +581,10 @@ def main(argv=None):
         "roofline": roofline,
         "memory": {"resident_bytes": int(resident), "peak_bytes": int(peak),
                    "extra_over_resident": int(peak - resident),
+                   "device_free_bytes_lost": int(free_before - free_after),
                    "unfused_fp32_score_bytes": unfused_score_bytes(w.B * w.Hq, w.Lq, 4)},
     }
+    out["gemm_canary"] = gemm_canary(dev)
     ceil = mfma_ceiling(dev, cus)
     if ceil is not None:
         ceil["dominant_kernel_frac_of_random"] = round(achieved / ceil["random_operands"], 4)

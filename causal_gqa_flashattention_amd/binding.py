@@ -22,6 +22,7 @@ STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_ALIGN", 3: "FA_ERR_SHAPE",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_GQA", 6: "FA_ERR_CAUSAL_LQ_GT_LK",
     7: "FA_ERR_SCALE", 8: "FA_ERR_LAUNCH", 9: "FA_ERR_STRIDE", 10: "FA_ERR_DTYPE",
+    11: "FA_ERR_WORKSPACE",
 }
 
 _c_int, _c_float, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
@@ -47,6 +48,10 @@ _SIGS = {
     "fa_bwd_delta_ex": [_T, _T, _vp] + [_c_int] * 4 + [_c_int, _vp],
     "fa_bwd_ex": [_T] * 3 + [_vp, _vp] + [_T] * 4 + [_c_int] * 6
                  + [_c_float, _c_int, _c_int, _vp, ctypes.c_uint, _vp],
+    "fa_short_workspace_bytes": [_c_int] * 6,
+    "fa_fwd_short": [_T] * 4 + [_vp] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _vp, ctypes.c_size_t, _vp],
+    "fa_bwd_short": [_T] * 3 + [_vp, _vp] + [_T] * 4 + [_c_int] * 6
+                    + [_c_float, _c_int, _c_int, ctypes.c_uint, _vp, ctypes.c_size_t, _vp],
     "fa_fwd_block_sparse": [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp, _vp],
     "fa_bwd_block_sparse": [_vp] * 10 + [_c_int] * 6 + [_c_float, _c_int, _vp, _vp],
     "fa_bwd_dq_block_sparse": [_vp] * 7 + [_c_int] * 6 + [_c_float, _c_int, _vp, _vp],
@@ -80,7 +85,8 @@ def load_library() -> ctypes.CDLL:
         for name, argtypes in _SIGS.items():
             fn = getattr(lib, name)
             fn.argtypes = argtypes
-            fn.restype = ctypes.c_char_p if name in ("fa_status_str", "fa_version") else ctypes.c_int
+            fn.restype = (ctypes.c_char_p if name in ("fa_status_str", "fa_version")
+                          else ctypes.c_size_t if name == "fa_short_workspace_bytes" else ctypes.c_int)
         _lib = lib
     return _lib
 
@@ -419,6 +425,92 @@ def fa_bwd_ex(q, k, v, lse, delta, do, dq=None, dk=None, dv=None, *, scale: floa
                                   B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)),
                                   _DTYPES[q.dtype], mask, want, _stream_ptr(stream))
     _check(st, "fa_bwd_ex")
+    return (dq if want & FA_GRAD_DQ else None,
+            dk if want & FA_GRAD_DKV else None,
+            dv if want & FA_GRAD_DKV else None)
+
+
+# ---------------------------------------------------------------- short queries
+
+SHORT_MAX_LQ = 8
+
+
+def fa_short_workspace_bytes(B: int, Hq: int, Hkv: int, Lq: int, Lk: int, D: int) -> int:
+    """Bytes of device workspace fa_fwd_short / fa_bwd_short need (0: sizes refused)."""
+    return int(load_library().fa_short_workspace_bytes(B, Hq, Hkv, Lq, Lk, D))
+
+
+def _workspace(ws, nbytes, device):
+    if ws is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return ws
+
+
+def fa_fwd_short(q, k, v, o=None, lse=None, *, scale: float, causal: bool, workspace=None, stream=None):
+    """Forward for Lq <= 8 (bf16 or fp16 strided views).  `workspace`: a GPU
+    byte tensor of at least fa_short_workspace_bytes(...) bytes, allocated
+    here through torch when not given."""
+    qt = _view(q, "q")
+    kt, vt = _view(k, "k", q.dtype), _view(v, "v", q.dtype)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k/v shapes do not match q")
+    o = _out_like(q) if o is None else o
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have the shape of q")
+    ot = _view(o, "o", q.dtype)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    _require(lse, "lse", torch.float32, 3)
+    if tuple(lse.shape) != (B, Hq, Lq):
+        raise ValueError("lse must be [B, Hq, Lq]")
+    nbytes = fa_short_workspace_bytes(B, Hq, Hkv, Lq, Lk, D)
+    ws = _workspace(workspace, nbytes, q.device)
+    st = load_library().fa_fwd_short(qt, kt, vt, ot, _ptr(lse), B, Hq, Hkv, Lq, Lk, D, float(scale),
+                                     int(bool(causal)), _DTYPES[q.dtype], _ptr(ws), ws.numel(),
+                                     _stream_ptr(stream))
+    _check(st, "fa_fwd_short")
+    return o, lse
+
+
+def fa_bwd_short(q, k, v, lse, delta, do, dq=None, dk=None, dv=None, *, scale: float, causal: bool,
+                 grads: str = "all", workspace=None, stream=None):
+    """Backward for Lq <= 8; grads "all", "dq" or "dkv" (see fa_bwd_ex)."""
+    want = {"all": FA_GRAD_DQ | FA_GRAD_DKV, "dq": FA_GRAD_DQ, "dkv": FA_GRAD_DKV}[grads]
+    qt = _view(q, "q")
+    kt, vt, dot = _view(k, "k", q.dtype), _view(v, "v", q.dtype), _view(do, "do", q.dtype)
+    _require(lse, "lse", torch.float32, 3)
+    _require(delta, "delta", torch.float32, 3)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or tuple(do.shape) != tuple(q.shape) or k.shape[0] != B \
+            or k.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if tuple(lse.shape) != (B, Hq, Lq) or tuple(delta.shape) != (B, Hq, Lq):
+        raise ValueError("lse/delta must be [B, Hq, Lq]")
+    dqt = dkt = dvt = _null_view()
+    ws_ptr, ws_len = None, 0
+    if want & FA_GRAD_DQ:
+        dq = _out_like(q) if dq is None else dq
+        if tuple(dq.shape) != tuple(q.shape):
+            raise ValueError("dq has the wrong shape")
+        dqt = _view(dq, "dq", q.dtype)
+        ws = _workspace(workspace, fa_short_workspace_bytes(B, Hq, Hkv, Lq, Lk, D), q.device)
+        ws_ptr, ws_len = _ptr(ws), ws.numel()
+    if want & FA_GRAD_DKV:
+        dk = _out_like(k) if dk is None else dk
+        dv = _out_like(v) if dv is None else dv
+        for t, n in ((dk, "dk"), (dv, "dv")):
+            if tuple(t.shape) != tuple(k.shape):
+                raise ValueError(f"{n} has the wrong shape")
+        dkt, dvt = _view(dk, "dk", q.dtype), _view(dv, "dv", q.dtype)
+    st = load_library().fa_bwd_short(qt, kt, vt, _ptr(lse), _ptr(delta), dot, dqt, dkt, dvt,
+                                     B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)),
+                                     _DTYPES[q.dtype], want, ws_ptr, ws_len, _stream_ptr(stream))
+    _check(st, "fa_bwd_short")
     return (dq if want & FA_GRAD_DQ else None,
             dk if want & FA_GRAD_DKV else None,
             dv if want & FA_GRAD_DKV else None)

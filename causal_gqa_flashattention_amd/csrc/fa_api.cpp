@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "../../include/fa.h"
@@ -143,6 +144,7 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_STRIDE:
       return "a stride is negative, not a multiple of 8 elements or too large, or makes an output overlap itself";
     case FA_ERR_DTYPE: return "unknown element type";
+    case FA_ERR_WORKSPACE: return "workspace too small (see fa_short_workspace_bytes)";
   }
   return "unknown status";
 }
@@ -383,6 +385,146 @@ fa_status fa_bwd_ex(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, con
                     fa_dtype dtype, const unsigned char* block_mask, unsigned grads, void* stream) {
   return bwd_common(q, k, v, lse, delta, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal, dtype,
                     block_mask, grads, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------- short queries
+// Work split of the short-query kernels: packed rows R = G * Lq in blocks of
+// 128, keys in chunks of whole 64-key tiles.  Enough chunks that the grid has
+// about 1024 workgroups (four per CU), but at least 256 keys per chunk so that
+// a workgroup's fixed costs stay small against its loads.
+struct ShortPlan {
+  int R, nrb, nsplit, chunk;
+  size_t part_bytes, ml_bytes;
+};
+
+bool short_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, ShortPlan* p) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || Hq % Hkv) return false;
+  const int G = Hq / Hkv;
+  p->R = G * Lq;
+  p->nrb = (p->R + 127) / 128;
+  const int64_t tiles = ((int64_t)Lk + 63) / 64;
+  const int64_t groups = (int64_t)B * Hkv * p->nrb;
+  int64_t ns = (1024 + groups - 1) / groups;
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, tiles / 4));
+  ns = std::max<int64_t>(ns, 1);
+  const int64_t chunk_tiles = (tiles + ns - 1) / ns;
+  p->nsplit = (int)((tiles + chunk_tiles - 1) / chunk_tiles);
+  p->chunk = (int)(chunk_tiles * 64);
+  const int64_t rows = (int64_t)B * Hkv * p->nsplit * p->R;
+  if (groups * p->nsplit > INT32_MAX) return false;
+  p->part_bytes = (size_t)rows * D * sizeof(float);
+  p->ml_bytes = (size_t)rows * 2 * sizeof(float);
+  return true;
+}
+
+cgqa::SplitArgs split_args(const ShortPlan& pl, void* workspace, int B, int Hq, int Hkv, int Lq, int Lk,
+                           float scale) {
+  cgqa::SplitArgs a{};
+  a.part = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_bytes);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.G = Hq / Hkv; a.off = Lk - Lq;
+  a.R = pl.R; a.nrb = pl.nrb; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return a;
+}
+
+fa_status check_workspace(const ShortPlan& pl, const void* workspace, size_t bytes) {
+  FA_TRY(check_ptr(workspace));
+  if (bytes < pl.part_bytes + pl.ml_bytes) return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+static_assert(FA_SHORT_MAX_LQ == cgqa::kShortMaxLq, "short-query limit");
+
+size_t fa_short_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D) {
+  ShortPlan pl;
+  if (!fwd_head_dim_ok(D) || Lq > FA_SHORT_MAX_LQ || !short_plan(B, Hq, Hkv, Lq, Lk, D, &pl)) return 0;
+  return pl.part_bytes + pl.ml_bytes;
+}
+
+fa_status fa_fwd_short(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
+                       int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                       fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
+  if (!fwd_head_dim_ok(D)) return FA_ERR_HEAD_DIM;
+  FA_TRY(check_sizes(B, Hq, Hkv, Lq, Lk, D, causal != 0));
+  if (Lq > FA_SHORT_MAX_LQ) return FA_ERR_SHAPE;
+  FA_TRY(check_scale(scale));
+  if (B == 0 || Hq == 0 || Lq == 0) return FA_OK;
+  for (const void* p : {(const void*)q.data, (const void*)k.data, (const void*)v.data, (const void*)o.data,
+                        (const void*)lse})
+    FA_TRY(check_ptr(p));
+  FA_TRY(check_tensor(q, B, Hq, Lq, D, false));
+  FA_TRY(check_tensor(k, B, Hkv, Lk, D, false));
+  FA_TRY(check_tensor(v, B, Hkv, Lk, D, false));
+  FA_TRY(check_tensor(o, B, Hq, Lq, D, true));
+  ShortPlan pl;
+  if (!short_plan(B, Hq, Hkv, Lq, Lk, D, &pl)) return FA_ERR_SHAPE;
+  FA_TRY(check_workspace(pl, workspace, workspace_bytes));
+  cgqa::SplitArgs a = split_args(pl, workspace, B, Hq, Hkv, Lq, Lk, scale);
+  a.q = to_kernel(q);
+  a.k = to_kernel(k);
+  a.v = to_kernel(v);
+  a.o = to_kernel(o);
+  a.lse = lse;
+  const hipError_t e = cgqa::launch_fwd_short(a, D, causal != 0, dtype == FA_F16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_bwd_short(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, const float* delta,
+                       fa_tensor dO, fa_tensor dq, fa_tensor dk, fa_tensor dv,
+                       int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                       fa_dtype dtype, unsigned grads, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
+  if (!bwd_head_dim_ok(D)) return FA_ERR_HEAD_DIM;
+  FA_TRY(check_sizes(B, Hq, Hkv, Lq, Lk, D, causal != 0));
+  if (Lq > FA_SHORT_MAX_LQ) return FA_ERR_SHAPE;
+  FA_TRY(check_scale(scale));
+  grads &= FA_GRAD_DQ | FA_GRAD_DKV;
+  if (B == 0 || Hq == 0) return FA_OK;
+  if (Lq == 0) grads &= FA_GRAD_DKV;
+  if (Lk == 0) grads &= FA_GRAD_DQ;
+  if (grads == 0) return FA_OK;
+  // every check before the first launch
+  ShortPlan pl{};
+  if (grads & FA_GRAD_DQ) {
+    for (const void* p : {(const void*)q.data, (const void*)k.data, (const void*)v.data, (const void*)lse,
+                          (const void*)delta, (const void*)dO.data, (const void*)dq.data})
+      FA_TRY(check_ptr(p));
+    FA_TRY(check_tensor(q, B, Hq, Lq, D, false));
+    FA_TRY(check_tensor(k, B, Hkv, Lk, D, false));
+    FA_TRY(check_tensor(v, B, Hkv, Lk, D, false));
+    FA_TRY(check_tensor(dO, B, Hq, Lq, D, false));
+    FA_TRY(check_tensor(dq, B, Hq, Lq, D, true));
+    if (!short_plan(B, Hq, Hkv, Lq, Lk, D, &pl)) return FA_ERR_SHAPE;
+    FA_TRY(check_workspace(pl, workspace, workspace_bytes));
+  }
+  // dK/dV: the key-block kernel, whose grid over keys already fills the chip
+  // (its own checks run before it launches)
+  if (grads & FA_GRAD_DKV)
+    FA_TRY(bwd_common(q, k, v, lse, delta, dO, fa_tensor{}, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal,
+                      dtype, nullptr, FA_GRAD_DKV, stream));
+  if (!(grads & FA_GRAD_DQ)) return FA_OK;
+  cgqa::SplitArgs a = split_args(pl, workspace, B, Hq, Hkv, Lq, Lk, scale);
+  a.q = to_kernel(q);
+  a.k = to_kernel(k);
+  a.v = to_kernel(v);
+  a.dO = to_kernel(dO);
+  a.dq = to_kernel(dq);
+  a.lse = const_cast<float*>(lse);
+  a.delta = delta;
+  const hipError_t e = cgqa::launch_dq_short(a, D, causal != 0, dtype == FA_F16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -50,11 +50,31 @@ struct BwdArgs {
   int nkb;              // ceil(Lk / 64)
 };
 
+// Short-query path (Lq <= kShortMaxLq): the G * Lq (query head, query row)
+// pairs of one key/value head form the rows of a workgroup ("packed rows",
+// r = head_in_group * Lq + query), so K and V are read once per group, and
+// the keys are split into `nsplit` chunks of `chunk` keys whose partial
+// results go to a caller workspace and are combined by a second kernel.
+constexpr int kShortMaxLq = 8;
+struct SplitArgs {
+  Tensor q, k, v, o, dO, dq;
+  float* lse;           // forward: written; backward: read
+  const float* delta;   // backward
+  float* part;          // [B * Hkv][nsplit][R][D] fp32: partial O (unnormalised) or dQ (unscaled)
+  float* part_ml;       // [B * Hkv][nsplit][R][2] fp32: partial running max (exp2 units) and sum
+  int B, Hq, Hkv, Lq, Lk, G, off;
+  int R, nrb, nsplit, chunk;  // packed rows per group, 128-row blocks, key chunks, keys per chunk
+  float scale, scale_log2;
+};
+
 // Each launcher enqueues on `stream` and returns hipGetLastError().  f16:
 // the elements are IEEE half instead of bfloat16.
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, bool f16, hipStream_t stream);
 hipError_t launch_delta(const DeltaArgs& a, int D, bool f16, hipStream_t stream);
 // which: 1 = dQ kernel, 2 = dK/dV kernel, 3 = both (dQ first).
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, bool f16, hipStream_t stream);
+// short path: split forward + combine; split dQ + reduce
+hipError_t launch_fwd_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream);
+hipError_t launch_dq_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream);
 
 }  // namespace cgqa

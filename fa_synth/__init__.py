@@ -140,6 +140,10 @@ WORKLOADS = {
     # tensor a [B, L, H, D] buffer (sequence-major) passed as a strided view
     "train8k_f16": AttnShape("train8k_f16", 1, 32, 8, 8192, 8192, 128, True, seed=2200, dtype="f16"),
     "train8k_bshd": AttnShape("train8k_bshd", 1, 32, 8, 8192, 8192, 128, True, seed=2300, layout="bshd"),
+    # decode-style: one query row per head against 32768 keys (the head-dim
+    # 256 page measures decode at L = 1, S = 32768, 32/8 heads)
+    "decode32k_d256": AttnShape("decode32k_d256", 1, 32, 8, 1, 32768, 256, True, seed=7100, scale=1.0 / 16),
+    "decode32k_d128": AttnShape("decode32k_d128", 1, 32, 8, 1, 32768, 128, True, seed=7200),
     "train8k_window": AttnShape("train8k_window", 1, 32, 8, 8192, 8192, 128, True, seed=2100,
                                 mask=("window", 1024, 0)),
 }

@@ -55,6 +55,7 @@
 #ifndef CGQA_FA_H
 #define CGQA_FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -72,7 +73,8 @@ typedef enum {
   FA_ERR_SCALE = 7,             /* scale not finite or not positive           */
   FA_ERR_LAUNCH = 8,            /* the HIP runtime refused a kernel launch    */
   FA_ERR_STRIDE = 9,            /* bad stride, or an output overlaps itself   */
-  FA_ERR_DTYPE = 10             /* unknown element type                       */
+  FA_ERR_DTYPE = 10,            /* unknown element type                       */
+  FA_ERR_WORKSPACE = 11         /* workspace smaller than required            */
 } fa_status;
 
 /*
@@ -224,6 +226,40 @@ fa_status fa_bwd_ex(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, con
                     fa_tensor dO, fa_tensor dq, fa_tensor dk, fa_tensor dv,
                     int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
                     fa_dtype dtype, const unsigned char* block_mask, unsigned grads, void* stream);
+
+/*
+ * Short queries (Lq <= FA_SHORT_MAX_LQ; decode-style shapes).  Page
+ * "feat(attention): complete Flash Attention VJP implementation" sends query
+ * lengths of at most 8 to separate vector kernels with fp32 accumulators
+ * (overview and file summary).  Same results as fa_fwd_ex / fa_bwd_ex, without
+ * block masks, for shapes with few query rows and many keys:
+ *   - the G = Hq/Hkv query heads' rows of a key/value head are computed
+ *     together, so K and V are read once per group;
+ *   - the keys are split into chunks processed in parallel, whose fp32
+ *     partial results go to a caller-provided DEVICE workspace of at least
+ *     fa_short_workspace_bytes(B, Hq, Hkv, Lq, Lk, D) bytes (16-byte
+ *     aligned; contents on entry do not matter and are overwritten; it must
+ *     not be shared by calls that may run at the same time).
+ * fa_short_workspace_bytes returns 0 for sizes the short calls refuse.
+ * fa_bwd_short writes dk/dv with the key-block kernel of fa_bwd_ex (no
+ * workspace needed for them) and dq from key chunks reduced in a second
+ * pass.  Errors: those of the *_ex calls, FA_ERR_SHAPE for Lq >
+ * FA_SHORT_MAX_LQ, FA_ERR_NULL / FA_ERR_ALIGN / FA_ERR_WORKSPACE for the
+ * workspace when one is needed.  lse and delta as in the plain calls.
+ */
+#define FA_SHORT_MAX_LQ 8
+
+size_t fa_short_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D);
+
+fa_status fa_fwd_short(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
+                       int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                       fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+fa_status fa_bwd_short(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, const float* delta,
+                       fa_tensor dO, fa_tensor dq, fa_tensor dk, fa_tensor dv,
+                       int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                       fa_dtype dtype, unsigned grads, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_str(fa_status s);

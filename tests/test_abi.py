@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(11):
+    for s in range(12):
         assert lib.fa_status_str(s)
     assert b"Lq <= Lk" in lib.fa_status_str(6)
 
@@ -181,3 +181,40 @@ def test_bwd_ex_validation(lib):
     # misaligned data pointer in a strided view
     mis = _t(lib, P + 8, 2 * 128 * 64, 128 * 64, 64)
     assert lib.fa_bwd_ex(mis, kv, kv, P, P, q, q, kv, kv, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 3, None) == 2
+
+
+# ---------------------------------------------------------------- short queries
+
+def test_short_workspace_bytes(lib):
+    f = lib.fa_short_workspace_bytes
+    f.restype = ctypes.c_size_t
+    assert f(1, 32, 8, 9, 1000, 128) == 0          # Lq above the short limit
+    assert f(1, 32, 8, 1, 1000, 80) == 0           # head dim
+    assert f(1, 6, 4, 1, 1000, 128) == 0           # Hq % Hkv
+    assert f(0, 32, 8, 1, 1000, 128) == 0          # empty
+    a = f(1, 32, 8, 1, 32768, 128)
+    assert a > 0 and a % 16 == 0
+    assert f(1, 32, 8, 8, 32768, 128) >= a          # more rows, more partials
+    assert f(1, 32, 8, 1, 32768, 256) >= a
+
+
+def test_short_validation(lib):
+    q = _dense(lib, 4, 1, 64)
+    kv = _dense(lib, 1, 256, 64)
+    ws_bytes = lib.fa_short_workspace_bytes(1, 4, 1, 1, 256, 64)
+    assert lib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 9, 256, 64, 0.1, 1, 0, P, 1 << 30, None) == 3
+    assert lib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, None, 1 << 30, None) == 1
+    assert lib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, P + 4, 1 << 30, None) == 2
+    assert lib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, P, ws_bytes - 16, None) == 11
+    assert lib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 3, P, 1 << 30, None) == 10
+    z = _t(lib, None, 0, 0, 0)
+    assert lib.fa_fwd_short(z, z, z, z, None, 0, 4, 1, 1, 256, 64, 0.1, 1, 0, None, 0, None) == 0
+    # dq needs the workspace; dK/dV alone does not (the misaligned dk is what fails)
+    mis = _t(lib, P + 8, 256 * 64, 256 * 64, 64)
+    assert lib.fa_bwd_short(q, kv, kv, P, P, q, q, z, z, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 1, None, 0, None) == 1
+    assert lib.fa_bwd_short(q, kv, kv, P, P, q, q, z, z, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 1, P, 64, None) == 11
+    assert lib.fa_bwd_short(q, kv, kv, P, P, q, z, mis, kv, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 2, None, 0,
+                            None) == 2
+    # a failing dq check launches nothing, not even the dK/dV half
+    assert lib.fa_bwd_short(q, kv, kv, P, P, q, q, kv, kv, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 3, None, 0,
+                            None) == 1
