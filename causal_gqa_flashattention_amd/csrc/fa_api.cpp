@@ -410,7 +410,7 @@ bool short_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, ShortPlan* p) {
   const int64_t groups = (int64_t)B * Hkv * p->nrb;
   int64_t ns = (1024 + groups - 1) / groups;
   ns = std::min<int64_t>(ns, std::max<int64_t>(1, tiles / 4));
-  ns = std::max<int64_t>(ns, 1);
+  ns = std::max<int64_t>(std::min<int64_t>(ns, 1024), 1);  // the merge kernels hold <= 1024 weights
   const int64_t chunk_tiles = (tiles + ns - 1) / ns;
   p->nsplit = (int)((tiles + chunk_tiles - 1) / chunk_tiles);
   p->chunk = (int)(chunk_tiles * 64);
@@ -510,10 +510,31 @@ fa_status fa_bwd_short(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, 
     FA_TRY(check_workspace(pl, workspace, workspace_bytes));
   }
   // dK/dV: the key-block kernel, whose grid over keys already fills the chip
-  // (its own checks run before it launches)
-  if (grads & FA_GRAD_DKV)
-    FA_TRY(bwd_common(q, k, v, lse, delta, dO, fa_tensor{}, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal,
-                      dtype, nullptr, FA_GRAD_DKV, stream));
+  // (its own checks run before it launches).  When every packed row sees
+  // every key (one query row, or no causal mask) and the group's rows sit
+  // at one stride, the G query heads of a group are handed to it as one
+  // head of G * Lq rows: one pass over the group's rows instead of G
+  // passes of mostly padded query tiles.  lse and delta, [B, Hq, Lq]
+  // contiguous, are already laid out as [B, Hkv, G * Lq].
+  if (grads & FA_GRAD_DKV) {
+    const int G = Hq / Hkv;
+    auto packed_stride = [&](const fa_tensor& t) -> int64_t {
+      if (Lq == 1) return t.stride_h;
+      return t.stride_h == (int64_t)Lq * t.stride_l ? t.stride_l : -1;
+    };
+    const int64_t rq = Lq > 0 ? packed_stride(q) : -1, ro = Lq > 0 ? packed_stride(dO) : -1;
+    const bool pack = G > 1 && (Lq == 1 || !causal) && rq >= 0 && ro >= 0 && rq < (int64_t{1} << 24) &&
+                      ro < (int64_t{1} << 24);
+    if (pack) {
+      const fa_tensor q2{q.data, q.stride_b, q.stride_h * G, rq};
+      const fa_tensor o2{dO.data, dO.stride_b, dO.stride_h * G, ro};
+      FA_TRY(bwd_common(q2, k, v, lse, delta, o2, fa_tensor{}, dk, dv, B, Hkv, Hkv, G * Lq, Lk, D, scale,
+                        0, dtype, nullptr, FA_GRAD_DKV, stream));
+    } else {
+      FA_TRY(bwd_common(q, k, v, lse, delta, dO, fa_tensor{}, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal,
+                        dtype, nullptr, FA_GRAD_DKV, stream));
+    }
+  }
   if (!(grads & FA_GRAD_DQ)) return FA_OK;
   cgqa::SplitArgs a = split_args(pl, workspace, B, Hq, Hkv, Lq, Lk, scale);
   a.q = to_kernel(q);

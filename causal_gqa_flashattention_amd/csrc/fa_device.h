@@ -398,11 +398,12 @@ __device__ __forceinline__ int build_list(int* list, int n, int lane, Order orde
 // s_waitcnt vmcnt(0), leaving expcnt/lgkmcnt unconstrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// s_waitcnt vmcnt(N): all but the N most recent vector-memory loads done.
+// s_waitcnt vmcnt(N): all but the N most recent vector-memory loads done
+// (vmcnt's low four bits in 3:0, its high two in 15:14).
 template <int N>
 __device__ __forceinline__ void wait_vmem_n() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Map a launch-order block id to a logical work id so that the blocks the

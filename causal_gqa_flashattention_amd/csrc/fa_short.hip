@@ -54,15 +54,47 @@ struct SplitWork {
 
 }  // namespace
 
+// Both split kernels stream their chunk through NBUF tile buffers, loading
+// NBUF - 1 tiles ahead: with one tile in flight a workgroup would wait out
+// the memory latency on every tile, and these kernels are bound by HBM.
+// Each wavefront issues ROUNDS loads per operand and tile, so after tile t
+// it waits until at most (NBUF - 2) tiles' loads are outstanding.
+template <int D, int BN, int NBUF>
+struct SplitPipe {
+  static constexpr int P = Tile<D>::P;
+  static constexpr int BUF = 2 * BN * P;  // [K tile | V tile]
+  static constexpr int ROUNDS = BN * Tile<D>::PC / 256;
+  static constexpr int AHEAD = NBUF - 1;
+  static_assert((BUF & (BUF - 1)) == 0, "buffer size must be a power of two");
+  static_assert(NBUF == 2 || NBUF == 4, "the readers step through 2 or 4 buffers by XOR");
+  // XOR moving the readers from buffer t % NBUF to (t + 1) % NBUF
+  __device__ static constexpr int step(int t) { return (NBUF == 4 && (t & 1)) ? 3 * BUF : BUF; }
+  // the wait after tile t: tiles t + 2 .. t + AHEAD may still be in flight
+  template <int OPS>
+  __device__ static void wait(int t, int nt) {
+    if constexpr (NBUF == 4) {
+      const int pend = min(AHEAD - 1, nt - 2 - t);  // tiles issued beyond t + 1
+      if (pend >= 2)
+        wait_vmem_n<2 * OPS * ROUNDS>();
+      else if (pend == 1)
+        wait_vmem_n<OPS * ROUNDS>();
+      else
+        wait_vmem();
+    } else {
+      wait_vmem();
+    }
+  }
+};
+
 // ---------------------------------------------------------------- forward
-template <class E, int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_split_kernel(SplitArgs a) {
+template <class E, int D, int BN, bool CAUSAL, int NBUF>
+__global__ __launch_bounds__(256, (D <= 128 && NBUF == 2 ? 2 : 1)) void fa_fwd_split_kernel(SplitArgs a) {
+  using Pipe = SplitPipe<D, BN, NBUF>;
   constexpr int P = Tile<D>::P;
   constexpr int NKD = D / 16, NDB = D / 32, NNB = BN / 32, NKS = BN / 16;
   constexpr float kSlack = 8.f;
-  constexpr int BUF = 2 * BN * P;  // [K tile | V tile], double buffered
-  static_assert((BUF & (BUF - 1)) == 0, "buffer size must be a power of two");
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF];
+  constexpr int BUF = Pipe::BUF;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NBUF * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -78,11 +110,13 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_split_kernel(S
 
   const TileLoader<D> ldk(w, lane, a.k.sl), ldv(w, lane, a.v.sl);
   auto issue = [&](int t) {
-    bf16_t* buf = smem + (t & 1) * BUF;
+    bf16_t* buf = smem + (t % NBUF) * BUF;
     ldk.template load<BN>(buf, kp, wk.kb + t * BN, Lk, w);
     ldv.template load<BN>(buf + BN * P, vp, wk.kb + t * BN, Lk, w);
   };
-  if (nt > 0) issue(0);
+#pragma unroll
+  for (int t = 0; t < Pipe::AHEAD; ++t)
+    if (t < nt) issue(t);
 
   bf16x8 qf[NKD];
   {
@@ -102,10 +136,10 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_split_kernel(S
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = zero16();
 
-  wait_vmem();
+  Pipe::template wait<2>(-1, nt);  // tile 0 landed
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
-    if (t + 1 < nt) issue(t + 1);
+    if (t + Pipe::AHEAD < nt) issue(t + Pipe::AHEAD);
     const bf16_t* Ks = smem;
     const bf16_t* Vs = smem + BN * P;
     if (w_rows) {
@@ -163,15 +197,15 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_split_kernel(S
       for (int ks = 0; ks < NKS; ++ks) acc[db] = E::mma(rd.trA(Vs, 16 * ks, db), pf[ks], acc[db]);
     }
 
-    rd.flip(BUF);
-    wait_vmem();
+    rd.flip(Pipe::step(t));
+    Pipe::template wait<2>(t, nt);
     __syncthreads();
   }
 
   // ---- partials of this chunk: (m, l) and the unnormalised accumulator
   const float l_tot = l_run + xor32(l_run);
   if (wk.row_ok) {
-    const int64_t idx = ((int64_t)wk.bh * a.nsplit + wk.s) * a.R + wk.r;
+    const int64_t idx = ((int64_t)wk.bh * a.R + wk.r) * a.nsplit + wk.s;  // a row's chunks adjacent
     float* pa = a.part + idx * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -185,63 +219,124 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_split_kernel(S
   }
 }
 
-// One wavefront per packed row: merge the chunks' (m, l, acc) into O and LSE.
+// Merge of one packed row's chunk partials, one workgroup per row.  A row's
+// nsplit partials are adjacent in the workspace, so the workgroup streams
+// one contiguous block: thread t takes float4 column t % (D/4) of chunks
+// t / (D/4), + G, + 2G, ... (G = 256 / (D/4) groups), and the groups' sums
+// are added through LDS.  `wts` holds the chunks' weights 2^(m_c - M).
+template <int D, bool WEIGHTED>
+__device__ __forceinline__ void merge_row(const float* part, const float* wts, int ns, float* out,
+                                          float4* red) {
+  constexpr int NF4 = D / 4;
+  constexpr int G = 256 / NF4;
+  const int t = threadIdx.x;
+  const int d4 = t % NF4, g = t / NF4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (g < G) {
+    const float4* p4 = reinterpret_cast<const float4*>(part);
+    int c = g;
+    for (; c + 3 * G < ns; c += 4 * G) {  // four independent loads in flight per thread
+      float4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = p4[(int64_t)(c + u * G) * NF4 + d4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = WEIGHTED ? wts[c + u * G] : 1.f;
+        acc.x = fmaf(x[u].x, wgt, acc.x);
+        acc.y = fmaf(x[u].y, wgt, acc.y);
+        acc.z = fmaf(x[u].z, wgt, acc.z);
+        acc.w = fmaf(x[u].w, wgt, acc.w);
+      }
+    }
+    for (; c < ns; c += G) {
+      const float4 x = p4[(int64_t)c * NF4 + d4];
+      const float wgt = WEIGHTED ? wts[c] : 1.f;
+      acc.x = fmaf(x.x, wgt, acc.x);
+      acc.y = fmaf(x.y, wgt, acc.y);
+      acc.z = fmaf(x.z, wgt, acc.z);
+      acc.w = fmaf(x.w, wgt, acc.w);
+    }
+    red[g * NF4 + d4] = acc;
+  }
+  __syncthreads();
+  if (t < NF4) {
+    float4 sum = red[t];
+    for (int k = 1; k < G; ++k) {
+      const float4 x = red[k * NF4 + t];
+      sum.x += x.x;
+      sum.y += x.y;
+      sum.z += x.z;
+      sum.w += x.w;
+    }
+    reinterpret_cast<float4*>(out)[t] = sum;
+  }
+  __syncthreads();
+}
+
+// Block-wide max or sum of one float per thread (256 threads).
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float x, float* scratch) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float y = __shfl_xor(x, m, 64);
+    x = MAX ? fmaxf(x, y) : x + y;
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[w] = x;
+  __syncthreads();
+  x = scratch[0];
+#pragma unroll
+  for (int k = 1; k < 4; ++k) x = MAX ? fmaxf(x, scratch[k]) : x + scratch[k];
+  return x;
+}
+
+constexpr int kMaxSplit = 1024;  // chunks per row (the host plans at most this many)
+
+// Forward merge: O = sum_c 2^(m_c - M) acc_c / L, L = sum_c 2^(m_c - M) l_c.
 template <class E, int D>
 __global__ __launch_bounds__(256) void fa_fwd_combine_kernel(SplitArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * Hkv + hk) * R + r
-  if (row >= (int64_t)a.B * a.Hkv * a.R) return;                     // whole wavefronts leave
+  __shared__ float wts[kMaxSplit];
+  __shared__ float4 red[256];
+  __shared__ float scratch[4];
+  __shared__ __attribute__((aligned(16))) float orow[D];
+  const int64_t row = blockIdx.x;  // (b * Hkv + hk) * R + r
   const int bh = (int)(row / a.R), r = (int)(row - (int64_t)bh * a.R);
   const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
   const int hi = r / a.Lq, qi = r - hi * a.Lq, hq = hk * a.G + hi;
   const int ns = a.nsplit;
-  const int64_t base = (int64_t)bh * ns * a.R + r;  // chunk c: base + c * R
+  const int64_t base = row * ns;
 
-  float M = -INFINITY;
-  for (int c = lane; c < ns; c += 64) M = fmaxf(M, a.part_ml[2 * (base + (int64_t)c * a.R)]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-  float L = 0.f;
-  for (int c = lane; c < ns; c += 64) {
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * (base + (int64_t)c * a.R));
-    if (ml.y > 0.f) L += ml.y * fast_exp2(ml.x - M);
+  float m = -INFINITY;
+  for (int c = threadIdx.x; c < ns; c += 256) m = fmaxf(m, a.part_ml[2 * (base + c)]);
+  const float M = block_reduce<true>(m, scratch);
+  float l = 0.f;
+  for (int c = threadIdx.x; c < ns; c += 256) {
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * (base + c));
+    const float wgt = ml.y > 0.f ? fast_exp2(ml.x - M) : 0.f;  // a chunk this row saw nothing of: 0
+    wts[c] = wgt;
+    l = fmaf(ml.y, wgt, l);
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m, 64);
+  const float L = block_reduce<false>(l, scratch);  // (its barriers also publish wts)
+  merge_row<D, true>(a.part + base * D, wts, ns, orow, red);
 
   const float inv = L > 0.f ? 1.f / L : 0.f;  // no visible key at all: O = 0, LSE = -inf
   bf16_t* op = a.o.head(b, hq) + (int64_t)qi * a.o.sl;
-  constexpr int PER = (D + 63) / 64;
-  float o[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  for (int c = 0; c < ns; ++c) {
-    const int64_t idx = base + (int64_t)c * a.R;
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * idx);
-    if (!(ml.y > 0.f)) continue;  // a chunk this row saw nothing of
-    const float wgt = fast_exp2(ml.x - M);
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-      if (lane + 64 * e < D) o[e] = fmaf(a.part[idx * D + lane + 64 * e], wgt, o[e]);
-  }
-#pragma unroll
-  for (int e = 0; e < PER; ++e)
-    if (lane + 64 * e < D) {
-      const uint2 u = E::pack4(o[e] * inv, 0.f, 0.f, 0.f);
-      op[lane + 64 * e] = (bf16_t)(u.x & 0xFFFFu);
-    }
-  if (lane == 0)
+  for (int d = 4 * threadIdx.x; d < D; d += 1024)
+    *reinterpret_cast<uint2*>(op + d) =
+        E::pack4(orow[d] * inv, orow[d + 1] * inv, orow[d + 2] * inv, orow[d + 3] * inv);
+  if (threadIdx.x == 0)
     a.lse[((int64_t)b * a.Hq + hq) * a.Lq + qi] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- dQ
-template <class E, int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_split_kernel(SplitArgs a) {
+template <class E, int D, int BN, bool CAUSAL, int NBUF>
+__global__ __launch_bounds__(256, (D <= 128 && NBUF == 2 ? 2 : 1)) void fa_dq_split_kernel(SplitArgs a) {
+  using Pipe = SplitPipe<D, BN, NBUF>;
   constexpr int P = Tile<D>::P;
   constexpr int NKD = D / 16, NDB = D / 32, NNB = BN / 32, NKS = BN / 16;
-  constexpr int BUF = 2 * BN * P;
-  static_assert((BUF & (BUF - 1)) == 0, "buffer size must be a power of two");
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF];
+  constexpr int BUF = Pipe::BUF;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NBUF * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -256,11 +351,13 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_split_kernel(Sp
 
   const TileLoader<D> ldk(w, lane, a.k.sl), ldv(w, lane, a.v.sl);
   auto issue = [&](int t) {
-    bf16_t* buf = smem + (t & 1) * BUF;
+    bf16_t* buf = smem + (t % NBUF) * BUF;
     ldk.template load<BN>(buf, kp, wk.kb + t * BN, Lk, w);
     ldv.template load<BN>(buf + BN * P, vp, wk.kb + t * BN, Lk, w);
   };
-  if (nt > 0) issue(0);
+#pragma unroll
+  for (int t = 0; t < Pipe::AHEAD; ++t)
+    if (t < nt) issue(t);
 
   bf16x8 qf[NKD], dof[NKD];
   {
@@ -286,10 +383,10 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_split_kernel(Sp
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq[db] = zero16();
 
-  wait_vmem();
+  Pipe::template wait<2>(-1, nt);
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
-    if (t + 1 < nt) issue(t + 1);
+    if (t + Pipe::AHEAD < nt) issue(t + Pipe::AHEAD);
     const bf16_t* Ks = smem;
     const bf16_t* Vs = smem + BN * P;
     if (w_rows) {
@@ -332,13 +429,13 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_split_kernel(Sp
     read_ahead<NKS * NDB, 2>();
     }
 
-    rd.flip(BUF);
-    wait_vmem();
+    rd.flip(Pipe::step(t));
+    Pipe::template wait<2>(t, nt);
     __syncthreads();
   }
 
   if (wk.row_ok) {
-    const int64_t idx = ((int64_t)wk.bh * a.nsplit + wk.s) * a.R + wk.r;
+    const int64_t idx = ((int64_t)wk.bh * a.R + wk.r) * a.nsplit + wk.s;  // a row's chunks adjacent
     float* pd = a.part + idx * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -351,45 +448,38 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_split_kernel(Sp
   }
 }
 
-// One wavefront per packed row: dQ = scale * sum over chunks.
+// dQ = scale * sum over chunks, one workgroup per packed row.
 template <class E, int D>
 __global__ __launch_bounds__(256) void fa_dq_reduce_kernel(SplitArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (int64_t)a.B * a.Hkv * a.R) return;
+  __shared__ float4 red[256];
+  __shared__ __attribute__((aligned(16))) float orow[D];
+  const int64_t row = blockIdx.x;
   const int bh = (int)(row / a.R), r = (int)(row - (int64_t)bh * a.R);
   const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
   const int hi = r / a.Lq, qi = r - hi * a.Lq, hq = hk * a.G + hi;
-  const int64_t base = (int64_t)bh * a.nsplit * a.R + r;
-  constexpr int PER = (D + 63) / 64;
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int c = 0; c < a.nsplit; ++c) {
-    const float* pd = a.part + (base + (int64_t)c * a.R) * D;
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-      if (lane + 64 * e < D) acc[e] += pd[lane + 64 * e];
-  }
+  merge_row<D, false>(a.part + row * a.nsplit * D, nullptr, a.nsplit, orow, red);
   bf16_t* out = a.dq.head(b, hq) + (int64_t)qi * a.dq.sl;
-#pragma unroll
-  for (int e = 0; e < PER; ++e)
-    if (lane + 64 * e < D) {
-      const uint2 u = E::pack4(acc[e] * a.scale, 0.f, 0.f, 0.f);
-      out[lane + 64 * e] = (bf16_t)(u.x & 0xFFFFu);
-    }
+  const float sc = a.scale;
+  for (int d = 4 * threadIdx.x; d < D; d += 1024)
+    *reinterpret_cast<uint2*>(out + d) =
+        E::pack4(orow[d] * sc, orow[d + 1] * sc, orow[d + 2] * sc, orow[d + 3] * sc);
 }
 
 // ---------------------------------------------------------------- launchers
+#ifndef CGQA_SPLIT_NBUF
+#define CGQA_SPLIT_NBUF 2
+#endif
+constexpr int kSplitBufs = CGQA_SPLIT_NBUF;
+
 template <class E, int D, int BN>
 static hipError_t launch_fwd_short_d(const SplitArgs& a, bool causal, hipStream_t stream) {
   const int nwg = a.B * a.Hkv * a.nsplit * a.nrb;
   if (causal)
-    hipLaunchKernelGGL((fa_fwd_split_kernel<E, D, BN, true>), dim3(nwg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_split_kernel<E, D, BN, true, kSplitBufs>), dim3(nwg), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((fa_fwd_split_kernel<E, D, BN, false>), dim3(nwg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_split_kernel<E, D, BN, false, kSplitBufs>), dim3(nwg), dim3(256), 0, stream, a);
   const int64_t rows = (int64_t)a.B * a.Hkv * a.R;
-  hipLaunchKernelGGL((fa_fwd_combine_kernel<E, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fa_fwd_combine_kernel<E, D>), dim3((unsigned)rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -397,11 +487,11 @@ template <class E, int D, int BN>
 static hipError_t launch_dq_short_d(const SplitArgs& a, bool causal, hipStream_t stream) {
   const int nwg = a.B * a.Hkv * a.nsplit * a.nrb;
   if (causal)
-    hipLaunchKernelGGL((fa_dq_split_kernel<E, D, BN, true>), dim3(nwg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fa_dq_split_kernel<E, D, BN, true, kSplitBufs>), dim3(nwg), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((fa_dq_split_kernel<E, D, BN, false>), dim3(nwg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fa_dq_split_kernel<E, D, BN, false, kSplitBufs>), dim3(nwg), dim3(256), 0, stream, a);
   const int64_t rows = (int64_t)a.B * a.Hkv * a.R;
-  hipLaunchKernelGGL((fa_dq_reduce_kernel<E, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fa_dq_reduce_kernel<E, D>), dim3((unsigned)rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

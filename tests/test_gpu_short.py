@@ -129,3 +129,21 @@ def test_decode_32k_every_output(Hq, Hkv, D):
     """One query row per head against 32768 keys (the decode shape of the
     head-dim-256 page's measurements), every output against the oracle."""
     short_case(1, Hq, Hkv, 1, 32768, D, True, seed=10500 + D)
+
+
+@pytest.mark.parametrize("Lq,causal", [(1, True), (4, False), (4, True)])
+def test_short_sequence_major_queries(Lq, causal):
+    """q, dO (and the outputs) in [B, L, H, D] buffers: with one query row the
+    dK/dV pass takes a group's heads as rows at the head stride; with more
+    rows that stride pattern is not a single stride and the per-head pass
+    runs.  Both against the oracle."""
+    B, Hq, Hkv, Lk, D = 2, 8, 2, 1200, 128
+    bits = make_bits(B, Hq, Hkv, Lq, Lk, D, 10600 + Lq)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    g = {n: to_gpu(b) for n, b in bits.items()}
+    for n in ("q", "do"):
+        g[n] = g[n].transpose(1, 2).contiguous().transpose(1, 2)
+    out = run_short(g, scale, causal)
+    ref = oracle_full(bits, scale, causal)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        check(n, to_f64(out[n]), ref[n], f"short bshd Lq{Lq} causal={causal}")
