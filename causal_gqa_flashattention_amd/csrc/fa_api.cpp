@@ -518,6 +518,48 @@ fa_status fa_bwd_short(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, 
   // contiguous, are already laid out as [B, Hkv, G * Lq].
   if (grads & FA_GRAD_DKV) {
     const int G = Hq / Hkv;
+    // a group's rows resident in one workgroup, keys streamed past them
+    // (at most 64 packed rows, 32 at D = 256; row offsets within 2^30 elements)
+    auto span = [&](const fa_tensor& t) {
+      return (int64_t)(G - 1) * t.stride_h + (int64_t)(Lq - 1) * t.stride_l + D;
+    };
+    const bool stream_ok = Lq > 0 && G * Lq <= (D <= 128 ? 64 : 32) && q.stride_h >= 0 && dO.stride_h >= 0 &&
+                           q.stride_l >= 0 && dO.stride_l >= 0 && span(q) < (int64_t{1} << 30) &&
+                           span(dO) < (int64_t{1} << 30);
+    if (stream_ok) {
+      for (const void* p : {(const void*)q.data, (const void*)k.data, (const void*)v.data, (const void*)lse,
+                            (const void*)delta, (const void*)dO.data, (const void*)dk.data, (const void*)dv.data})
+        FA_TRY(check_ptr(p));
+      FA_TRY(check_tensor(q, B, Hq, Lq, D, false));
+      FA_TRY(check_tensor(k, B, Hkv, Lk, D, false));
+      FA_TRY(check_tensor(v, B, Hkv, Lk, D, false));
+      FA_TRY(check_tensor(dO, B, Hq, Lq, D, false));
+      FA_TRY(check_tensor(dk, B, Hkv, Lk, D, true));
+      FA_TRY(check_tensor(dv, B, Hkv, Lk, D, true));
+      cgqa::SplitArgs s{};
+      s.q = to_kernel(q);
+      s.k = to_kernel(k);
+      s.v = to_kernel(v);
+      s.dO = to_kernel(dO);
+      s.dk = to_kernel(dk);
+      s.dv = to_kernel(dv);
+      s.lse = const_cast<float*>(lse);
+      s.delta = delta;
+      s.B = B; s.Hq = Hq; s.Hkv = Hkv; s.Lq = Lq; s.Lk = Lk; s.G = G; s.off = Lk - Lq;
+      s.R = G * Lq;
+      // chunks of whole 128-key steps, about 512 workgroups (two per CU)
+      const int64_t steps = ((int64_t)Lk + 127) / 128;
+      const int64_t groups = (int64_t)B * Hkv;
+      const int64_t want = std::max<int64_t>(1, std::min<int64_t>(steps, (512 + groups - 1) / groups));
+      const int64_t per = (steps + want - 1) / want;
+      s.chunk = (int)(per * 128);
+      s.nsplit = (int)((steps + per - 1) / per);
+      if (groups * s.nsplit > INT32_MAX) return FA_ERR_SHAPE;
+      s.scale = scale;
+      s.scale_log2 = scale * 1.4426950408889634f;
+      const hipError_t e = cgqa::launch_dkv_short(s, D, causal != 0, dtype == FA_F16, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return FA_ERR_LAUNCH;
+    }
     auto packed_stride = [&](const fa_tensor& t) -> int64_t {
       if (Lq == 1) return t.stride_h;
       return t.stride_h == (int64_t)Lq * t.stride_l ? t.stride_l : -1;
@@ -525,7 +567,9 @@ fa_status fa_bwd_short(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, 
     const int64_t rq = Lq > 0 ? packed_stride(q) : -1, ro = Lq > 0 ? packed_stride(dO) : -1;
     const bool pack = G > 1 && (Lq == 1 || !causal) && rq >= 0 && ro >= 0 && rq < (int64_t{1} << 24) &&
                       ro < (int64_t{1} << 24);
-    if (pack) {
+    if (stream_ok) {
+      // done above
+    } else if (pack) {
       const fa_tensor q2{q.data, q.stride_b, q.stride_h * G, rq};
       const fa_tensor o2{dO.data, dO.stride_b, dO.stride_h * G, ro};
       FA_TRY(bwd_common(q2, k, v, lse, delta, o2, fa_tensor{}, dk, dv, B, Hkv, Hkv, G * Lq, Lk, D, scale,

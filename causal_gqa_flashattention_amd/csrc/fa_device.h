@@ -326,6 +326,20 @@ struct TileLoader {
     }
   }
 
+  // The same layout from rows at arbitrary offsets: tile row r comes from
+  // g + rowoff(r) (elements, per lane, < 2^30), e.g. rows gathered from
+  // several heads.  Issued like load(): ROWS * PC / 256 loads per wave.
+  template <int ROWS, class RowOff>
+  __device__ __forceinline__ void gather(bf16_t* tile, const bf16_t* g, RowOff rowoff, int w) const {
+    constexpr int ROUNDS = ROWS * PC / 256;
+    static_assert(ROWS * PC % 256 == 0, "tile must split evenly over four waves");
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+      const int r = 4 * RW * i + rl;
+      lds_dma16(tile + (4 * i + w) * 512, g, (uint32_t)(rowoff(r) + src_off(r)) * 2u);
+    }
+  }
+
   // One global_load_lds_dwordx4: lane l's 16 bytes at sbase + voff go to LDS
   // address dst + 16*l (dst and sbase wave-uniform).  Issued as inline
   // assembly so that the compiler does not treat the load as a write to LDS

@@ -57,11 +57,11 @@ struct BwdArgs {
 // results go to a caller workspace and are combined by a second kernel.
 constexpr int kShortMaxLq = 8;
 struct SplitArgs {
-  Tensor q, k, v, o, dO, dq;
+  Tensor q, k, v, o, dO, dq, dk, dv;
   float* lse;           // forward: written; backward: read
   const float* delta;   // backward
-  float* part;          // [B * Hkv][nsplit][R][D] fp32: partial O (unnormalised) or dQ (unscaled)
-  float* part_ml;       // [B * Hkv][nsplit][R][2] fp32: partial running max (exp2 units) and sum
+  float* part;          // [B * Hkv][R][nsplit][D] fp32: partial O (unnormalised) or dQ (unscaled)
+  float* part_ml;       // [B * Hkv][R][nsplit][2] fp32: partial running max (exp2 units) and sum
   int B, Hq, Hkv, Lq, Lk, G, off;
   int R, nrb, nsplit, chunk;  // packed rows per group, 128-row blocks, key chunks, keys per chunk
   float scale, scale_log2;
@@ -76,5 +76,8 @@ hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, bool f16,
 // short path: split forward + combine; split dQ + reduce
 hipError_t launch_fwd_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream);
 hipError_t launch_dq_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream);
+// short path dK/dV for R <= 64: nsplit chunks of `chunk` keys
+// (a multiple of 128) per key/value head, no workspace
+hipError_t launch_dkv_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream);
 
 }  // namespace cgqa

@@ -465,6 +465,173 @@ __global__ __launch_bounds__(256) void fa_dq_reduce_kernel(SplitArgs a) {
         E::pack4(orow[d] * sc, orow[d + 1] * sc, orow[d + 2] * sc, orow[d + 3] * sc);
 }
 
+// ---------------------------------------------------------------- dK / dV
+// Streaming dK/dV for short queries (R <= 64 packed rows).  Each key's
+// gradient depends only on the group's R rows, so instead of a key-block
+// grid that reloads those rows per block, one workgroup keeps the rows
+// resident: Q and dO in LDS (gathered once from their heads), LSE and delta
+// beside them.  Its four wavefronts walk their own 32-key blocks of the
+// workgroup's chunk (block j of wavefront w: keys kb + 32 (w + 4 j)),
+// loading the next block's K and V operand fragments straight into
+// registers while the current block is computed, and store each block's
+// dV and then dK when done: no barrier inside the loop, and one set of
+// accumulators serves both.  Per block and 32-row block rb of the packed
+// rows (lane = key, as in the long kernel):
+//   S = Q K^T, dP = dO V^T                 (A = rows from LDS, B = K, V)
+//   P = exp2(S c - LSE log2 e), dS = P (dP - delta)
+//   dV^T = sum_rb dO^T P, dK^T = sum_rb Q^T dS   (A by transposed LDS reads)
+template <class E, int D, bool CAUSAL, int NRB>
+__global__ __launch_bounds__(256, (D <= 128 && NRB == 1 ? 2 : 1)) void fa_dkv_stream_kernel(SplitArgs a) {
+  constexpr int BM = 32 * NRB;  // packed rows held
+  constexpr int P = Tile<D>::P;
+  constexpr int NKD = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * 64 * P];  // [Q rows | dO rows]
+  __shared__ __attribute__((aligned(16))) float stat[2][64];          // [lse | delta][row]
+  // per-wavefront staging of a finished 32-key block, rows of D + 8
+  // elements (16-byte aligned, bank-shifted), so that its rows leave in
+  // 16-byte pieces that fill whole rows instead of one 8-byte piece per key
+  constexpr int SP = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t stage[4][32 * SP];
+
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = blockIdx.x % a.nsplit, bh = blockIdx.x / a.nsplit;
+  const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
+  const int Lq = a.Lq, Lk = a.Lk, off = a.off, R = a.R;
+  const int kb = s * a.chunk, ke = min(Lk, kb + a.chunk);
+
+  // ---- resident rows: packed row r is query r % Lq of query head hk G + r / Lq
+  // (rows past R repeat row R - 1 and are masked)
+  {
+    const TileLoader<D> ld(w, lane, 0);
+    auto rowoff = [&](const Tensor& t) {
+      return [&t, R, Lq](int r) {
+        const int rr = min(r, R - 1), hi = rr / Lq;
+        return (int)(hi * t.sh + (int64_t)(rr - hi * Lq) * t.sl);
+      };
+    };
+    ld.template gather<64>(smem, a.q.head(b, hk * a.G), rowoff(a.q), w);
+    ld.template gather<64>(smem + 64 * P, a.dO.head(b, hk * a.G), rowoff(a.dO), w);
+    const int64_t srow = ((int64_t)b * a.Hq + hk * a.G) * Lq;  // the group's rows are adjacent
+    if (w == 0) load_row_stat(&stat[0][0], a.lse + srow, 0, R, lane);
+    if (w == 1) load_row_stat(&stat[1][0], a.delta + srow, 0, R, lane);
+  }
+
+  const bf16_t* kp = a.k.head(b, hk);
+  const bf16_t* vp = a.v.head(b, hk);
+  auto fetch = [&](int key0, bf16x8* kf, bf16x8* vf) {
+    const int key = min(key0 + lr, Lk - 1);  // keys past Lk: a copy, never stored
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) {
+      kf[kd] = as_bf16x8(ldg16(kp + (int64_t)key * a.k.sl + 16 * kd + 8 * lg));
+      vf[kd] = as_bf16x8(ldg16(vp + (int64_t)key * a.v.sl + 16 * kd + 8 * lg));
+    }
+  };
+  int key0 = kb + 32 * w;
+  bf16x8 kf[NKD], vf[NKD];
+  if (key0 < ke) fetch(key0, kf, vf);
+  wait_vmem();
+  __syncthreads();
+
+  TileReaderX<D> rq(lane);
+  const bf16_t* Qs = smem;
+  const bf16_t* Ds = smem + 64 * P;
+  const float c2 = a.scale_log2, sc = a.scale;
+
+  for (; key0 < ke; key0 += 128) {
+    bf16x8 kn[NKD], vn[NKD];
+    const bool more = key0 + 128 < ke;
+    if (more) fetch(key0 + 128, kn, vn);
+    const int krow = key0 + lr;
+    bf16x8 pf[NRB][2], ds[NRB][2];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r0 = 32 * rb;
+      f32x16 sv = zero16(), dp = zero16();
+#pragma unroll
+      for (int kd = 0; kd < NKD; ++kd) {
+        sv = E::mma(rq.row16(Qs, r0, kd), kf[kd], sv);
+        dp = E::mma(rq.row16(Ds, r0, kd), vf[kd], dp);
+      }
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[0][r0 + 8 * i4 + 4 * lg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[4 * i4 + e] = fast_exp2(fmaf(sv[4 * i4 + e], c2, l4[e] * -kLog2e));
+      }
+      // rows past R, and (causal) keys past a row's diagonal: key krow is
+      // visible to packed row r iff krow <= r % Lq + off
+      if (r0 + 32 > R || (CAUSAL && key0 + 31 > off)) {
+        __asm__ volatile("");
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = r0 + crow(i, lg);
+          const bool ok = r < R && (!CAUSAL || krow <= r % Lq + off);
+          sv[i] = ok ? sv[i] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[1][r0 + 8 * i4 + 4 * lg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = sv[4 * i4 + e] * (dp[4 * i4 + e] - d4[e]);
+      }
+      pf[rb][0] = E::pack8(sv, 0);
+      pf[rb][1] = E::pack8(sv, 1);
+      ds[rb][0] = E::pack8(dp, 0);
+      ds[rb][1] = E::pack8(dp, 1);
+    }
+    // dV^T, then dK^T, through one set of accumulators
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const bf16_t* src = pass == 0 ? Ds : Qs;
+      f32x16 acc[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = E::mma(rq.trA(src, 32 * rb + 16 * h, db), pass == 0 ? pf[rb][h] : ds[rb][h], acc[db]);
+      // C layout (lane = key, registers = d) into the staging rows, then
+      // whole rows out: lane l takes 16-byte chunk l % CPR of row l / CPR
+      const float mul = pass == 0 ? 1.f : sc;
+      bf16_t* stg = stage[w];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16& c = acc[db];
+          *reinterpret_cast<uint2*>(stg + lr * SP + 32 * db + 8 * q4 + 4 * lg) =
+              E::pack4(c[4 * q4] * mul, c[4 * q4 + 1] * mul, c[4 * q4 + 2] * mul, c[4 * q4 + 3] * mul);
+        }
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's LDS writes are in order
+      constexpr int CPR = D / 8, RPI = 64 / CPR;               // 16-byte chunks per row, rows per pass
+      const Tensor& out = pass == 0 ? a.dv : a.dk;
+      if (lane < RPI * CPR) {
+        const int c8 = 8 * (lane % CPR);
+#pragma unroll
+        for (int r = lane / CPR; r < 32; r += RPI) {
+          const int key = key0 + r;
+          if (key < Lk)
+            *reinterpret_cast<uint4*>(out.head(b, hk) + (int64_t)key * out.sl + c8) =
+                *reinterpret_cast<const uint4*>(stg + r * SP + c8);
+        }
+      }
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass writes
+    }
+    if (more) {
+#pragma unroll
+      for (int kd = 0; kd < NKD; ++kd) {
+        kf[kd] = kn[kd];
+        vf[kd] = vn[kd];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 #ifndef CGQA_SPLIT_NBUF
 #define CGQA_SPLIT_NBUF 2
@@ -515,6 +682,41 @@ static hipError_t dq_short_e(const SplitArgs& a, int D, bool causal, hipStream_t
     case 256: return launch_dq_short_d<E, 256, 32>(a, causal, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <class E, int D, int NRB>
+static void launch_dkv_short_r(const SplitArgs& a, bool causal, hipStream_t stream) {
+  const int nwg = a.B * a.Hkv * a.nsplit;
+  if (causal)
+    hipLaunchKernelGGL((fa_dkv_stream_kernel<E, D, true, NRB>), dim3(nwg), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fa_dkv_stream_kernel<E, D, false, NRB>), dim3(nwg), dim3(256), 0, stream, a);
+}
+
+template <class E, int D>
+static hipError_t launch_dkv_short_d(const SplitArgs& a, bool causal, hipStream_t stream) {
+  if (a.R <= 32)
+    launch_dkv_short_r<E, D, 1>(a, causal, stream);
+  else if constexpr (D <= 128)  // 64 rows at D = 256 would not fit the registers
+    launch_dkv_short_r<E, D, 2>(a, causal, stream);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <class E>
+static hipError_t dkv_short_e(const SplitArgs& a, int D, bool causal, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_dkv_short_d<E, 64>(a, causal, stream);
+    case 96: return launch_dkv_short_d<E, 96>(a, causal, stream);
+    case 128: return launch_dkv_short_d<E, 128>(a, causal, stream);
+    case 256: return launch_dkv_short_d<E, 256>(a, causal, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_dkv_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream) {
+  return f16 ? dkv_short_e<FP16>(a, D, causal, stream) : dkv_short_e<BF16>(a, D, causal, stream);
 }
 
 hipError_t launch_fwd_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream) {

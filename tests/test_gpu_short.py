@@ -97,12 +97,13 @@ def test_short_agrees_with_long_path(D):
     for n, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
         err = (s[n].float() - t.float()).abs().max().item()
         assert err <= 1e-2 * t.float().abs().max().item(), (n, err)
-    # the dK/dV half is the long path's kernel: from the same lse and delta,
-    # bitwise the same
+    # from the same lse and delta, the short dK/dV (rows resident, keys
+    # streamed) differs from the key-block kernel only in summation order
     _, dk2, dv2 = fa.fa_bwd_short(g["q"], g["k"], g["v"], lse, delta, g["do"], scale=sc, causal=True,
                                   grads="dkv")
     torch.cuda.synchronize()
-    assert torch.equal(dk2, dk) and torch.equal(dv2, dv)
+    for a_, b_ in ((dk2, dk), (dv2, dv)):
+        assert (a_.float() - b_.float()).abs().max().item() <= 4e-3 * b_.float().abs().max().item()
 
 
 def test_short_workspace_contract():
@@ -147,3 +148,11 @@ def test_short_sequence_major_queries(Lq, causal):
     ref = oracle_full(bits, scale, causal)
     for n in ("o", "lse", "dq", "dk", "dv"):
         check(n, to_f64(out[n]), ref[n], f"short bshd Lq{Lq} causal={causal}")
+
+
+@pytest.mark.parametrize("D", [64, 96, 128, 256])
+@pytest.mark.parametrize("Hq,Lq,causal", [(16, 3, True), (8, 8, False), (8, 8, True)])
+def test_short_two_row_blocks(D, Hq, Lq, causal):
+    """More than 32 packed rows per group (48 and 64): two 32-row blocks in
+    the streaming dK/dV (at D = 256 the key-block kernel takes them)."""
+    short_case(1, Hq, 1, Lq, 700, D, causal, seed=10700 + D + Hq + Lq)
