@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
 // previous batch, so a tile is resident at least one phase before it is read.
 // A vector step also reads the next matrix step's K fragments into registers,
 // so that step's S products start on register operands.
-template <class E, int D, int BN, bool CAUSAL, bool MASKED>
+template <class E, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   constexpr int BM = 256;
   constexpr int P = Tile<D>::P;
@@ -300,40 +300,16 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   if (CAUSAL) n_full = min(n_full, (r0 + off + 1) / BN);
   n_full = max(0, min(n_full, wnkt));
 
-  // ---- under a block mask: the key tiles some row of this workgroup needs
-  // (dynamic LDS: up to nkt entries, then the count).  The loop runs over
-  // list positions x; tile(x) is the key tile.
-  extern __shared__ int tlist[];
-  int nt = nkt;
-  if constexpr (MASKED) {
-    const int qb0 = q0 / kMaskBlock, qb1 = (min(q0 + BM, Lq) - 1) / kMaskBlock;
-    if (w == 0) {
-      const int cnt = build_list(tlist, nkt, lane, [](int i) { return i; }, [&](int jj) {
-        bool any = false;
-        for (int qb = qb0; qb <= qb1; ++qb) any |= a.mask[qb * a.nkb + jj * BN / kMaskBlock] != 0;
-        return any;
-      });
-      if (lane == 0) tlist[nkt] = cnt;
-    }
-    __syncthreads();
-    nt = __builtin_amdgcn_readfirstlane(tlist[nkt]);
-  }
-  auto tile = [&](int x) { return MASKED ? __builtin_amdgcn_readfirstlane(tlist[x]) : x; };
-  // does this wavefront's work include list position x?
-  const int wqb = r0 / kMaskBlock;
-  auto need = [&](int x) {
-    if (x < 0 || x >= nt) return false;
-    const int jj = tile(x);
-    if (jj >= wnkt) return false;
-    return !MASKED || a.mask[wqb * a.nkb + jj * BN / kMaskBlock] != 0;
-  };
+  const int nt = nkt;
+  // does this wavefront's work include key tile x?
+  auto need = [&](int x) { return x >= 0 && x < wnkt; };
 
   const TileLoader<D> ld(w & 3, lane, w < 4 ? ks : vs);  // waves 0-3 load K, 4-7 load V
   if (w < 4) {
-    if (nt > 0) ld.template load<BN>(sK, kp, tile(0) * BN, Lk, w);
-    if (nt > 1) ld.template load<BN>(sK + TILE, kp, tile(1) * BN, Lk, w);
+    if (nt > 0) ld.template load<BN>(sK, kp, 0, Lk, w);
+    if (nt > 1) ld.template load<BN>(sK + TILE, kp, BN, Lk, w);
   } else {
-    if (nt > 0) ld.template load<BN>(sV, vp, tile(0) * BN, Lk, w & 3);
+    if (nt > 0) ld.template load<BN>(sV, vp, 0, Lk, w & 3);
   }
 
   bf16x8 qf[NKD];
@@ -343,8 +319,8 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
     for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + (int64_t)qr * qs + 16 * kd + 8 * lg));
   }
 
-  // row reads (K) follow list position x of the matrix step, transposed reads
-  // (V) position x - 1; buffer b sits b * TILE elements in, so moving from
+  // row reads (K) follow key tile x of the matrix step, transposed reads
+  // (V) tile x - 1; buffer b sits b * TILE elements in, so moving from
   // buffer x & 3 to (x + 1) & 3 is an XOR of the offsets with
   // (x odd ? 3 : 1) * TILE
   TileReaderX<D> rd(lane);
@@ -359,15 +335,15 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   for (int nb = 0; nb < NNB; ++nb) s[nb] = zero16();
   bf16x8 pf[NKS];
 
-  // loads issued by matrix step x: K of position x + 2 (waves 0-3) or V of
-  // position x + 1 (waves 4-7); returns whether this wavefront issued any
+  // loads issued by matrix step x: K of tile x + 2 (waves 0-3) or V of
+  // tile x + 1 (waves 4-7); returns whether this wavefront issued any
   auto loads = [&](int x) -> bool {
     if (w < 4) {
       if (x + 2 >= nt) return false;
-      ld.template load<BN>(sK + ((x + 2) & 3) * TILE, kp, tile(x + 2) * BN, Lk, w);
+      ld.template load<BN>(sK + ((x + 2) & 3) * TILE, kp, (x + 2) * BN, Lk, w);
     } else {
       if (x + 1 >= nt) return false;
-      ld.template load<BN>(sV + ((x + 1) & 3) * TILE, vp, tile(x + 1) * BN, Lk, w & 3);
+      ld.template load<BN>(sV + ((x + 1) & 3) * TILE, vp, (x + 1) * BN, Lk, w & 3);
     }
     return true;
   };
@@ -424,10 +400,10 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
     if (x >= 1) rd.flip_tr((((x - 1) & 1) ? 3 : 1) * TILE);
     wait_loads(issued);
   };
-  // vector step x: softmax of S(tile(x)) into P
+  // vector step x: softmax of S(x) into P
   auto vstep = [&](int x) {
     if (!need(x)) return;
-    const int j = tile(x);
+    const int j = x;
     if (j >= n_full) {  // diagonal or ragged tile
       __asm__ volatile("");
       const int last = CAUSAL ? min(qrow + off, Lk - 1) : Lk - 1;
@@ -518,15 +494,18 @@ static hipError_t launch_fwd_d(const FwdArgs& a0, bool causal, hipStream_t strea
   auto go = [&](auto kern, int threads) {
     hipLaunchKernelGGL(kern, dim3(a.B * a.Hq * a.nqt), dim3(threads), list_bytes, stream, a);
   };
-  // ping-pong for D = 96 and 128; at D = 64 the 4-wavefront kernel runs four
-  // wavefronts per SIMD, which hides latency better (measured faster)
+  // ping-pong for D = 96 and 128 without a mask.  At D = 64 the 4-wavefront
+  // kernel runs four wavefronts per SIMD, which hides latency better; under a
+  // block mask its 128-row workgroups visit fewer key tiles than 256-row ones
+  // (measured faster with a 1024-key sliding window at 8192 tokens)
   if constexpr (D == 96 || D == 128) {
-    a.nqt = (a.Lq + 255) / 256;
-    if (causal)
-      masked ? go(fa_fwd_pp_kernel<E, D, BN, true, true>, 512) : go(fa_fwd_pp_kernel<E, D, BN, true, false>, 512);
-    else
-      masked ? go(fa_fwd_pp_kernel<E, D, BN, false, true>, 512) : go(fa_fwd_pp_kernel<E, D, BN, false, false>, 512);
-  } else {
+    if (!masked) {
+      a.nqt = (a.Lq + 255) / 256;
+      causal ? go(fa_fwd_pp_kernel<E, D, BN, true>, 512) : go(fa_fwd_pp_kernel<E, D, BN, false>, 512);
+      return hipGetLastError();
+    }
+  }
+  {
     a.nqt = (a.Lq + 127) / 128;
     if (causal)
       masked ? go(fa_fwd_kernel<E, D, BN, true, true>, 256) : go(fa_fwd_kernel<E, D, BN, true, false>, 256);
