@@ -705,7 +705,7 @@ static hipError_t launch_bwd_e(const BwdArgs& a, int D, bool causal, int which, 
     case 64: return launch_bwd_d<E, 64, 64>(a, causal, which, stream);
     case 96: return launch_bwd_d<E, 96, 64>(a, causal, which, stream);
     case 128: return launch_bwd_d<E, 128, 64>(a, causal, which, stream);
-    case 256: return launch_bwd_d<E, 256, 32>(a, causal, which, stream);
+    case 256: return launch_bwd_d<E, 256, 64>(a, causal, which, stream);
     default: return hipErrorInvalidValue;
   }
 }

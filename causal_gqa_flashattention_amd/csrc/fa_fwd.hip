@@ -521,7 +521,7 @@ static hipError_t launch_fwd_e(const FwdArgs& a, int D, bool causal, hipStream_t
     case 64: return launch_fwd_d<E, 64, 64>(a, causal, stream);
     case 96: return launch_fwd_d<E, 96, 64>(a, causal, stream);
     case 128: return launch_fwd_d<E, 128, 64>(a, causal, stream);
-    case 256: return launch_fwd_d<E, 256, 32>(a, causal, stream);
+    case 256: return launch_fwd_d<E, 256, 64>(a, causal, stream);
     default: return hipErrorInvalidValue;
   }
 }
