@@ -292,6 +292,23 @@ def summarize_inst(csv_path, workload):
 
 # ------------------------------------------------------------ main
 
+def realtime_counter_hz(lib, dev):
+    """The s_memrealtime counter's rate against HIP events (csrc/probe: one
+    wavefront spins on it for 5e6 ticks); the clock figures assume 100 MHz."""
+    import ctypes
+    import torch
+    if not hasattr(lib, "cgqa_counter_rates"):
+        return None
+    f = lib.cgqa_counter_rates
+    f.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    f.restype = ctypes.c_int
+    st = torch.zeros(4, dtype=torch.int64, device=dev)
+    rt, mt = ctypes.c_double(), ctypes.c_double()
+    rc = f(st.data_ptr(), 5_000_000, ctypes.byref(rt), ctypes.byref(mt))
+    torch.cuda.synchronize()
+    return round(rt.value) if rc == 0 else None
+
+
 def mfma_ceiling(dev, cus):
     """Sustained MFMA throughput (csrc/probe) with constant and with random
     bf16 operands: the second is what kernels on real data can approach,
@@ -316,8 +333,32 @@ def mfma_ceiling(dev, cus):
     torch.cuda.synchronize()
     if rc != 0:
         raise RuntimeError(f"mfma ceiling probe failed: {rc}")
-    return {"constant_operands": round(c.value, 1), "random_operands": round(r.value, 1), "unit": "TFLOP/s",
-            "kernel": "v_mfma_f32_32x32x16_bf16, 2 wavefronts/SIMD, 4 accumulators each, operands in registers"}
+    res = {"constant_operands": round(c.value, 1), "random_operands": round(r.value, 1), "unit": "TFLOP/s",
+           "kernel": "v_mfma_f32_32x32x16_bf16, 2 wavefronts/SIMD, 4 accumulators each, operands in registers"}
+    # the same loops once more with s_memtime / s_memrealtime stamps: the
+    # shader clock they ran at
+    if hasattr(lib, "cgqa_mfma_clock"):
+        fc = lib.cgqa_mfma_clock
+        dbl = ctypes.POINTER(ctypes.c_double)
+        fc.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                       ctypes.c_int, ctypes.c_int, ctypes.c_double] + [dbl] * 4
+        fc.restype = ctypes.c_int
+        stamps = torch.zeros(6 * cus, dtype=torch.int64, device=dev)
+        host = (ctypes.c_uint64 * (6 * cus))()
+        v = [ctypes.c_double() for _ in range(4)]
+        rc = fc(bits.data_ptr(), out.data_ptr(), stamps.data_ptr(), ctypes.addressof(host), cus, 2048, 10, 100e6,
+                *(ctypes.byref(x) for x in v))
+        torch.cuda.synchronize()
+        if rc == 0:
+            tc, gc, tr, gr = (x.value for x in v)
+            res["clock"] = {
+                "realtime_counter_hz": realtime_counter_hz(lib, dev),
+                "constant": {"TFLOP/s": round(tc, 1), "shader_ghz": round(gc, 3)},
+                "random": {"TFLOP/s": round(tr, 1), "shader_ghz": round(gr, 3)},
+                "method": "shader clock = s_memtime ticks per s_memrealtime second (100 MHz) over the loop of "
+                          "wave 0 of each workgroup, median over workgroups, in the last of 10 timed launches",
+            }
+    return res
 
 
 def gemm_canary(dev, n=4096, reps=10):
