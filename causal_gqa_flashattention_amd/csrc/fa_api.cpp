@@ -393,9 +393,12 @@ namespace {
 
 // ---------------------------------------------------------------- short queries
 // Work split of the short-query kernels: packed rows R = G * Lq in blocks of
-// 128, keys in chunks of whole 64-key tiles.  Enough chunks that the grid has
-// about 1024 workgroups (four per CU), but at least 256 keys per chunk so that
-// a workgroup's fixed costs stay small against its loads.
+// 128, keys in chunks of whole 64-key tiles.  Enough chunks that the grid is
+// one round of resident workgroups on the 256 CUs of an MI355X (two per CU at
+// D <= 128, one at D = 256, where a workgroup fills a CU's registers): a
+// second round would repeat each workgroup's start-up and its wait for its
+// first tile (measured slower at 32768 keys).  At least 256 keys per chunk so
+// that a workgroup's fixed costs stay small against its loads.
 struct ShortPlan {
   int R, nrb, nsplit, chunk;
   size_t part_bytes, ml_bytes;
@@ -408,7 +411,8 @@ bool short_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, ShortPlan* p) {
   p->nrb = (p->R + 127) / 128;
   const int64_t tiles = ((int64_t)Lk + 63) / 64;
   const int64_t groups = (int64_t)B * Hkv * p->nrb;
-  int64_t ns = (1024 + groups - 1) / groups;
+  const int64_t target = D <= 128 ? 512 : 256;  // resident workgroups
+  int64_t ns = (target + groups - 1) / groups;
   ns = std::min<int64_t>(ns, std::max<int64_t>(1, tiles / 4));
   ns = std::max<int64_t>(std::min<int64_t>(ns, 1024), 1);  // the merge kernels hold <= 1024 weights
   const int64_t chunk_tiles = (tiles + ns - 1) / ns;
@@ -547,10 +551,12 @@ fa_status fa_bwd_short(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, 
       s.delta = delta;
       s.B = B; s.Hq = Hq; s.Hkv = Hkv; s.Lq = Lq; s.Lk = Lk; s.G = G; s.off = Lk - Lq;
       s.R = G * Lq;
-      // chunks of whole 128-key steps, about 512 workgroups (two per CU)
+      // chunks of whole 128-key steps, about one round of resident workgroups
+      // (two per CU where the kernel fits two, else one)
       const int64_t steps = ((int64_t)Lk + 127) / 128;
       const int64_t groups = (int64_t)B * Hkv;
-      const int64_t want = std::max<int64_t>(1, std::min<int64_t>(steps, (512 + groups - 1) / groups));
+      const int64_t target = D <= 128 && s.R <= 32 ? 512 : 256;
+      const int64_t want = std::max<int64_t>(1, std::min<int64_t>(steps, (target + groups - 1) / groups));
       const int64_t per = (steps + want - 1) / want;
       s.chunk = (int)(per * 128);
       s.nsplit = (int)((steps + per - 1) / per);
