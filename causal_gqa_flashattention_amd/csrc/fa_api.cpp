@@ -400,7 +400,7 @@ namespace {
 // first tile (measured slower at 32768 keys).  At least 256 keys per chunk so
 // that a workgroup's fixed costs stay small against its loads.
 struct ShortPlan {
-  int R, nrb, nsplit, chunk;
+  int R, nrb, nsplit, chunk, wsplit;
   size_t part_bytes, ml_bytes;
 };
 
@@ -411,12 +411,19 @@ bool short_plan(int B, int Hq, int Hkv, int Lq, int Lk, int D, ShortPlan* p) {
   p->nrb = (p->R + 127) / 128;
   const int64_t tiles = ((int64_t)Lk + 63) / 64;
   const int64_t groups = (int64_t)B * Hkv * p->nrb;
-  const int64_t target = D <= 128 ? 512 : 256;  // resident workgroups
+  // R <= 32 at D = 256: the wavefronts of a workgroup split a chunk's tiles
+  // four ways, one workgroup per CU (its four K/V buffers fill the LDS), four
+  // partials per chunk.  (At D = 256 the single computing wavefront of the
+  // plain kernels bounds the dQ split; at D <= 128 the plain kernels, two
+  // workgroups per CU with a tile in flight each, measured faster.)
+  p->wsplit = p->R <= 32 && D == 256 ? 1 : 0;
+  const int64_t target = p->wsplit ? 256 : (D <= 128 ? 512 : 256);  // resident workgroups
+  const int64_t per_chunk = p->wsplit ? 4 : 1;  // partials per chunk
   int64_t ns = (target + groups - 1) / groups;
   ns = std::min<int64_t>(ns, std::max<int64_t>(1, tiles / 4));
-  ns = std::max<int64_t>(std::min<int64_t>(ns, 1024), 1);  // the merge kernels hold <= 1024 weights
+  ns = std::max<int64_t>(std::min<int64_t>(ns, 1024 / per_chunk), 1);  // the merge kernels hold <= 1024 weights
   const int64_t chunk_tiles = (tiles + ns - 1) / ns;
-  p->nsplit = (int)((tiles + chunk_tiles - 1) / chunk_tiles);
+  p->nsplit = (int)(per_chunk * ((tiles + chunk_tiles - 1) / chunk_tiles));
   p->chunk = (int)(chunk_tiles * 64);
   const int64_t rows = (int64_t)B * Hkv * p->nsplit * p->R;
   if (groups * p->nsplit > INT32_MAX) return false;
@@ -431,7 +438,7 @@ cgqa::SplitArgs split_args(const ShortPlan& pl, void* workspace, int B, int Hq, 
   a.part = static_cast<float*>(workspace);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_bytes);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.G = Hq / Hkv; a.off = Lk - Lq;
-  a.R = pl.R; a.nrb = pl.nrb; a.nsplit = pl.nsplit; a.chunk = pl.chunk;
+  a.R = pl.R; a.nrb = pl.nrb; a.nsplit = pl.nsplit; a.chunk = pl.chunk; a.wsplit = pl.wsplit;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   return a;

@@ -353,6 +353,51 @@ struct TileLoader {
   }
 };
 
+// Direct global->LDS copy of a ROWS x D tile by ONE wavefront, into the
+// layout TileLoader<D> produces with four: 1 KiB block b holds tile rows
+// RW * b .. RW * b + RW - 1, lane l filling physical chunk l % PC of row
+// RW * b + l / PC.  The per-lane source offsets repeat every 16 / RW blocks
+// (the swizzle depends on the row modulo 16), so they are kept for one period;
+// each block adds its rows' offset to the wave-uniform base.
+template <int D, int ROWS>
+struct WaveTileLoader {
+  using T = Tile<D>;
+  static constexpr int PC = T::PC, CPR = T::CPR;
+  static constexpr int RW = 64 / PC;               // tile rows per 1 KiB block
+  static constexpr int NBLK = ROWS / RW;           // blocks (loads) per tile
+  static constexpr int PER = 16 / RW < NBLK ? 16 / RW : NBLK;  // blocks per swizzle period
+  static_assert(ROWS % RW == 0 && NBLK % PER == 0, "tile rows");
+  int rs;         // row stride of the source in elements (wave-uniform)
+  int lrow;       // this lane's row within a block
+  int so[PER];    // per-lane source element offset of block b % PER, row offset included
+  __device__ __forceinline__ WaveTileLoader(int lane, int row_stride) : rs(row_stride), lrow(lane / PC) {
+    const int x = lane % PC;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = x ^ T::swz(RW * j + lrow);
+      so[j] = lrow * row_stride + (c < CPR ? c : 0) * 8;  // padding slots (D = 96): any in-bounds data
+    }
+  }
+  // Rows row0 .. row0 + ROWS - 1 of g; rows at or past nrows repeat row
+  // nrows - 1 (row0 < nrows).  NBLK loads; the caller waits on vmcnt.
+  __device__ __forceinline__ void load(bf16_t* tile, const bf16_t* g, int row0, int nrows) const {
+    const bf16_t* const g0 = g + (int64_t)row0 * rs;  // wave-uniform
+    if (row0 + ROWS <= nrows) {
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b)
+        TileLoader<D>::lds_dma16(tile + b * 512, g0 + (int64_t)(RW * b) * rs, (uint32_t)so[b % PER] * 2u);
+    } else {
+      const int last = nrows - 1 - row0;
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b) {
+        const int r = RW * b + lrow;
+        const int c = (so[b % PER] - lrow * rs);  // the chunk's element offset
+        TileLoader<D>::lds_dma16(tile + b * 512, g0, (uint32_t)(min(r, last) * rs + c) * 2u);
+      }
+    }
+  }
+};
+
 // One global_load_lds_dword: lane l's 4 bytes at sbase + voff go to LDS
 // address dst + 4*l (dst and sbase wave-uniform); inline assembly for the
 // reason given at TileLoader::lds_dma16.
@@ -408,6 +453,10 @@ __device__ __forceinline__ int build_list(int* list, int n, int lane, Order orde
   }
   return count;
 }
+
+// s_waitcnt lgkmcnt(0), leaving vmcnt/expcnt unconstrained: this wavefront's
+// LDS reads have returned (before a direct load overwrites what they read).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // s_waitcnt vmcnt(0), leaving expcnt/lgkmcnt unconstrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).

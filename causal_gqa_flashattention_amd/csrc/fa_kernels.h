@@ -65,6 +65,9 @@ struct SplitArgs {
   int B, Hq, Hkv, Lq, Lk, G, off;
   int R, nrb, nsplit, chunk;  // packed rows per group, 128-row blocks, key chunks, keys per chunk
   float scale, scale_log2;
+  // 1 (R <= 32 at D = 256): the four wavefronts of a workgroup split each
+  // chunk's key tiles and write a partial each, so nsplit = 4 x chunks
+  int wsplit;
 };
 
 // Each launcher enqueues on `stream` and returns hipGetLastError().  f16:

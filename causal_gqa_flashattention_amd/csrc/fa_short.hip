@@ -219,6 +219,157 @@ __global__ __launch_bounds__(256, (D <= 128 && NBUF == 2 ? 2 : 1)) void fa_fwd_s
   }
 }
 
+// ---------------------------------------------------------------- forward, R <= 32
+// When all packed rows fit one wavefront (R <= 32) the kernel above computes
+// on one wavefront of four, and at D = 256 a workgroup fills a CU.  Here (the
+// host picks it for D = 256) the four wavefronts of a workgroup split
+// the chunk's key tiles instead (wavefront w takes tiles w, w + 4, ...), each
+// with the same rows, its own K and V buffers in LDS and no barrier, and each
+// writes its own partial (a.nsplit = 4 x chunks; partial 4 c + w of chunk c).
+// A wavefront's K tile is reloaded as soon as its score products have read
+// it, and its V tile after the value products, so the next tile's loads
+// overlap the rest of this one.
+template <class E, int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fa_fwd_split4_kernel(SplitArgs a) {
+  constexpr int P = Tile<D>::P;
+  constexpr int NKD = D / 16, NDB = D / 32, NNB = BN / 32, NKS = BN / 16;
+  constexpr float kSlack = 8.f;
+  constexpr int BUF = 2 * BN * P;  // [K tile | V tile] per wavefront
+  using WL = WaveTileLoader<D, BN>;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = a.nsplit / 4;
+  const int s = blockIdx.x % nch, bh = blockIdx.x / nch;
+  const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
+  const int r = lr;  // packed row (R <= 32)
+  const bool row_ok = r < a.R;
+  const int rr = min(r, a.R - 1), hi = rr / a.Lq, qi = rr - hi * a.Lq, hq = hk * a.G + hi;
+  const int Lk = a.Lk, off = a.off;
+  const int kb = s * a.chunk, ke = min(Lk, kb + a.chunk);
+
+  const bf16_t* kp = a.k.head(b, hk);
+  const bf16_t* vp = a.v.head(b, hk);
+  const int nt = (ke - kb + BN - 1) / BN;
+  const int ntw = nt > w ? (nt - w + 3) / 4 : 0;  // this wavefront's tiles
+  const int full_end = CAUSAL ? min(Lk, off + 1) : Lk;
+  const int n_full = max(0, min(nt, (full_end - kb) / BN));
+
+  bf16_t* const tk = smem + w * BUF;
+  bf16_t* const tv = tk + BN * P;
+  const WL ldk(lane, a.k.sl), ldv(lane, a.v.sl);
+  if (ntw > 0) {
+    ldk.load(tk, kp, kb + w * BN, Lk);
+    ldv.load(tv, vp, kb + w * BN, Lk);
+  }
+  bf16x8 qf[NKD];
+  {
+    const bf16_t* qp = a.q.head(b, hq) + (int64_t)qi * a.q.sl;
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) qf[kd] = as_bf16x8(ldg16(qp + 16 * kd + 8 * lg));
+  }
+  const int last = CAUSAL ? min(qi + off, Lk - 1) : Lk - 1;
+
+  TileReader<D> rd(lane);
+  const float c2 = a.scale_log2;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+
+  wait_vmem();  // first tile and the Q rows
+  for (int i = 0; i < ntw; ++i) {
+    const int t = w + 4 * i;
+    const bool more = i + 1 < ntw;
+    f32x16 sc[NNB];
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) {
+      sc[nb] = zero16();
+#pragma unroll
+      for (int kd = 0; kd < NKD; ++kd) sc[nb] = E::mma(rd.row16(tk, nb * 32, kd), qf[kd], sc[nb]);
+    }
+    read_ahead<NNB * NKD, 1>();
+    if (more) {  // K tile read: load the next one
+      wait_lds();
+      ldk.load(tk, kp, kb + (t + 4) * BN, Lk);
+    }
+    if (t >= n_full) {  // keys past this row's diagonal or past Lk
+      __asm__ volatile("");
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb) {
+        const int thr = last - (kb + t * BN + nb * 32 + 4 * lg);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sc[nb][j] = (crow(j, 0) <= thr) ? sc[nb][j] : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[nb][j]);
+    mx = fmaxf(mx, xor32(mx));
+    const float m_cand = mx * c2;
+    if (__any(m_cand > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[db][j] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float rsum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = fast_exp2(fmaf(sc[nb][j], c2, -m_use));
+        sc[nb][j] = p;
+        rsum += p;
+      }
+    l_run += rsum;
+    bf16x8 pf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) pf[ks] = E::pack8(sc[ks / 2], ks % 2);
+    // V tile of t: it was issued before the next K tile, so at most that
+    // one's loads may still be in flight
+    if (more)
+      wait_vmem_n<WL::NBLK>();
+    else
+      wait_vmem();
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) acc[db] = E::mma(rd.trA(tv, 16 * ks, db), pf[ks], acc[db]);
+    read_ahead<NKS * NDB, 2>();
+    if (more) {  // V tile read: load the next one, then wait for the next K tile
+      wait_lds();
+      ldv.load(tv, vp, kb + (t + 4) * BN, Lk);
+      wait_vmem_n<WL::NBLK>();
+    }
+  }
+
+  // ---- this wavefront's partial: (m, l) and the unnormalised accumulator
+  // (a wavefront without tiles writes l = 0, which the merge skips)
+  const float l_tot = l_run + xor32(l_run);
+  if (row_ok) {
+    const int64_t idx = ((int64_t)bh * a.R + r) * a.nsplit + 4 * s + w;
+    float* pa = a.part + idx * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x16& c = acc[db];
+        *reinterpret_cast<float4*>(pa + 32 * db + 8 * q4 + 4 * lg) =
+            make_float4(c[4 * q4], c[4 * q4 + 1], c[4 * q4 + 2], c[4 * q4 + 3]);
+      }
+    if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + 2 * idx) = make_float2(m_run, l_tot);
+  }
+}
+
 // Merge of one packed row's chunk partials, one workgroup per row.  A row's
 // nsplit partials are adjacent in the workspace, so the workgroup streams
 // one contiguous block: thread t takes float4 column t % (D/4) of chunks
@@ -448,6 +599,140 @@ __global__ __launch_bounds__(256, (D <= 128 && NBUF == 2 ? 2 : 1)) void fa_dq_sp
   }
 }
 
+// ---------------------------------------------------------------- dQ, R <= 32
+// The split of fa_fwd_split4_kernel for dQ: the four wavefronts take the
+// chunk's key tiles in turn, each with its own K and V buffers, and write
+// their own plain partial sums.  dP (V) comes before S (K) in each tile, so
+// that V is reloaded once dP has read it and K once the dQ products have.
+template <class E, int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fa_dq_split4_kernel(SplitArgs a) {
+  constexpr int P = Tile<D>::P;
+  constexpr int NKD = D / 16, NDB = D / 32, NNB = BN / 32, NKS = BN / 16;
+  constexpr int BUF = 2 * BN * P;
+  using WL = WaveTileLoader<D, BN>;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = a.nsplit / 4;
+  const int s = blockIdx.x % nch, bh = blockIdx.x / nch;
+  const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
+  const int r = lr;
+  const bool row_ok = r < a.R;
+  const int rr = min(r, a.R - 1), hi = rr / a.Lq, qi = rr - hi * a.Lq, hq = hk * a.G + hi;
+  const int Lk = a.Lk, off = a.off;
+  const int kb = s * a.chunk, ke = min(Lk, kb + a.chunk);
+
+  const bf16_t* kp = a.k.head(b, hk);
+  const bf16_t* vp = a.v.head(b, hk);
+  const int nt = (ke - kb + BN - 1) / BN;
+  const int ntw = nt > w ? (nt - w + 3) / 4 : 0;
+  const int full_end = CAUSAL ? min(Lk, off + 1) : Lk;
+  const int n_full = max(0, min(nt, (full_end - kb) / BN));
+
+  bf16_t* const tk = smem + w * BUF;
+  bf16_t* const tv = tk + BN * P;
+  const WL ldk(lane, a.k.sl), ldv(lane, a.v.sl);
+  if (ntw > 0) {
+    ldv.load(tv, vp, kb + w * BN, Lk);
+    ldk.load(tk, kp, kb + w * BN, Lk);
+  }
+  bf16x8 qf[NKD], dof[NKD];
+  {
+    const bf16_t* qp = a.q.head(b, hq) + (int64_t)qi * a.q.sl;
+    const bf16_t* dp = a.dO.head(b, hq) + (int64_t)qi * a.dO.sl;
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) {
+      qf[kd] = as_bf16x8(ldg16(qp + 16 * kd + 8 * lg));
+      dof[kd] = as_bf16x8(ldg16(dp + 16 * kd + 8 * lg));
+    }
+  }
+  const int64_t srow = ((int64_t)b * a.Hq + hq) * a.Lq + qi;
+  // rows past R: lse = +inf makes every P exactly 0
+  const float lse2 = row_ok ? a.lse[srow] * kLog2e : INFINITY;
+  const float dl = row_ok ? a.delta[srow] : 0.f;
+  const int last = CAUSAL ? min(qi + off, Lk - 1) : Lk - 1;
+
+  TileReaderX<D> rd(lane);
+  const float c2 = a.scale_log2;
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dq[db] = zero16();
+
+  wait_vmem();
+  for (int i = 0; i < ntw; ++i) {
+    const int t = w + 4 * i;
+    const bool more = i + 1 < ntw;
+    f32x16 sc[NNB], dp[NNB];
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) {
+      dp[nb] = zero16();
+#pragma unroll
+      for (int kd = 0; kd < NKD; ++kd) dp[nb] = E::mma(rd.row16(tv, nb * 32, kd), dof[kd], dp[nb]);
+    }
+    read_ahead<NNB * NKD, 1>();
+    // V tile read: load the next one; the K tile of t, issued before it, has
+    // to be in
+    if (more) {
+      wait_lds();
+      ldv.load(tv, vp, kb + (t + 4) * BN, Lk);
+      wait_vmem_n<WL::NBLK>();
+    } else {
+      wait_vmem();
+    }
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) {
+      sc[nb] = zero16();
+#pragma unroll
+      for (int kd = 0; kd < NKD; ++kd) sc[nb] = E::mma(rd.row16(tk, nb * 32, kd), qf[kd], sc[nb]);
+    }
+    read_ahead<NNB * NKD, 1>();
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sc[nb][j] = fast_exp2(fmaf(sc[nb][j], c2, -lse2));
+    if (t >= n_full) {
+      __asm__ volatile("");
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb) {
+        const int thr = last - (kb + t * BN + nb * 32 + 4 * lg);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sc[nb][j] = (crow(j, 0) <= thr) ? sc[nb][j] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sc[nb][j] = sc[nb][j] * (dp[nb][j] - dl);  // dS^T
+    bf16x8 dsf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) dsf[ks] = E::pack8(sc[ks / 2], ks % 2);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dq[db] = E::mma(rd.trA(tk, 16 * ks, db), dsf[ks], dq[db]);
+    read_ahead<NKS * NDB, 2>();
+    if (more) {  // K tile read: load the next one, then wait for the next V tile
+      wait_lds();
+      ldk.load(tk, kp, kb + (t + 4) * BN, Lk);
+      wait_vmem_n<WL::NBLK>();
+    }
+  }
+
+  if (row_ok) {
+    const int64_t idx = ((int64_t)bh * a.R + r) * a.nsplit + 4 * s + w;
+    float* pd = a.part + idx * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x16& c = dq[db];
+        *reinterpret_cast<float4*>(pd + 32 * db + 8 * q4 + 4 * lg) =
+            make_float4(c[4 * q4], c[4 * q4 + 1], c[4 * q4 + 2], c[4 * q4 + 3]);
+      }
+  }
+}
+
 // dQ = scale * sum over chunks, one workgroup per packed row.
 template <class E, int D>
 __global__ __launch_bounds__(256) void fa_dq_reduce_kernel(SplitArgs a) {
@@ -640,6 +925,16 @@ constexpr int kSplitBufs = CGQA_SPLIT_NBUF;
 
 template <class E, int D, int BN>
 static hipError_t launch_fwd_short_d(const SplitArgs& a, bool causal, hipStream_t stream) {
+  if (a.wsplit) {
+    const int nwg = a.B * a.Hkv * (a.nsplit / 4);
+    if (causal)
+      hipLaunchKernelGGL((fa_fwd_split4_kernel<E, D, BN, true>), dim3(nwg), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fa_fwd_split4_kernel<E, D, BN, false>), dim3(nwg), dim3(256), 0, stream, a);
+    const int64_t rows = (int64_t)a.B * a.Hkv * a.R;
+    hipLaunchKernelGGL((fa_fwd_combine_kernel<E, D>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const int nwg = a.B * a.Hkv * a.nsplit * a.nrb;
   if (causal)
     hipLaunchKernelGGL((fa_fwd_split_kernel<E, D, BN, true, kSplitBufs>), dim3(nwg), dim3(256), 0, stream, a);
@@ -652,6 +947,16 @@ static hipError_t launch_fwd_short_d(const SplitArgs& a, bool causal, hipStream_
 
 template <class E, int D, int BN>
 static hipError_t launch_dq_short_d(const SplitArgs& a, bool causal, hipStream_t stream) {
+  if (a.wsplit) {
+    const int nwg = a.B * a.Hkv * (a.nsplit / 4);
+    if (causal)
+      hipLaunchKernelGGL((fa_dq_split4_kernel<E, D, BN, true>), dim3(nwg), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fa_dq_split4_kernel<E, D, BN, false>), dim3(nwg), dim3(256), 0, stream, a);
+    const int64_t rows = (int64_t)a.B * a.Hkv * a.R;
+    hipLaunchKernelGGL((fa_dq_reduce_kernel<E, D>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const int nwg = a.B * a.Hkv * a.nsplit * a.nrb;
   if (causal)
     hipLaunchKernelGGL((fa_dq_split_kernel<E, D, BN, true, kSplitBufs>), dim3(nwg), dim3(256), 0, stream, a);
