@@ -89,6 +89,21 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// c *= alpha for an accumulator the compiler keeps in AGPRs (kernels at one
+// wavefront per SIMD with a 128-register accumulator).  Written as inline
+// assembly on the AGPRs themselves: as plain code the compiler copies every
+// accumulator register to a VGPR at the top of the loop, on every tile, for
+// a rescale that runs on few of them.
+__device__ __forceinline__ void scale_agpr(f32x16& c, float alpha) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float t;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(c[i]), "=&v"(t)
+                 : "v"(alpha));
+  }
+}
+
 // Row of the C/D layout held by register i of lane group g = lane / 32.
 __device__ __forceinline__ constexpr int crow(int i, int g) { return 8 * (i / 4) + 4 * g + (i % 4); }
 

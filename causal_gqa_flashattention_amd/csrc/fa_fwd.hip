@@ -173,13 +173,18 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
     mx = fmaxf(mx, xor32(mx));
     const float m_cand = mx * c2;
     if (__any(m_cand > m_run + kSlack)) {
+      __asm__ volatile("");  // a real branch: the rescale is rare, not done on every tile
       const float m_new = fmaxf(m_run, m_cand);
       const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db) {
+        if constexpr (D > 128)
+          scale_agpr(acc[db], alpha);
+        else
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      }
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
@@ -422,13 +427,18 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
     mx = max_xor32(mx);
     const float m_cand = mx * c2;
     if (__any(m_cand > m_run + kSlack)) {
+      __asm__ volatile("");  // a real branch: the rescale is rare, not done on every tile
       const float m_new = fmaxf(m_run, m_cand);
       const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db) {
+        if constexpr (D > 128)
+          scale_agpr(acc[db], alpha);
+        else
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      }
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
