@@ -223,9 +223,11 @@ def cpu_baseline(w, bits, budget_s=30.0, mask=None, pairs=None):
 
 
 def executed_mfma(w):
-    """MFMA instructions the kernels issue for workload w, following their
-    tilings (diagonal tiles run whole, waves past Lq idle): the count that
-    SQ_INSTS_MFMA should read.  One instruction is 32x32x16, 32768 FLOP."""
+    """Matrix work the kernels issue for workload w, following their tilings
+    (diagonal tiles run whole, waves past Lq idle), in units of one
+    32x32x16 instruction (32768 FLOP; a 16x16x32 one counts half).  Where
+    only 32x32x16 instructions run (D <= 128) it is the count SQ_INSTS_MFMA
+    should read."""
     cdiv = lambda a, b: -(-a // b)
     D, B, Hq, Hkv, Lq, Lk = w.D, w.B, w.Hq, w.Hkv, w.Lq, w.Lk
     G, off, causal = Hq // Hkv, Lk - Lq, w.causal
@@ -242,21 +244,26 @@ def executed_mfma(w):
                 r0 = qt * 256 + 32 * wv
                 if r0 < Lq:
                     fwd += per_tile * cdiv(kv_end(r0 + 32), 64)
-    else:  # 4 waves, 128 rows, 64-key tiles (D=256: 32)
-        bn = 32 if D == 256 else 64
-        per_tile = (bn // 32) * NKD + NDB * (bn // 16)
+    else:  # 4 waves, 128 rows, 64-key tiles
+        per_tile = 2 * NKD + NDB * 4
         for qt in range(cdiv(Lq, 128)):
-            fwd += 4 * per_tile * cdiv(kv_end(qt * 128 + 128), bn)
-    bn = 32 if D == 256 else 64  # dQ: 4 waves, 128 rows
-    dq = 0
+            fwd += 4 * per_tile * cdiv(kv_end(qt * 128 + 128), 64)
+    dq = 0  # 4 waves, 128 rows, 64-key tiles
     for qt in range(cdiv(Lq, 128)):
-        dq += 4 * (2 * (bn // 32) * NKD + NDB * (bn // 16)) * cdiv(kv_end(qt * 128 + 128), bn)
-    bnk, waves = (64, 4) if D == 256 else (128, 8)  # dK/dV: query tiles of 64
+        dq += 4 * (4 * NKD + NDB * 4) * cdiv(kv_end(qt * 128 + 128), 64)
+    # dK/dV, query tiles of 64: 8 waves x 128 keys up to D = 128; at D = 256
+    # 4 waves x 64 keys, or x 32 keys (16 rows each) below 1024 64-key workgroups
+    if D != 256:
+        bnk, per_iter = 128, 8 * (2 * NKD + 4 * NDB)
+    elif B * Hkv * cdiv(Lk, 64) >= 1024:
+        bnk, per_iter = 64, 4 * (2 * NKD + 4 * NDB)
+    else:
+        bnk, per_iter = 32, 4 * (2 * (D // 32) + 2 * NDB)
     dkv = 0
     for kt in range(cdiv(Lk, bnk)):
         qfirst = max(0, kt * bnk - off) if causal else 0
         nq = max(0, cdiv(Lq, 64) - qfirst // 64)
-        dkv += waves * G * nq * (2 * NKD + 4 * NDB)
+        dkv += G * nq * per_iter
     return {"fwd": fwd * B * Hq, "dq": dq * B * Hq, "dkv": dkv * B * Hkv}
 
 

@@ -640,6 +640,253 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- dK / dV, wide heads, 32 keys
+// Head dim 256 with few key/value heads: with 64-key workgroups a causal
+// triangle at 8192 tokens and two heads is 256 workgroups, one per CU, and
+// the kernel lasts as long as the first key tile.  Here a workgroup of 4
+// wavefronts takes 32 keys, which doubles the workgroups; they are numbered
+// key tile major, so each XCD (workgroups round-robin over the eight) gets
+// one key/value head's tiles, every fourth one, heaviest first, and the
+// second round fills the CUs that light first-round workgroups free.
+// Wavefront w owns rows 16 w .. 16 w + 15 of every 64-row query tile and all
+// 32 keys: S and dP are 16x16x32 products over two 16-key blocks, which
+// v_permlane16_swap turns into the k-major B operand of the 32x32x16 dV / dK
+// products (k = this wavefront's 16 rows).  The four wavefronts' partial dK /
+// dV are added through LDS at the end, each finishing a quarter of the
+// columns.
+template <class E, int D, bool CAUSAL, bool MASKED>
+__global__ __launch_bounds__(256, 1) void fa_dkv_k32_kernel(BwdArgs a) {
+  constexpr int BN = 32;  // keys per workgroup
+  constexpr int BM = 64;  // query rows per tile, 16 per wavefront
+  constexpr int P = Tile<D>::P;
+  constexpr int NS = D / 32;   // 16x16x32 steps over the head dim
+  constexpr int NDB = D / 32;  // 32-column blocks of dK / dV
+  constexpr int OWN = NDB / 4;  // column blocks each wavefront finishes
+  static_assert(NDB % 4 == 0, "column blocks must split over four wavefronts");
+
+  constexpr int BUF = 2 * BM * P;  // [Q tile | dO tile]
+  static_assert((BUF & (BUF - 1)) == 0, "buffer size must be a power of two");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][64];  // [buf][lse / delta][row]
+
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int l16 = lane & 15, g16 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r0 = 16 * w;  // this wavefront's rows within a tile
+  const int G = a.G;
+  const int nbh = a.B * a.Hkv;
+  const int kt = blockIdx.x / nbh;  // key tile 0 sees the most queries: heaviest first
+  const int bh = blockIdx.x - kt * nbh;
+  const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
+  const int Lq = a.Lq, Lk = a.Lk, off = a.off;
+
+  const int k0 = kt * BN;
+  const int krow = k0 + lr;  // key of this lane's dK / dV column
+  const bool key_ok = krow < Lk;
+
+  const int qfirst = CAUSAL ? max(0, k0 - off) : 0;
+  const int qt_first = qfirst / BM;
+  const int nqt = (Lq + BM - 1) / BM;
+  const int nq = max(0, nqt - qt_first);
+  // iteration n: query tile nqt - 1 - n / G of query head n % G (last tile
+  // first, heads innermost: the workgroups on one XCD share each tile in L2)
+  extern __shared__ int qlist[];
+  int nql = nq;
+  if constexpr (MASKED) {
+    const int kb0 = k0 / kMaskBlock, kb1 = (min(k0 + BN, Lk) - 1) / kMaskBlock;
+    if (w == 0) {
+      const int cnt = build_list(qlist, nq, lane, [&](int i) { return nqt - 1 - i; }, [&](int qtl) {
+        bool any = false;
+        for (int kbk = kb0; kbk <= kb1; ++kbk) any |= a.mask[qtl * a.nkb + kbk] != 0;
+        return any;
+      });
+      if (lane == 0) qlist[nq] = cnt;
+    }
+    __syncthreads();
+    nql = __builtin_amdgcn_readfirstlane(qlist[nq]);
+  }
+  const int niter = G * nql;
+  auto qtile_of = [&](int n) { return MASKED ? __builtin_amdgcn_readfirstlane(qlist[n / G]) : nqt - 1 - n / G; };
+
+  const TileLoader<D> ldq(w, lane, a.q.sl), ldo(w, lane, a.dO.sl);
+  const bf16_t* const qsrc = a.q.head(b, hk * G);
+  const bf16_t* const osrc = a.dO.head(b, hk * G);
+  auto issue = [&](int n) {
+    bf16_t* qt_lds = smem + (n & 1) * BUF;
+    const int hi = n % G, qtile = qtile_of(n);
+    const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
+    const int qbase = qtile * BM;
+    if (w == 0) load_row_stat(&stat[n & 1][0][0], a.lse + qh, qbase, Lq, lane);
+    if (w == 1) load_row_stat(&stat[n & 1][1][0], a.delta + qh, qbase, Lq, lane);
+    ldq.template load<BM>(qt_lds, qsrc + hi * a.q.sh, qbase, Lq, w);
+    ldo.template load<BM>(qt_lds + BM * P, osrc + hi * a.dO.sh, qbase, Lq, w);
+  };
+  if (niter > 0) issue(0);
+
+  // K and V as 16x16x32 B fragments: key 16 kb + lane % 16, head-dim slots
+  // 32 s + 8 (lane / 16) + e
+  bf16x8 kf[NS][2], vf[NS][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int kr = min(k0 + 16 * kb + l16, Lk - 1);  // keys past Lk: a copy, never stored
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      kf[st][kb] = as_bf16x8(ldg16(a.k.head(b, hk) + (int64_t)kr * a.k.sl + 32 * st + 8 * g16));
+      vf[st][kb] = as_bf16x8(ldg16(a.v.head(b, hk) + (int64_t)kr * a.v.sl + 32 * st + 8 * g16));
+    }
+  }
+
+  TileReader16<D> rd(lane);
+  const float c2 = a.scale_log2;
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+  const int rq = r0 + 4 * g16;  // first of this lane's four S rows within a tile
+
+  wait_vmem();
+  __syncthreads();
+  for (int n = 0; n < niter; ++n) {
+    const int buf = n & 1;
+    const int q0 = qtile_of(n) * BM;
+    if (n + 1 < niter) issue(n + 1);
+    const bf16_t* Qs = smem;  // + buf * BUF through the reader's flipped offsets
+    const bf16_t* Ds = smem + BM * P;
+
+    f32x4 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[kb][i] = dp[kb][i] = 0.f;
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const bf16x8 qa = rd.a16(Qs, r0, st), da = rd.a16(Ds, r0, st);
+      s[0] = E::mma16(qa, kf[st][0], s[0]);
+      s[1] = E::mma16(qa, kf[st][1], s[1]);
+      dp[0] = E::mma16(da, vf[st][0], dp[0]);
+      dp[1] = E::mma16(da, vf[st][1], dp[1]);
+    }
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][rq]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], c2, l4[i] * -kLog2e));
+    // tiles that cross the diagonal or hold rows past Lq
+    if ((CAUSAL && k0 + BN - 1 > q0 + off) || q0 + BM > Lq) {
+      __asm__ volatile("");
+      const int rlim = Lq - q0 - rq;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int thr = CAUSAL ? k0 + 16 * kb + l16 - off - q0 - rq : INT_MIN;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kb][i] = (i >= thr && i < rlim) ? s[kb][i] : 0.f;
+      }
+    }
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][rq]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dp[kb][i] = s[kb][i] * (dp[kb][i] - d4[i]);
+    // C layout (rows 4 (lane / 16) + i of key block kb) -> B operand (key
+    // lane % 32, rows 8 (lane / 32) + e): even 16-lane rows keep block 0 and
+    // take the odd row's block 0, odd rows give their block 0 for the even
+    // row's block 1
+    uint2 p0 = E::pack4(s[0][0], s[0][1], s[0][2], s[0][3]);
+    uint2 p1 = E::pack4(s[1][0], s[1][1], s[1][2], s[1][3]);
+    uint2 t0 = E::pack4(dp[0][0], dp[0][1], dp[0][2], dp[0][3]);
+    uint2 t1 = E::pack4(dp[1][0], dp[1][1], dp[1][2], dp[1][3]);
+    swap16(p0.x, p1.x);
+    swap16(p0.y, p1.y);
+    swap16(t0.x, t1.x);
+    swap16(t0.y, t1.y);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(p0.x, p0.y, p1.x, p1.y));
+    const bf16x8 dsf = __builtin_bit_cast(bf16x8, make_uint4(t0.x, t0.y, t1.x, t1.y));
+    // dV / dK: the transposed reads run two column blocks ahead of their
+    // products (one wavefront per SIMD: nothing else covers their latency)
+    bf16x8 fo[2], fq[2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      fo[db] = rd.trA(Ds, r0, db);
+      fq[db] = rd.trA(Qs, r0, db);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      dv[db] = E::mma(fo[db & 1], pf, dv[db]);
+      dk[db] = E::mma(fq[db & 1], dsf, dk[db]);
+      if (db + 2 < NDB) {
+        fo[db & 1] = rd.trA(Ds, r0, db + 2);
+        fq[db & 1] = rd.trA(Qs, r0, db + 2);
+      }
+    }
+    // keep that order: LDS reads (delta, then blocks 0 and 1), then per block
+    // its two products and the reads of the block two ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (db + 2 < NDB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+
+    rd.flip(BUF);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // ---- add the four wavefronts' partials: each hands the column blocks it
+  // does not finish to their owner through LDS (the tile buffers are free)
+  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [wave][db][i4][lane]
+  static_assert(4 * NDB * 4 * 64 * 16 <= 2 * BUF * 2, "reduction buffer too small");
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    f32x16* acc = pass == 0 ? dk : dv;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      if (db / OWN != w) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          red[((w * NDB + db) * 4 + i4) * 64 + lane] =
+              f32x4{acc[db][4 * i4], acc[db][4 * i4 + 1], acc[db][4 * i4 + 2], acc[db][4 * i4 + 3]};
+      }
+    __syncthreads();
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      if (db / OWN == w) {
+#pragma unroll
+        for (int src = 0; src < 4; ++src)
+          if (src != w) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const f32x4 v = red[((src * NDB + db) * 4 + i4) * 64 + lane];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[db][4 * i4 + e] += v[e];
+            }
+          }
+      }
+    __syncthreads();
+  }
+
+  if (key_ok) {
+    bf16_t* dkp = a.dk.head(b, hk) + (int64_t)krow * a.dk.sl;
+    bf16_t* dvp = a.dv.head(b, hk) + (int64_t)krow * a.dv.sl;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      if (db / OWN == w) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16 &ck = dk[db], &cv = dv[db];
+          *reinterpret_cast<uint2*>(dkp + 32 * db + 8 * q4 + 4 * lg) =
+              E::pack4(ck[4 * q4] * sc, ck[4 * q4 + 1] * sc, ck[4 * q4 + 2] * sc, ck[4 * q4 + 3] * sc);
+          *reinterpret_cast<uint2*>(dvp + 32 * db + 8 * q4 + 4 * lg) =
+              E::pack4(cv[4 * q4], cv[4 * q4 + 1], cv[4 * q4 + 2], cv[4 * q4 + 3]);
+        }
+      }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 template <class E>
@@ -666,7 +913,12 @@ hipError_t launch_delta(const DeltaArgs& a, int D, bool f16, hipStream_t stream)
 template <class E, int D, int BN_Q>
 static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStream_t stream) {
   BwdArgs a = a0;
-  a.nkt = (a.Lk + (D > 128 ? 63 : 127)) / (D > 128 ? 64 : 128);  // keys per dK/dV workgroup
+  // keys per dK/dV workgroup: 128 up to D = 128; at D = 256, 64, or 32 when
+  // 64-key workgroups would make fewer than four per CU (measured: 32-key
+  // workgroups are faster up to 512 64-key ones, slower from 1024)
+  const bool k32 = D > 128 && (int64_t)a.B * a.Hkv * ((a.Lk + 63) / 64) < 1024;
+  const int bnk = D > 128 ? (k32 ? 32 : 64) : 128;
+  a.nkt = (a.Lk + bnk - 1) / bnk;
   const bool masked = a.mask != nullptr;
   // dynamic LDS under a block mask: each workgroup's tile list and its count
   const size_t dq_list = masked ? ((size_t)(a.Lk + BN_Q - 1) / BN_Q + 1) * sizeof(int) : 0;
@@ -685,7 +937,12 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
   }
   if (ndkv > 0) {
     if constexpr (D > 128) {
-      if (causal)
+      if (k32) {
+        if (causal)
+          masked ? dkv(fa_dkv_k32_kernel<E, D, true, true>) : dkv(fa_dkv_k32_kernel<E, D, true, false>);
+        else
+          masked ? dkv(fa_dkv_k32_kernel<E, D, false, true>) : dkv(fa_dkv_k32_kernel<E, D, false, false>);
+      } else if (causal)
         masked ? dkv(fa_dkv_reg_kernel<E, D, true, true>) : dkv(fa_dkv_reg_kernel<E, D, true, false>);
       else
         masked ? dkv(fa_dkv_reg_kernel<E, D, false, true>) : dkv(fa_dkv_reg_kernel<E, D, false, false>);

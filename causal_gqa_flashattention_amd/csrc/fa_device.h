@@ -53,6 +53,12 @@ struct BF16 {
     for (int s = 0; s < 8; ++s) r[s] = (__bf16)c[8 * half + s];
     return r;
   }
+  // v_mfma_f32_16x16x32_bf16: C[16x16] += A[16x32] * B[32x16]; lane l holds
+  // A row / B column l % 16 with k = 8*(l / 16) + s, and C column l % 16,
+  // rows 4*(l / 16) + i
+  __device__ __forceinline__ static f32x4 mma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
   __device__ __forceinline__ static uint2 pack4(float x0, float x1, float x2, float x3) {
     const bf16x4 r = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
     return __builtin_bit_cast(uint2, r);
@@ -72,6 +78,10 @@ struct FP16 {
 #pragma unroll
     for (int s = 0; s < 8; ++s) r[s] = (_Float16)c[8 * half + s];
     return __builtin_bit_cast(bf16x8, r);
+  }
+  __device__ __forceinline__ static f32x4 mma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                  c, 0, 0, 0);
   }
   __device__ __forceinline__ static uint2 pack4(float x0, float x1, float x2, float x3) {
     const f16x4 r = {(_Float16)x0, (_Float16)x1, (_Float16)x2, (_Float16)x3};
@@ -135,6 +145,12 @@ __device__ __forceinline__ float max_xor32(float x) {
   float a = x, b = x;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return fmaxf(a, b);
+}
+
+// v_permlane16_swap: within each pair of 16-lane rows, the odd row of `a`
+// and the even row of `b` trade places.
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
 __device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -275,6 +291,45 @@ struct TileReaderX {
     const int o = tr0 ^ (64 * (db % NTR));
     return cat8(lds_read_tr4(reinterpret_cast<const bf16_t*>(p + o)),
                 lds_read_tr4(reinterpret_cast<const bf16_t*>(p + (o ^ (32 | 16 * P)))));
+  }
+};
+
+// Reads for a wavefront that owns 16 rows of a tile (rows of >= 256 bytes).
+//  a16(tile, r0, s): 16x16x32 A/B fragment of rows r0 + lane % 16, head-dim
+//    slots 32*s + 8*(lane/16) + e (one 16-byte read).
+//  trA(tile, r0, db): 32x32x16 A operand whose rows are tile columns
+//    32*db + lane % 32 and whose k slots are tile rows r0 + 8*(lane/32) + e,
+//    e = 0..7 in order; two transposed reads of four rows each.
+// The chunk of step s is (4s + lane/16) ^ swz = 4s ^ (lane/16 ^ swz), and of
+// column block db (4db + y) ^ swz = 4db ^ (y ^ swz), so one base offset per
+// read kind and an XOR per read cover them; row r + 4 (r % 8 < 4) has
+// swz(r) ^ 1 and sits 4 P elements further, a bit the row term leaves clear.
+template <int D>
+struct TileReader16 {
+  using T = Tile<D>;
+  static constexpr int P = T::P;
+  static_assert(T::PC >= 16 && T::PC == T::CPR, "16-row reads need unpadded rows of >= 256 bytes");
+  int ra0, tr0;  // byte offsets
+  __device__ __forceinline__ explicit TileReader16(int lane) {
+    const int r = lane & 15;
+    ra0 = 2 * (r * P + (((lane >> 4) ^ T::swz(r)) << 3));
+    const int rl = 8 * (lane >> 5) + ((lane >> 2) & 3);
+    const int y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    tr0 = 2 * (rl * P + ((y ^ T::swz(rl)) << 3) + 4 * (lane & 1));
+  }
+  __device__ __forceinline__ void flip(int half) {
+    ra0 ^= 2 * half;
+    tr0 ^= 2 * half;
+  }
+  __device__ __forceinline__ bf16x8 a16(const bf16_t* tile, int r0, int s) const {
+    const char* p = reinterpret_cast<const char*>(tile + r0 * P) + (ra0 ^ (64 * s));
+    return lds_read16(reinterpret_cast<const bf16_t*>(p));
+  }
+  __device__ __forceinline__ bf16x8 trA(const bf16_t* tile, int r0, int db) const {
+    const char* p = reinterpret_cast<const char*>(tile + r0 * P);
+    const int o = tr0 ^ (64 * db);
+    return cat8(lds_read_tr4(reinterpret_cast<const bf16_t*>(p + o)),
+                lds_read_tr4(reinterpret_cast<const bf16_t*>(p + (o ^ (8 * P | 16)))));
   }
 };
 

@@ -122,6 +122,12 @@ def test_head_dim_256_backward(Lq, Lk, causal):
     run_case(1, 4, 2, Lq, Lk, 256, causal, seed=7750 + Lq)
 
 
+def test_head_dim_256_backward_many_heads():
+    # 4 x 32 key/value heads x 9 key tiles of 64 = 1152 workgroups: the
+    # 64-key dK/dV kernel (the cases above take the 32-key one)
+    run_case(4, 64, 32, 520, 520, 256, True, seed=7790)
+
+
 # ---------------------------------------------------------------- structure
 
 def test_bitwise_repeatable():
