@@ -141,22 +141,30 @@ def test_long23k_sampled_and_identities():
     check("dk", to_f64(dk[0, kvh, tail]), dk_tail, f"long23k kv head {kvh} last 512 keys")
     check("dv", to_f64(dv[0, kvh, tail]), dv_tail, f"long23k kv head {kvh} last 512 keys")
 
-    # identities over the whole tensors (every head): rows of dS sum to zero,
-    # rows of P sum to one.  bf16 outputs: compare against the size of the
-    # summed terms.
+    check_key_sums(w, dk, dv, g["do"])
+
+
+def check_key_sums(w, dk, dv, do):
+    """Identities over the whole tensors, every key of every head: rows of dS
+    sum to zero, so sum_j dK[j] = scale * sum_i q_i * sum_j dS_ij = 0; rows of
+    P sum to one, so sum_j dV[j] = sum over the group's rows of dO.  Causal
+    with Lq == Lk: every row sees at least one key.  bf16 outputs: compared
+    against the size of the summed terms."""
+    G = w.Hq // w.Hkv
     dkf = dk.float()
     ksum = dkf.sum(dim=2).abs().max().item()
     kscale = dkf.abs().sum(dim=2).max().item()
     assert ksum <= 1e-2 * kscale, (ksum, kscale)
     dvs = dv.float().sum(dim=2)
-    dos = g["do"].float().reshape(w.B, w.Hkv, G, w.Lq, w.D).sum(dim=(2, 3))
+    dos = do.float().reshape(w.B, w.Hkv, G, w.Lq, w.D).sum(dim=(2, 3))
     err = (dvs - dos).abs().max().item()
     assert err <= 1e-2 * dv.float().abs().sum(dim=2).max().item(), err
 
 
 def test_d256_fwd_bwd_sampled():
     """Head dim 256 forward + backward at 8192 tokens (16/2 heads, causal):
-    sampled rows of one group for O, LSE, dQ and the last 512 keys' dK/dV."""
+    sampled rows of one group for O, LSE, dQ and the last 512 keys' dK/dV,
+    and the key-sum identities over every head."""
     w, bits, g, out = run_workload("d256_train8k")
     G = w.Hq // w.Hkv
     kvh = 1
@@ -177,6 +185,9 @@ def test_d256_fwd_bwd_sampled():
         dv_tail += rt["dv"]
     check("dk", to_f64(out["dk"][0, kvh, tail]), dk_tail, f"d256_train8k kv head {kvh} last 512 keys")
     check("dv", to_f64(out["dv"][0, kvh, tail]), dv_tail, f"d256_train8k kv head {kvh} last 512 keys")
+    # the first key tiles (the longest dK/dV accumulations) through the
+    # whole-tensor identities
+    check_key_sums(w, out["dk"], out["dv"], g["do"])
 
 
 @pytest.mark.parametrize("L", [4096, 8192, 16384])
