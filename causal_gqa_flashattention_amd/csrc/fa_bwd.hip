@@ -785,6 +785,11 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_k32_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i) s[kb][i] = (i >= thr && i < rlim) ? s[kb][i] : 0.f;
       }
     }
+    // dP is read from its accumulators only after this point.  The products
+    // that write it may end right before the branch above, and on the path
+    // that skips the masking the compiler has left too few wait states before
+    // those reads (stale dP, seen on gfx950): 12 wait states here, on both paths.
+    asm volatile("s_nop 7\n\ts_nop 3" : "+a"(dp[0]), "+a"(dp[1]));
     const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][rq]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
