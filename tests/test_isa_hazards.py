@@ -1,15 +1,16 @@
 """Static check of the compiled kernels (CPU, no GPU needed): no read of a
-matrix-core accumulator right after a branch whose taken path leaves too few
+matrix-core result right after a branch whose taken path leaves too few
 wait states after the MFMA that wrote it.
 
-gfx950 does not interlock a VALU read (v_accvgpr_read) of an AGPR against an
-in-flight MFMA writing it: the compiler must separate them by wait states.
+gfx950 does not interlock a vector read (v_accvgpr_read of an AGPR, or any
+VALU, LDS or store operand in a VGPR) against an in-flight MFMA writing the
+register: the compiler must separate them by wait states.
 Within a basic block it does; across a branch it once left three, and the read
 returned the accumulator without the last products (wrong dK in one kernel,
 found by the GPU parity tests).  This test compiles every kernel source to
 gfx950 assembly with the library's own flags and measures, for every branch,
-the wait states between the last MFMA of the branching block that writes an
-AGPR and the first read of that AGPR at the branch target.
+the wait states between the last MFMA of the branching block that writes a
+register and the first read of that register at the branch target.
 """
 import os
 import re
@@ -31,12 +32,30 @@ SCAN = 16  # instructions / wait states scanned at a branch target
 SOURCES = ("fa_fwd.hip", "fa_bwd.hip", "fa_short.hip")
 
 
-def _agprs(tok):
-    m = re.match(r"a\[(\d+):(\d+)\]", tok)
+def _regs(tok):
+    """Registers named by one operand, as ('a' | 'v', index) pairs."""
+    m = re.match(r"([av])\[(\d+):(\d+)\]", tok)
     if m:
-        return set(range(int(m.group(1)), int(m.group(2)) + 1))
-    m = re.match(r"a(\d+)$", tok)
-    return {int(m.group(1))} if m else set()
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([av])(\d+)$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+def _operands(ins):
+    return [o.strip().split()[0] for o in ins.split(None, 1)[1].split(",")] if " " in ins else []
+
+
+_STORES = ("ds_write", "ds_store", "global_store", "buffer_store", "scratch_store", "flat_store")
+
+
+def _reads(ins):
+    """Registers a vector instruction reads (every operand of a store, every
+    operand but the first otherwise)."""
+    if ins.startswith("s_") or ins.startswith("v_mfma"):
+        return set()
+    ops = _operands(ins)
+    srcs = ops if ins.startswith(_STORES) else ops[1:]
+    return set().union(*[_regs(o) for o in srcs]) if srcs else set()
 
 
 def _states(ins):
@@ -54,19 +73,25 @@ def short_branch_reads(asm):
         lines = [l.split(";")[0].strip() for l in asm[fm.end():end].splitlines()]
         lines = [l for l in lines if l]
         labels = {l[:-1]: n for n, l in enumerate(lines) if re.match(r"^\.LBB\S+:$", l)}
+        # (instruction index the predecessor path ends at, target label): every
+        # branch, and the fall-through into a label from a block that does
+        # not end in an unconditional branch
+        edges = []
         for n, ins in enumerate(lines):
             m = re.match(r"^s_c?branch\S*\s+(\.LBB\S+)", ins)
-            if not m or m.group(1) not in labels:
-                continue
+            if m and m.group(1) in labels:
+                edges.append((n, m.group(1)))
+            if n and re.match(r"^\.LBB\S+:$", ins) and not lines[n - 1].startswith("s_branch"):
+                edges.append((n, ins[:-1]))
+        for n, label in edges:
             reads, waited = {}, 0
-            for k in range(labels[m.group(1)] + 1, len(lines)):
+            for k in range(labels[label] + 1, len(lines)):
                 tgt = lines[k]
                 if tgt.startswith(".LBB") or waited >= SCAN:
                     break
                 waited += _states(tgt)
-                if tgt.startswith("v_accvgpr_read"):
-                    for r in _agprs(tgt.split(None, 1)[1].split(",")[1].strip()):
-                        reads.setdefault(r, waited)
+                for r in _reads(tgt):
+                    reads.setdefault(r, waited)
             if not reads:
                 continue
             back = 0
@@ -76,10 +101,10 @@ def short_branch_reads(asm):
                     break
                 back += _states(src)
                 if src.startswith("v_mfma"):
-                    hit = [w for r, w in reads.items() if r in _agprs(src.split(None, 1)[1].split(",")[0].strip())]
+                    hit = [w for r, w in reads.items() if r in _regs(_operands(src)[0])]
                     if hit:
                         if back + min(hit) < _need(src):
-                            found.append((fm.group(1), m.group(1), back + min(hit)))
+                            found.append((fm.group(1), label, back + min(hit)))
                         break
                 if back > 64:
                     break
@@ -99,11 +124,16 @@ _BAD = """_Zkern:
 
 
 def test_checker_flags_a_short_path_and_accepts_padding():
-    assert short_branch_reads(_BAD) == [("_Zkern", ".LBB0_2", 3)]
+    # the branch path (3) and the fall-through path (5) are both short
+    assert short_branch_reads(_BAD) == [("_Zkern", ".LBB0_2", 3), ("_Zkern", ".LBB0_2", 5)]
     padded = _BAD.replace("  s_cbranch_scc1", "  s_nop 7\n  s_nop 3\n  s_cbranch_scc1")
     assert short_branch_reads(padded) == []
     other = _BAD.replace("v_accvgpr_read_b32 v20, a7", "v_accvgpr_read_b32 v20, a9")
     assert short_branch_reads(other) == []
+    # a result in VGPRs read by an ordinary VALU instruction
+    vgpr = _BAD.replace("a[4:7], v[0:3], v[4:7], a[4:7]", "v[24:27], v[0:3], v[4:7], v[24:27]").replace(
+        "v_accvgpr_read_b32 v20, a7", "v_add_f32_e32 v20, v26, v20")
+    assert short_branch_reads(vgpr) == [("_Zkern", ".LBB0_2", 3), ("_Zkern", ".LBB0_2", 5)]
 
 
 @pytest.mark.skipif(not os.path.exists(B._hipcc()), reason="hipcc not installed")
