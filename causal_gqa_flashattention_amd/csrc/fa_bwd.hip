@@ -80,11 +80,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.G;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = a.nqt * G;
-  const int bg = logical / per_group;
-  const int rr = logical - bg * per_group;
-  const int t = rr / G, hi = rr - (rr / G) * G;
+  const TileHead th = tile_major(blockIdx.x, a.B * a.Hq);  // query tiles x (batch, query head)
+  const int t = th.t, bg = th.h / G, hi = th.h - (th.h / G) * G;
   const int qt = CAUSAL ? (a.nqt - 1 - t) : t;
   const int b = bg / a.Hkv, hk = bg - (bg / a.Hkv) * a.Hkv;
   const int hq = hk * G + hi;
@@ -266,9 +263,9 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = w & 3, qhalf = w >> 2;
   const int G = a.G;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / a.nkt;
-  const int kt = logical - bh * a.nkt;  // key tile 0 sees the most queries: heaviest first
+  const TileHead th = tile_major(blockIdx.x, a.B * a.Hkv);  // key tiles x (batch, key/value head)
+  const int bh = th.h;
+  const int kt = th.t;  // key tile 0 sees the most queries: heaviest first
   const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
@@ -475,9 +472,9 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   const int kb = w & 1, qhalf = w >> 1;
   const int r0 = 32 * qhalf;  // this wavefront's rows within a tile
   const int G = a.G;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / a.nkt;
-  const int kt = logical - bh * a.nkt;  // key tile 0 sees the most queries: heaviest first
+  const TileHead th = tile_major(blockIdx.x, a.B * a.Hkv);  // key tiles x (batch, key/value head)
+  const int bh = th.h;
+  const int kt = th.t;  // key tile 0 sees the most queries: heaviest first
   const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
@@ -674,9 +671,9 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_k32_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = 16 * w;  // this wavefront's rows within a tile
   const int G = a.G;
-  const int nbh = a.B * a.Hkv;
-  const int kt = blockIdx.x / nbh;  // key tile 0 sees the most queries: heaviest first
-  const int bh = blockIdx.x - kt * nbh;
+  const TileHead th = tile_major(blockIdx.x, a.B * a.Hkv);  // key tiles x (batch, key/value head)
+  const int bh = th.h;
+  const int kt = th.t;  // key tile 0 sees the most queries: heaviest first
   const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 

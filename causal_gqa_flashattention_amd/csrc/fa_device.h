@@ -539,14 +539,21 @@ __device__ __forceinline__ void wait_vmem_n() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// Map a launch-order block id to a logical work id so that the blocks the
-// hardware places on one XCD (block id mod 8, round robin) get a contiguous
-// range of logical ids, which share key/value heads and so hit one L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  constexpr int kXcd = 8;
-  const int per = nblocks / kXcd, rem = nblocks % kXcd;
-  const int x = bid % kXcd, idx = bid / kXcd;
-  return x * per + min(x, rem) + idx;
+// Tile t and head h of workgroup `bid` in a grid of (tiles) x nh heads
+// numbered tile-major, so that tile 0 (the caller's heaviest) goes first.
+// Workgroups are dealt round-robin over the 8 XCDs: with nh a multiple of 8,
+// XCD bid % 8 = j % 8 (j = bid mod nh) for every tile, and it is given heads
+// (j % 8) nh / 8 .. + nh / 8 - 1, consecutive ones (those of one key/value
+// head share K and V in that XCD's L2); every XCD gets every tile, so a
+// causal triangle's heavy tiles spread over all of them.  Otherwise heads go
+// round-robin.
+struct TileHead {
+  int t, h;
+};
+__device__ __forceinline__ TileHead tile_major(int bid, int nh) {
+  const int t = bid / nh, j = bid - t * nh;
+  const int h = (nh & 7) == 0 ? (j & 7) * (nh >> 3) + (j >> 3) : j;
+  return {t, h};
 }
 
 }  // namespace cgqa

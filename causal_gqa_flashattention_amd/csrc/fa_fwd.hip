@@ -54,11 +54,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
 
   // ---- which (batch, head, query tile) this workgroup computes
   const int G = a.G;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = a.nqt * G;
-  const int bg = logical / per_group;
-  const int rr = logical - bg * per_group;
-  const int t = rr / G, hi = rr - (rr / G) * G;
+  const TileHead th = tile_major(blockIdx.x, a.B * a.Hq);  // query tiles x (batch, query head)
+  const int t = th.t, bg = th.h / G, hi = th.h - (th.h / G) * G;
   const int qt = CAUSAL ? (a.nqt - 1 - t) : t;  // heaviest tiles first
   const int b = bg / a.Hkv, hk = bg - (bg / a.Hkv) * a.Hkv;
   const int hq = hk * G + hi;
@@ -275,11 +272,8 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   const bool grp_b = w >= 4;
 
   const int G = a.G;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = a.nqt * G;
-  const int bg = logical / per_group;
-  const int rr = logical - bg * per_group;
-  const int t = rr / G, hi = rr - (rr / G) * G;
+  const TileHead th = tile_major(blockIdx.x, a.B * a.Hq);  // query tiles x (batch, query head)
+  const int t = th.t, bg = th.h / G, hi = th.h - (th.h / G) * G;
   const int qt = CAUSAL ? (a.nqt - 1 - t) : t;  // heaviest tiles first
   const int b = bg / a.Hkv, hk = bg - (bg / a.Hkv) * a.Hkv;
   const int hq = hk * G + hi;
