@@ -252,10 +252,10 @@ def executed_mfma(w):
     for qt in range(cdiv(Lq, 128)):
         dq += 4 * (4 * NKD + NDB * 4) * cdiv(kv_end(qt * 128 + 128), 64)
     # dK/dV, query tiles of 64: 8 waves x 128 keys up to D = 128; at D = 256
-    # 4 waves x 64 keys, or x 32 keys (16 rows each) below 1024 64-key workgroups
+    # 4 waves x 64 keys, or x 32 keys (16 rows each) below 512 64-key workgroups
     if D != 256:
         bnk, per_iter = 128, 8 * (2 * NKD + 4 * NDB)
-    elif B * Hkv * cdiv(Lk, 64) >= 1024:
+    elif B * Hkv * cdiv(Lk, 64) >= 512:
         bnk, per_iter = 64, 4 * (2 * NKD + 4 * NDB)
     else:
         bnk, per_iter = 32, 4 * (2 * (D // 32) + 2 * NDB)

@@ -916,9 +916,9 @@ template <class E, int D, int BN_Q>
 static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStream_t stream) {
   BwdArgs a = a0;
   // keys per dK/dV workgroup: 128 up to D = 128; at D = 256, 64, or 32 when
-  // 64-key workgroups would make fewer than four per CU (measured: 32-key
-  // workgroups are faster up to 512 64-key ones, slower from 1024)
-  const bool k32 = D > 128 && (int64_t)a.B * a.Hkv * ((a.Lk + 63) / 64) < 1024;
+  // 64-key workgroups would make fewer than two per CU (measured: 32-key
+  // workgroups are faster at 128-258 64-key ones, slower from 512)
+  const bool k32 = D > 128 && (int64_t)a.B * a.Hkv * ((a.Lk + 63) / 64) < 512;
   const int bnk = D > 128 ? (k32 ? 32 : 64) : 128;
   a.nkt = (a.Lk + bnk - 1) / bnk;
   const bool masked = a.mask != nullptr;
