@@ -279,9 +279,9 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   const int nqt = (Lq + BM - 1) / BM;
   const int nq = max(0, nqt - qt_first);
   // iteration n: query tile nqt - 1 - n / G of query head n % G.  Last tile
-  // first and heads innermost, so the workgroups of one key/value head (placed
-  // on one XCD) read the same Q/dO tile at about the same time and share it
-  // in L2, whatever their first tile.
+  // first and heads innermost, so the workgroups of one key/value head on one
+  // XCD read the same Q/dO tile at about the same time and share it in L2,
+  // whatever their first tile.
   // ---- under a block mask: the query tiles (last first) that some key of
   // this workgroup sees (dynamic LDS: up to nq entries, then the count)
   extern __shared__ int qlist[];
@@ -487,9 +487,9 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   const int nqt = (Lq + BM - 1) / BM;
   const int nq = max(0, nqt - qt_first);
   // iteration n: query tile nqt - 1 - n / G of query head n % G.  Last tile
-  // first and heads innermost, so the workgroups of one key/value head (placed
-  // on one XCD) read the same Q/dO tile at about the same time and share it
-  // in L2, whatever their first tile.
+  // first and heads innermost, so the workgroups of one key/value head on one
+  // XCD read the same Q/dO tile at about the same time and share it in L2,
+  // whatever their first tile.
   // ---- under a block mask: the query tiles (last first) that some key of
   // this workgroup sees (dynamic LDS: up to nq entries, then the count)
   extern __shared__ int qlist[];
