@@ -105,14 +105,25 @@ def short_bytes(w):
 
 # ------------------------------------------------------------ traffic record
 
-def source_digest():
+def _code_only(text):
+    """C/C++ source without comments and with whitespace runs collapsed: what
+    the compiler sees.  String literals in these sources hold no comment
+    markers."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def source_digest(root=ROOT):
+    """Digest of the kernel sources' code (comments and layout ignored)."""
     import glob
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "causal_gqa_flashattention_amd", "csrc", "*"))):
+    for p in sorted(glob.glob(os.path.join(root, "causal_gqa_flashattention_amd", "csrc", "*"))):
         if not os.path.isfile(p):
             continue
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8", errors="replace") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
