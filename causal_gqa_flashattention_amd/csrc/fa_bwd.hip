@@ -245,7 +245,11 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
 template <class E, int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   constexpr int BN = 128;   // keys per workgroup
-  constexpr int BM = 64;    // query rows per tile (two halves of 32)
+  // query rows per tile: 64 (two halves of 32), or 128 at head dim 64, where a
+  // 64-row tile is too little matrix work per barrier; each wave then takes
+  // two 32-row units per tile (under a block mask, one per 64-row mask block)
+  constexpr int BM = D == 64 ? 128 : 64;
+  static_assert(BM % kMaskBlock == 0, "query tiles are whole mask blocks");
   constexpr int P = Tile<D>::P;
   constexpr int NKD = D / 16;
   constexpr int NDB = D / 32;
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF + 2 * BN * P];
   bf16_t* const sK = smem + 2 * BUF;
   bf16_t* const sV = sK + BN * P;
-  __shared__ __attribute__((aligned(16))) float stat[2][2][64];  // [buf][lse / delta][row]
+  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buf][lse / delta][row]
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -291,7 +295,9 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     if (w == 0) {
       const int cnt = build_list(qlist, nq, lane, [&](int i) { return nqt - 1 - i; }, [&](int qtl) {
         bool any = false;
-        for (int kbk = kb0; kbk <= kb1; ++kbk) any |= a.mask[qtl * a.nkb + kbk] != 0;
+        const int rb_end = min((qtl + 1) * (BM / kMaskBlock), (Lq + kMaskBlock - 1) / kMaskBlock);
+        for (int rb = qtl * (BM / kMaskBlock); rb < rb_end; ++rb)
+          for (int kbk = kb0; kbk <= kb1; ++kbk) any |= a.mask[rb * a.nkb + kbk] != 0;
         return any;
       });
       if (lane == 0) qlist[nq] = cnt;
@@ -303,6 +309,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   auto qtile_of = [&](int n) { return MASKED ? __builtin_amdgcn_readfirstlane(qlist[n / G]) : nqt - 1 - n / G; };
   const int wkb = (k0 + 32 * kb) / kMaskBlock;  // mask column of this wavefront's keys
   const bool w_keys = k0 + 32 * kb < Lk;
+  const int nqb = (Lq + kMaskBlock - 1) / kMaskBlock;  // mask rows
 
   // the 8 waves load as two groups of four: waves 0-3 fill Q, waves 4-7 fill dO
   const int wl = w & 3;
@@ -321,8 +328,12 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
       ld.template load<BM>(qt_lds, qsrc + hi * a.q.sh, qbase, Lq, wl);
     else
       ld.template load<BM>(dt_lds, osrc + hi * a.dO.sh, qbase, Lq, wl);
-    if (w == 0) load_row_stat(&stat[n & 1][0][0], a.lse + qh, qbase, Lq, lane);
-    if (w == 4) load_row_stat(&stat[n & 1][1][0], a.delta + qh, qbase, Lq, lane);
+    // 64 rows per load; a half past Lq repeats row Lq - 1
+#pragma unroll
+    for (int hr = 0; hr < BM / 64; ++hr) {
+      if (w == 0) load_row_stat(&stat[n & 1][0][64 * hr], a.lse + qh, min(qbase + 64 * hr, Lq - 1), Lq, lane);
+      if (w == 4) load_row_stat(&stat[n & 1][1][64 * hr], a.delta + qh, min(qbase + 64 * hr, Lq - 1), Lq, lane);
+    }
   };
   // K and V of this key tile, once (rows past Lk repeat the last key)
   {
@@ -346,13 +357,20 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   for (int n = 0; n < niter; ++n) {
     const int buf = n & 1;
     const int q0 = qtile_of(n) * BM;
-    bool skip = false;  // this wavefront's keys do not see query tile q0 / BM
-    if constexpr (MASKED) skip = !w_keys || a.mask[(q0 / BM) * a.nkb + wkb] == 0;
     if (n + 1 < niter) issue(n + 1);
     const bf16_t* Qs = smem;            // + buf * BUF through rq's flipped offsets
     const bf16_t* Ds = smem + BM * P;
-    const int r0 = 32 * qhalf;  // this wave's rows within the tile
-    if (!skip) {
+    {
+#pragma unroll
+    for (int u = 0; u < BM / 64; ++u) {
+    const int r0 = 32 * qhalf + 64 * u;  // this wave's rows within the tile
+    // under a block mask, a unit whose 64-row block this wavefront's keys do
+    // not see is skipped (blocks past the mask's last row are computed, to
+    // zero contributions, as without a mask)
+    if constexpr (MASKED) {
+      const int rb = q0 / kMaskBlock + u;
+      if (!w_keys || (rb < nqb && a.mask[rb * a.nkb + wkb] == 0)) continue;
+    }
 
     f32x16 s = zero16(), dp = zero16();
     prio_hi();
@@ -397,6 +415,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
         dk[db] = E::mma(rq.trA(Qs, r0 + 16 * h, db), ds[h], dk[db]);
       }
     prio_lo();
+    }
     }
 
     rq.flip(BUF);
