@@ -661,9 +661,10 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
 // triangle at 8192 tokens and two heads is 256 workgroups, one per CU, and
 // the kernel lasts as long as the first key tile.  Here a workgroup of 4
 // wavefronts takes 32 keys, which doubles the workgroups; they are numbered
-// key tile major, so each XCD (workgroups round-robin over the eight) gets
-// one key/value head's tiles, every fourth one, heaviest first, and the
-// second round fills the CUs that light first-round workgroups free.
+// key tile major (tile_major), heaviest first, so every XCD gets a share of
+// each stretch of key tiles (at two key/value heads: one head, every fourth
+// tile), and the second round fills the CUs that light first-round
+// workgroups free.
 // Wavefront w owns rows 16 w .. 16 w + 15 of every 64-row query tile and all
 // 32 keys: S and dP are 16x16x32 products over two 16-key blocks, which
 // v_permlane16_swap turns into the k-major B operand of the 32x32x16 dV / dK
