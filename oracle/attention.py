@@ -118,33 +118,41 @@ def head_forward(qh, kh, vh, scale, causal, rows=None, block=256, block_mask=Non
 
 
 def head_forward_online(qh, kh, vh, scale, causal, block_n=32):
-    """Forward by the tiled online-softmax recurrence (all rows of one head).
+    """Forward from per-key-block softmax summaries (all rows of one head).
 
-    Follows section 3 of "When the Bottleneck Moved": per key block keep a
-    running row maximum m, denominator l and unnormalised accumulator acc;
-    m_new = max(m_old, rowmax(S_blk)), alpha = exp(m_old - m_new),
-    p = exp(S_blk - m_new), l = alpha*l + rowsum(p), acc = alpha*acc + p V_blk;
-    finally O = acc / l and L = m + log(l).  It is an independent route to
-    the same numbers as ``head_forward`` and pins the schedule the GPU uses.
+    Section 3 of "When the Bottleneck Moved" computes attention one key block
+    at a time, keeping per query row only a small summary of the keys seen so
+    far instead of the score matrix.  Here the summary of a set of keys is a
+    triple (m, l, a): m the row's largest score over the set, l the sum of
+    exp(s - m) and a the sum of exp(s - m) * v_j over it.  The set's softmax
+    output is then a / l and its log-sum-exp m + log l, whatever m is, as long
+    as every term uses the same m.  Each key block's own triple is formed
+    directly; two triples combine by moving both onto the larger of their
+    maxima (a factor exp(m_old - m_max) on each sum).  Folding the blocks in
+    order gives the result; it is an independent route to the numbers of
+    ``head_forward`` and pins the block-by-block schedule of the kernels.
     """
     Lq, Lk = qh.shape[0], kh.shape[0]
     D = vh.shape[1]
     vis = visible_mask(Lq, Lk, causal)
-    m = np.full(Lq, _NEG_INF)
+    m = np.full(Lq, _NEG_INF)     # the empty set: no maximum, zero sums
     l = np.zeros(Lq)
-    acc = np.zeros((Lq, D))
+    a = np.zeros((Lq, D))
     for j0 in range(0, Lk, block_n):
         j1 = min(Lk, j0 + block_n)
         s = np.where(vis[:, j0:j1], scale * (qh @ kh[j0:j1].T), _NEG_INF)
-        m_new = np.maximum(m, s.max(axis=1))
-        # rows that have seen nothing yet keep m = -inf; their alpha and p are 0
-        safe = np.where(np.isfinite(m_new), m_new, 0.0)
-        alpha = np.where(np.isfinite(m), np.exp(m - safe), 0.0)
-        p = np.exp(s - safe[:, None])
-        l = alpha * l + p.sum(axis=1)
-        acc = alpha[:, None] * acc + p @ vh[j0:j1]
-        m = m_new
-    return acc / l[:, None], m + np.log(l)
+        # this block's own summary (a row that sees none of its keys has the
+        # empty summary)
+        mb = s.max(axis=1)
+        eb = np.exp(s - np.where(np.isfinite(mb), mb, 0.0)[:, None])
+        lb, ab = eb.sum(axis=1), eb @ vh[j0:j1]
+        # combine the two summaries on the larger maximum
+        top = np.maximum(m, mb)
+        ref = np.where(np.isfinite(top), top, 0.0)
+        w_run = np.where(np.isfinite(m), np.exp(m - ref), 0.0)
+        w_blk = np.where(np.isfinite(mb), np.exp(mb - ref), 0.0)
+        m, l, a = top, w_run * l + w_blk * lb, w_run[:, None] * a + w_blk[:, None] * ab
+    return a / l[:, None], m + np.log(l)
 
 
 def head_backward(qh, kh, vh, doh, scale, causal, rows=None, key_rows=None, block=256, block_mask=None):
