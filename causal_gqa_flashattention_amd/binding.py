@@ -70,8 +70,8 @@ class FAError(RuntimeError):
 
 
 def lib_path() -> str:
-    """The in-tree library; CGQA_FA_LIBRARY may name another build of it."""
-    return os.environ.get("CGQA_FA_LIBRARY") or os.path.join(PKG_DIR, LIB_NAME)
+    """The in-tree library built by ``build.build_library()``."""
+    return os.path.join(PKG_DIR, LIB_NAME)
 
 
 def load_library() -> ctypes.CDLL:

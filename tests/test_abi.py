@@ -25,6 +25,19 @@ def lib():
     return fa.load_library()
 
 
+@pytest.fixture(scope="module")
+def vlib(lib):
+    """The library for validation tests that pass fake device pointers (P
+    below).  Every such call must fail on the host before any launch; in a
+    process that sees a GPU a regressed check would launch a kernel on an
+    unmapped address instead, so these tests run only where no device is
+    visible (the unmarked CPU suite)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("fake-pointer validation tests run only without a visible GPU")
+    return lib
+
+
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("fa_fwd", "fa_bwd_delta", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkv", "fa_status_str", "fa_version",
@@ -61,29 +74,29 @@ P = 4096  # a fake, 16-byte aligned pointer value: validation never dereferences
     ((P, P, P + 2, P, P, 1, 2, 1, 8, 8, 64, 0.1, 1), 2), # misaligned v
     ((P, P, P, P, P, 65536, 65536, 1, 65536, 65536, 256, 0.1, 0), 3),  # int64 overflow
 ])
-def test_fwd_validation(lib, args, status):
-    assert lib.fa_fwd(*args, None) == status
+def test_fwd_validation(vlib, args, status):
+    assert vlib.fa_fwd(*args, None) == status
 
 
-def test_empty_forward_is_ok_without_pointers(lib):
-    assert lib.fa_fwd(0, 0, 0, 0, 0, 0, 2, 1, 8, 8, 64, 0.1, 1, None) == 0
-    assert lib.fa_fwd(0, 0, 0, 0, 0, 1, 2, 1, 0, 8, 64, 0.1, 1, None) == 0
+def test_empty_forward_is_ok_without_pointers(vlib):
+    assert vlib.fa_fwd(0, 0, 0, 0, 0, 0, 2, 1, 8, 8, 64, 0.1, 1, None) == 0
+    assert vlib.fa_fwd(0, 0, 0, 0, 0, 1, 2, 1, 0, 8, 64, 0.1, 1, None) == 0
 
 
-def test_bwd_validation(lib):
+def test_bwd_validation(vlib):
     a = [P] * 10
-    assert lib.fa_bwd(*a, 1, 2, 1, 8, 8, 80, 0.1, 1, None) == 4    # unsupported head dim
-    assert lib.fa_bwd(*a, 1, 4, 3, 8, 8, 64, 0.1, 1, None) == 5
-    assert lib.fa_bwd(*a, 1, 2, 1, 9, 8, 64, 0.1, 1, None) == 6
+    assert vlib.fa_bwd(*a, 1, 2, 1, 8, 8, 80, 0.1, 1, None) == 4    # unsupported head dim
+    assert vlib.fa_bwd(*a, 1, 4, 3, 8, 8, 64, 0.1, 1, None) == 5
+    assert vlib.fa_bwd(*a, 1, 2, 1, 9, 8, 64, 0.1, 1, None) == 6
     bad = list(a)
     bad[7] = 0  # dq NULL
-    assert lib.fa_bwd(*bad, 1, 2, 1, 8, 8, 64, 0.1, 1, None) == 1
+    assert vlib.fa_bwd(*bad, 1, 2, 1, 8, 8, 64, 0.1, 1, None) == 1
     # the dK/dV half does not need dq
-    assert lib.fa_bwd_dq(P, P, P, P, P, P, 0, 1, 2, 1, 8, 8, 64, 0.1, 1, None) == 1
-    assert lib.fa_bwd_dkv(P, P, P, P, P, P, 0, P, 1, 2, 1, 8, 8, 64, 0.1, 1, None) == 1
-    assert lib.fa_bwd_delta(P, P, P, 1, 2, 8, 80, None) == 4
-    assert lib.fa_bwd_delta(P, 0, P, 1, 2, 8, 64, None) == 1
-    assert lib.fa_bwd_delta(0, 0, 0, 1, 2, 0, 64, None) == 0
+    assert vlib.fa_bwd_dq(P, P, P, P, P, P, 0, 1, 2, 1, 8, 8, 64, 0.1, 1, None) == 1
+    assert vlib.fa_bwd_dkv(P, P, P, P, P, P, 0, P, 1, 2, 1, 8, 8, 64, 0.1, 1, None) == 1
+    assert vlib.fa_bwd_delta(P, P, P, 1, 2, 8, 80, None) == 4
+    assert vlib.fa_bwd_delta(P, 0, P, 1, 2, 8, 64, None) == 1
+    assert vlib.fa_bwd_delta(0, 0, 0, 1, 2, 0, 64, None) == 0
 
 
 @pytest.mark.parametrize("args,status", [
@@ -93,31 +106,31 @@ def test_bwd_validation(lib):
     ((0, P, P, P, P, 1, 2, 1, 8, 8, 64, 0.1, 1), 1),
     ((P, P, P + 2, P, P, 1, 2, 1, 8, 8, 64, 0.1, 1), 2),
 ])
-def test_block_sparse_validation_matches_dense(lib, args, status):
+def test_block_sparse_validation_matches_dense(vlib, args, status):
     # the mask pointer (here a fake one, or NULL) changes none of the checks
     for m in (None, P + 1):
-        assert lib.fa_fwd_block_sparse(*args, m, None) == status
+        assert vlib.fa_fwd_block_sparse(*args, m, None) == status
     a = list(args[:3]) + [P] * 7
     if args[0] == 0:
         a[0] = 0
     if args[2] == P + 2:
         a[2] = P + 2
     tail = list(args[5:])
-    assert lib.fa_bwd_block_sparse(*a, *tail, P + 1, None) == status
-    assert lib.fa_bwd_dq_block_sparse(*a[:7], *tail, P + 1, None) == status
-    assert lib.fa_bwd_dkv_block_sparse(*a[:8], *tail, P + 1, None) == status
+    assert vlib.fa_bwd_block_sparse(*a, *tail, P + 1, None) == status
+    assert vlib.fa_bwd_dq_block_sparse(*a[:7], *tail, P + 1, None) == status
+    assert vlib.fa_bwd_dkv_block_sparse(*a[:8], *tail, P + 1, None) == status
 
 
-def test_block_sparse_empty_is_ok(lib):
-    assert lib.fa_fwd_block_sparse(0, 0, 0, 0, 0, 0, 2, 1, 8, 8, 64, 0.1, 1, 0, None) == 0
-    assert lib.fa_bwd_block_sparse(*([0] * 10), 0, 2, 1, 8, 8, 64, 0.1, 1, 0, None) == 0
+def test_block_sparse_empty_is_ok(vlib):
+    assert vlib.fa_fwd_block_sparse(0, 0, 0, 0, 0, 0, 2, 1, 8, 8, 64, 0.1, 1, 0, None) == 0
+    assert vlib.fa_bwd_block_sparse(*([0] * 10), 0, 2, 1, 8, 8, 64, 0.1, 1, 0, None) == 0
 
 
-def test_block_sparse_length_limit(lib):
+def test_block_sparse_length_limit(vlib):
     # tile lists live in LDS: Lq, Lk <= FA_MASK_MAX_LEN under a mask (plain calls are not limited)
     big = 262144 + 64
-    assert lib.fa_fwd_block_sparse(P, P, P, P, P, 1, 1, 1, big, big, 128, 0.1, 1, P, None) == 3
-    assert lib.fa_bwd_block_sparse(*([P] * 10), 1, 1, 1, 64, big, 128, 0.1, 1, P, None) == 3
+    assert vlib.fa_fwd_block_sparse(P, P, P, P, P, 1, 1, 1, big, big, 128, 0.1, 1, P, None) == 3
+    assert vlib.fa_bwd_block_sparse(*([P] * 10), 1, 1, 1, 64, big, 128, 0.1, 1, P, None) == 3
 
 
 # ---------------------------------------------------------------- general calls
@@ -145,42 +158,42 @@ def test_ex_symbols_and_status_strings(lib):
     ((2 * 128 * 64, 128 * 64, 64), (2 * 128 * 64, 64, 64), 9),          # heads and rows collide
     ((2 * 128 * 64, 128 * 64, 64), (128 * 64, 128 * 64, 64), 9),       # batches overlap heads
 ])
-def test_fwd_ex_stride_validation(lib, q_strides, o_strides, status):
+def test_fwd_ex_stride_validation(vlib, q_strides, o_strides, status):
     # B=2, Hq=2, Hkv=1, Lq=Lk=128, D=64
-    q = _t(lib, P, *q_strides)
-    kv = _dense(lib, 1, 128, 64)
-    o = _t(lib, P, *o_strides)
-    assert lib.fa_fwd_ex(q, kv, kv, o, P, 2, 2, 1, 128, 128, 64, 0.1, 1, 0, None, None) == status
+    q = _t(vlib, P, *q_strides)
+    kv = _dense(vlib, 1, 128, 64)
+    o = _t(vlib, P, *o_strides)
+    assert vlib.fa_fwd_ex(q, kv, kv, o, P, 2, 2, 1, 128, 128, 64, 0.1, 1, 0, None, None) == status
 
 
-def test_ex_dtype_and_empty(lib):
-    q = _dense(lib, 2, 128, 64)
-    kv = _dense(lib, 1, 128, 64)
-    assert lib.fa_fwd_ex(q, kv, kv, q, P, 1, 2, 1, 128, 128, 64, 0.1, 1, 2, None, None) == 10
-    assert lib.fa_bwd_delta_ex(q, q, P, 1, 2, 128, 64, 7, None) == 10
-    z = _t(lib, None, 0, 0, 0)
-    assert lib.fa_fwd_ex(z, z, z, z, None, 0, 2, 1, 128, 128, 64, 0.1, 1, 1, None, None) == 0
-    assert lib.fa_bwd_ex(z, z, z, None, None, z, z, z, z, 0, 2, 1, 8, 8, 64, 0.1, 1, 1, None, 3, None) == 0
+def test_ex_dtype_and_empty(vlib):
+    q = _dense(vlib, 2, 128, 64)
+    kv = _dense(vlib, 1, 128, 64)
+    assert vlib.fa_fwd_ex(q, kv, kv, q, P, 1, 2, 1, 128, 128, 64, 0.1, 1, 2, None, None) == 10
+    assert vlib.fa_bwd_delta_ex(q, q, P, 1, 2, 128, 64, 7, None) == 10
+    z = _t(vlib, None, 0, 0, 0)
+    assert vlib.fa_fwd_ex(z, z, z, z, None, 0, 2, 1, 128, 128, 64, 0.1, 1, 1, None, None) == 0
+    assert vlib.fa_bwd_ex(z, z, z, None, None, z, z, z, z, 0, 2, 1, 8, 8, 64, 0.1, 1, 1, None, 3, None) == 0
     # no gradient asked for: nothing to do
-    assert lib.fa_bwd_ex(z, z, z, None, None, z, z, z, z, 1, 2, 1, 8, 8, 64, 0.1, 1, 0, None, 0, None) == 0
+    assert vlib.fa_bwd_ex(z, z, z, None, None, z, z, z, z, 1, 2, 1, 8, 8, 64, 0.1, 1, 0, None, 0, None) == 0
 
 
-def test_bwd_ex_validation(lib):
-    q = _dense(lib, 2, 128, 64)
-    kv = _dense(lib, 1, 128, 64)
-    z = _t(lib, None, 0, 0, 0)
-    bad = _t(lib, P, 2 * 128 * 64, 128 * 64, 32)  # rows overlap
+def test_bwd_ex_validation(vlib):
+    q = _dense(vlib, 2, 128, 64)
+    kv = _dense(vlib, 1, 128, 64)
+    z = _t(vlib, None, 0, 0, 0)
+    bad = _t(vlib, P, 2 * 128 * 64, 128 * 64, 32)  # rows overlap
     # dq only: the dK/dV tensors may be NULL; an overlapping dq is refused
-    assert lib.fa_bwd_ex(q, kv, kv, P, P, q, bad, z, z, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 1, None) == 9
+    assert vlib.fa_bwd_ex(q, kv, kv, P, P, q, bad, z, z, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 1, None) == 9
     # dK/dV only: dq may be NULL, dk must be given
-    assert lib.fa_bwd_ex(q, kv, kv, P, P, q, z, z, kv, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 2, None) == 1
+    assert vlib.fa_bwd_ex(q, kv, kv, P, P, q, z, z, kv, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 2, None) == 1
     # an overlapping dv (stride 0 rows) is refused, a stride-0 input is not looked at as an output
-    zero_rows = _t(lib, P, 128 * 64, 128 * 64, 0)
-    assert lib.fa_bwd_ex(q, kv, kv, P, P, q, z, kv, zero_rows, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 2,
+    zero_rows = _t(vlib, P, 128 * 64, 128 * 64, 0)
+    assert vlib.fa_bwd_ex(q, kv, kv, P, P, q, z, kv, zero_rows, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 2,
                          None) == 9
     # misaligned data pointer in a strided view
-    mis = _t(lib, P + 8, 2 * 128 * 64, 128 * 64, 64)
-    assert lib.fa_bwd_ex(mis, kv, kv, P, P, q, q, kv, kv, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 3, None) == 2
+    mis = _t(vlib, P + 8, 2 * 128 * 64, 128 * 64, 64)
+    assert vlib.fa_bwd_ex(mis, kv, kv, P, P, q, q, kv, kv, 1, 2, 1, 128, 128, 64, 0.1, 1, 0, None, 3, None) == 2
 
 
 # ---------------------------------------------------------------- short queries
@@ -198,23 +211,23 @@ def test_short_workspace_bytes(lib):
     assert f(1, 32, 8, 1, 32768, 256) >= a
 
 
-def test_short_validation(lib):
-    q = _dense(lib, 4, 1, 64)
-    kv = _dense(lib, 1, 256, 64)
-    ws_bytes = lib.fa_short_workspace_bytes(1, 4, 1, 1, 256, 64)
-    assert lib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 9, 256, 64, 0.1, 1, 0, P, 1 << 30, None) == 3
-    assert lib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, None, 1 << 30, None) == 1
-    assert lib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, P + 4, 1 << 30, None) == 2
-    assert lib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, P, ws_bytes - 16, None) == 11
-    assert lib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 3, P, 1 << 30, None) == 10
-    z = _t(lib, None, 0, 0, 0)
-    assert lib.fa_fwd_short(z, z, z, z, None, 0, 4, 1, 1, 256, 64, 0.1, 1, 0, None, 0, None) == 0
+def test_short_validation(vlib):
+    q = _dense(vlib, 4, 1, 64)
+    kv = _dense(vlib, 1, 256, 64)
+    ws_bytes = vlib.fa_short_workspace_bytes(1, 4, 1, 1, 256, 64)
+    assert vlib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 9, 256, 64, 0.1, 1, 0, P, 1 << 30, None) == 3
+    assert vlib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, None, 1 << 30, None) == 1
+    assert vlib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, P + 4, 1 << 30, None) == 2
+    assert vlib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, P, ws_bytes - 16, None) == 11
+    assert vlib.fa_fwd_short(q, kv, kv, q, P, 1, 4, 1, 1, 256, 64, 0.1, 1, 3, P, 1 << 30, None) == 10
+    z = _t(vlib, None, 0, 0, 0)
+    assert vlib.fa_fwd_short(z, z, z, z, None, 0, 4, 1, 1, 256, 64, 0.1, 1, 0, None, 0, None) == 0
     # dq needs the workspace; dK/dV alone does not (the misaligned dk is what fails)
-    mis = _t(lib, P + 8, 256 * 64, 256 * 64, 64)
-    assert lib.fa_bwd_short(q, kv, kv, P, P, q, q, z, z, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 1, None, 0, None) == 1
-    assert lib.fa_bwd_short(q, kv, kv, P, P, q, q, z, z, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 1, P, 64, None) == 11
-    assert lib.fa_bwd_short(q, kv, kv, P, P, q, z, mis, kv, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 2, None, 0,
+    mis = _t(vlib, P + 8, 256 * 64, 256 * 64, 64)
+    assert vlib.fa_bwd_short(q, kv, kv, P, P, q, q, z, z, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 1, None, 0, None) == 1
+    assert vlib.fa_bwd_short(q, kv, kv, P, P, q, q, z, z, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 1, P, 64, None) == 11
+    assert vlib.fa_bwd_short(q, kv, kv, P, P, q, z, mis, kv, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 2, None, 0,
                             None) == 2
     # a failing dq check launches nothing, not even the dK/dV half
-    assert lib.fa_bwd_short(q, kv, kv, P, P, q, q, kv, kv, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 3, None, 0,
+    assert vlib.fa_bwd_short(q, kv, kv, P, P, q, q, kv, kv, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 3, None, 0,
                             None) == 1

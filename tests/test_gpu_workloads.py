@@ -11,7 +11,8 @@ checked against the fp64 oracle on what it can compute in seconds:
   4064x4096 and 8200^2: 512 sampled rows (first, last, tile edges, ragged
   tail, seeded rest) of all 8 query heads of one key/value head;
 * 23040-token long context (B=1, 32/8, D=128, causal): 256 sampled rows of
-  one group (O, LSE, dQ), dK/dV of its last 512 keys, the identities
+  one group (O, LSE, dQ), dK/dV of its first 256 keys (seen by every row:
+  the longest accumulations) and of its last 512 keys, the identities
   sum_j dK_j = 0 and sum_j dV_j = sum over the group of dO over the whole
   tensors, and peak device memory equal to the resident tensors (the
   library allocates nothing; a materialised fp32 score matrix would need
@@ -126,8 +127,9 @@ def test_long23k_sampled_and_identities():
     v = oracle.bf16_bits_to_f64(bits["v"][0, kvh])
     rows = sample_rows(w.Lq, 256, seed=w.seed, tile=128)
     tail = np.arange(w.Lq - 512, w.Lq)
-    dk_tail = np.zeros((512, w.D))
-    dv_tail = np.zeros((512, w.D))
+    head = np.arange(256)
+    dk_tail, dv_tail = np.zeros((512, w.D)), np.zeros((512, w.D))
+    dk_head, dv_head = np.zeros((256, w.D)), np.zeros((256, w.D))
     for h in range(kvh * G, (kvh + 1) * G):
         q = oracle.bf16_bits_to_f64(bits["q"][0, h])
         do = oracle.bf16_bits_to_f64(bits["do"][0, h])
@@ -138,8 +140,15 @@ def test_long23k_sampled_and_identities():
         rt = oracle.head_backward(q, k, v, do, w.softmax_scale, True, rows=tail, key_rows=tail)
         dk_tail += rt["dk"]
         dv_tail += rt["dv"]
+        # keys 0..255 are seen by every row: all 23040 rows of the head
+        rh = oracle.head_backward(q, k, v, do, w.softmax_scale, True, key_rows=head)
+        dk_head += rh["dk"]
+        dv_head += rh["dv"]
+        print(f"[oracle] long23k head {h} done", flush=True)
     check("dk", to_f64(dk[0, kvh, tail]), dk_tail, f"long23k kv head {kvh} last 512 keys")
     check("dv", to_f64(dv[0, kvh, tail]), dv_tail, f"long23k kv head {kvh} last 512 keys")
+    check("dk", to_f64(dk[0, kvh, head]), dk_head, f"long23k kv head {kvh} first 256 keys")
+    check("dv", to_f64(dv[0, kvh, head]), dv_head, f"long23k kv head {kvh} first 256 keys")
 
     check_key_sums(w, dk, dv, g["do"])
 
@@ -163,8 +172,9 @@ def check_key_sums(w, dk, dv, do):
 
 def test_d256_fwd_bwd_sampled():
     """Head dim 256 forward + backward at 8192 tokens (16/2 heads, causal):
-    sampled rows of one group for O, LSE, dQ and the last 512 keys' dK/dV,
-    and the key-sum identities over every head."""
+    sampled rows of one group for O, LSE, dQ; dK/dV of the group's first 256
+    keys (seen by every row) and last 512 keys; the key-sum identities over
+    every head."""
     w, bits, g, out = run_workload("d256_train8k")
     G = w.Hq // w.Hkv
     kvh = 1
@@ -172,8 +182,9 @@ def test_d256_fwd_bwd_sampled():
     v = oracle.bf16_bits_to_f64(bits["v"][0, kvh])
     rows = sample_rows(w.Lq, 128, seed=w.seed, tile=128)
     tail = np.arange(w.Lq - 512, w.Lq)
-    dk_tail = np.zeros((512, w.D))
-    dv_tail = np.zeros((512, w.D))
+    head = np.arange(256)
+    dk_tail, dv_tail = np.zeros((512, w.D)), np.zeros((512, w.D))
+    dk_head, dv_head = np.zeros((256, w.D)), np.zeros((256, w.D))
     for h in range(kvh * G, (kvh + 1) * G):
         q = oracle.bf16_bits_to_f64(bits["q"][0, h])
         do = oracle.bf16_bits_to_f64(bits["do"][0, h])
@@ -183,10 +194,14 @@ def test_d256_fwd_bwd_sampled():
         rt = oracle.head_backward(q, k, v, do, w.softmax_scale, True, rows=tail, key_rows=tail)
         dk_tail += rt["dk"]
         dv_tail += rt["dv"]
+        # the first 256 keys are seen by every row: the longest accumulations
+        rh = oracle.head_backward(q, k, v, do, w.softmax_scale, True, key_rows=head)
+        dk_head += rh["dk"]
+        dv_head += rh["dv"]
     check("dk", to_f64(out["dk"][0, kvh, tail]), dk_tail, f"d256_train8k kv head {kvh} last 512 keys")
     check("dv", to_f64(out["dv"][0, kvh, tail]), dv_tail, f"d256_train8k kv head {kvh} last 512 keys")
-    # the first key tiles (the longest dK/dV accumulations) through the
-    # whole-tensor identities
+    check("dk", to_f64(out["dk"][0, kvh, head]), dk_head, f"d256_train8k kv head {kvh} first 256 keys")
+    check("dv", to_f64(out["dv"][0, kvh, head]), dv_head, f"d256_train8k kv head {kvh} first 256 keys")
     check_key_sums(w, out["dk"], out["dv"], g["do"])
 
 
