@@ -17,6 +17,8 @@ import torch
 
 from .build import LIB_NAME, PKG_DIR
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # FA_NOALLOC_SCRATCH_BYTES
+
 FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_ALIGN", 3: "FA_ERR_SHAPE",
@@ -50,6 +52,7 @@ _SIGS = {
                  + [_c_float, _c_int, _c_int, _vp, ctypes.c_uint, _vp],
     "fa_short_workspace_bytes": [_c_int] * 6,
     "fa_fwd_short": [_T] * 4 + [_vp] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _vp, ctypes.c_size_t, _vp],
+    "fa_fwd_short_noalloc": [_T] * 4 + [_vp] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _vp],
     "fa_bwd_short": [_T] * 3 + [_vp, _vp] + [_T] * 4 + [_c_int] * 6
                     + [_c_float, _c_int, _c_int, ctypes.c_uint, _vp, ctypes.c_size_t, _vp],
     "fa_fwd_block_sparse": [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp, _vp],
@@ -473,6 +476,28 @@ def fa_fwd_short(q, k, v, o=None, lse=None, *, scale: float, causal: bool, works
                                      int(bool(causal)), _DTYPES[q.dtype], _ptr(ws), ws.numel(),
                                      _stream_ptr(stream))
     _check(st, "fa_fwd_short")
+    return o, lse
+
+
+def fa_fwd_short_noalloc(q, k, v, o, lse, *, scale: float, causal: bool, stream=None):
+    """fa_fwd_short with the library's static per-device scratch instead of a
+    workspace: o and lse must be given (nothing is allocated, here or in the
+    library).  Calls that may overlap on one GPU race on that scratch."""
+    qt = _view(q, "q")
+    kt, vt = _view(k, "k", q.dtype), _view(v, "v", q.dtype)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k/v shapes do not match q")
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have the shape of q")
+    ot = _view(o, "o", q.dtype)
+    _require(lse, "lse", torch.float32, 3)
+    if tuple(lse.shape) != (B, Hq, Lq):
+        raise ValueError("lse must be [B, Hq, Lq]")
+    st = load_library().fa_fwd_short_noalloc(qt, kt, vt, ot, _ptr(lse), B, Hq, Hkv, Lq, Lk, D, float(scale),
+                                             int(bool(causal)), _DTYPES[q.dtype], _stream_ptr(stream))
+    _check(st, "fa_fwd_short_noalloc")
     return o, lse
 
 

@@ -462,9 +462,12 @@ size_t fa_short_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D) {
   return pl.part_bytes + pl.ml_bytes;
 }
 
-fa_status fa_fwd_short(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
-                       int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
-                       fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+// The checks of fa_fwd_short, then its launch with the given workspace;
+// `workspace` NULL asks for the static per-device scratch array instead.
+static fa_status fwd_short_common(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
+                                  int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                                  fa_dtype dtype, void* workspace, size_t workspace_bytes, bool noalloc,
+                                  void* stream) {
   if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
   if (!fwd_head_dim_ok(D)) return FA_ERR_HEAD_DIM;
   FA_TRY(check_sizes(B, Hq, Hkv, Lq, Lk, D, causal != 0));
@@ -480,6 +483,11 @@ fa_status fa_fwd_short(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float
   FA_TRY(check_tensor(o, B, Hq, Lq, D, true));
   ShortPlan pl;
   if (!short_plan(B, Hq, Hkv, Lq, Lk, D, &pl)) return FA_ERR_SHAPE;
+  if (noalloc) {
+    if (pl.part_bytes + pl.ml_bytes > cgqa::kNoAllocScratchBytes) return FA_ERR_WORKSPACE;
+    if (cgqa::noalloc_scratch(&workspace) != hipSuccess) return FA_ERR_LAUNCH;
+    workspace_bytes = cgqa::kNoAllocScratchBytes;
+  }
   FA_TRY(check_workspace(pl, workspace, workspace_bytes));
   cgqa::SplitArgs a = split_args(pl, workspace, B, Hq, Hkv, Lq, Lk, scale);
   a.q = to_kernel(q);
@@ -489,6 +497,22 @@ fa_status fa_fwd_short(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float
   a.lse = lse;
   const hipError_t e = cgqa::launch_fwd_short(a, D, causal != 0, dtype == FA_F16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_fwd_short(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
+                       int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                       fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_short_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, dtype, workspace,
+                          workspace_bytes, false, stream);
+}
+
+static_assert(FA_NOALLOC_SCRATCH_BYTES == cgqa::kNoAllocScratchBytes, "static scratch size");
+
+fa_status fa_fwd_short_noalloc(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
+                               int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                               fa_dtype dtype, void* stream) {
+  return fwd_short_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, dtype, nullptr, 0, true,
+                          stream);
 }
 
 fa_status fa_bwd_short(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, const float* delta,

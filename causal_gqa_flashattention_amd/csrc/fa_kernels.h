@@ -83,4 +83,9 @@ hipError_t launch_dq_short(const SplitArgs& a, int D, bool causal, bool f16, hip
 // (a multiple of 128) per key/value head, no workspace
 hipError_t launch_dkv_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream);
 
+// The short forward's static scratch array on the current device (looked up
+// once per device, then kept): its device address and size in bytes.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace cgqa

@@ -20,10 +20,42 @@
 // The per-tile products are those of the long-query kernels (transposed
 // S^T = K Q^T with one packed row per lane pair, O^T += V^T P^T or
 // dQ^T += K^T dS^T), on the same swizzled double-buffered tiles.
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
+// Split partials of fa_fwd_short_noalloc: one array per GPU, for callers that
+// cannot allocate.  In host code `scratch` names a host-side stand-in, never
+// the device memory: kernels and copies take the address obtained below.
+static __device__ __align__(256) unsigned char scratch[cgqa::kNoAllocScratchBytes];
+
 namespace cgqa {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Each GPU holds its own copy of the array at its own address: look it up
+// once per device, with that device current, and keep it.
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 namespace {
 

@@ -261,6 +261,27 @@ fa_status fa_bwd_short(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, 
                        fa_dtype dtype, unsigned grads, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/*
+ * fa_fwd_short without a caller workspace, for callers that cannot allocate
+ * device memory or pass one: code recorded under HIP graph capture, tight
+ * serving and decode loops, harnesses that forbid allocation.  The split
+ * partials go to a static device array of FA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on, until the process ends; the call
+ * itself allocates nothing.  Arguments, results, checks and errors are those
+ * of fa_fwd_short, and FA_ERR_WORKSPACE when the shape needs more scratch
+ * than FA_NOALLOC_SCRATCH_BYTES (fa_short_workspace_bytes(...) tells).
+ * Every call on one GPU uses that GPU's one array and leaves its contents
+ * behind (nothing in it needs to start at zero): calls that may run at the
+ * same time on one GPU (other streams, other host threads) race and must
+ * be ordered by the caller.  FA_ERR_LAUNCH if the array's device address
+ * cannot be obtained.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+fa_status fa_fwd_short_noalloc(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
+                               int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                               fa_dtype dtype, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_str(fa_status s);
 

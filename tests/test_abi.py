@@ -231,3 +231,21 @@ def test_short_validation(vlib):
     # a failing dq check launches nothing, not even the dK/dV half
     assert vlib.fa_bwd_short(q, kv, kv, P, P, q, q, kv, kv, 1, 4, 1, 1, 256, 64, 0.1, 1, 0, 3, None, 0,
                             None) == 1
+
+
+def test_short_noalloc_validation(vlib):
+    q = _dense(vlib, 4, 1, 64)
+    kv = _dense(vlib, 1, 4096, 64)
+    f = vlib.fa_fwd_short_noalloc
+    # the checks of fa_fwd_short
+    assert f(q, kv, kv, q, P, 1, 4, 1, 1, 4096, 80, 0.1, 1, 0, None) == 4   # head dim
+    assert f(q, kv, kv, q, P, 1, 4, 1, 9, 4096, 64, 0.1, 1, 0, None) == 3   # Lq above the short limit
+    assert f(q, kv, kv, q, 0, 1, 4, 1, 1, 4096, 64, 0.1, 1, 0, None) == 1   # lse NULL
+    assert f(q, kv, kv, q, P, 1, 4, 1, 1, 4096, 64, 0.1, 1, 3, None) == 10  # element type
+    # a shape whose partials exceed the static scratch: refused before launch
+    big_q = _dense(vlib, 32, 8, 256)
+    big_kv = _dense(vlib, 8, 4096, 256)
+    ws = vlib.fa_short_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    assert ws(128, 32, 8, 8, 4096, 256) > (64 << 20)
+    assert f(big_q, big_kv, big_kv, big_q, P, 128, 32, 8, 8, 4096, 256, 0.1, 1, 0, None) == 11
