@@ -316,8 +316,13 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   const TileLoader<D> ld(wl, lane, w < 4 ? a.q.sl : a.dO.sl);
   const bf16_t* const qsrc = a.q.head(b, hk * G);
   const bf16_t* const osrc = a.dO.head(b, hk * G);
-  // every load of the loop is a direct global->LDS load: Q, dO and the rows'
-  // LSE (wave 0) and delta (wave 4), rows past Lq repeating the last row
+  // Q and dO are direct global->LDS loads, and so are the rows' delta
+  // (wave 4), rows past Lq repeating the last row.  The rows' LSE goes to
+  // LDS already multiplied by -log2 e, so that a score's probability is one
+  // fma and one exp2: wave 0 loads it into a register with the tile and
+  // writes it scaled before the barrier that ends the iteration
+  // (publish_lse), when the buffer's previous readers are done.
+  float lse_next[BM / 64];
   auto issue = [&](int n) {
     bf16_t* qt_lds = smem + (n & 1) * BUF;
     bf16_t* dt_lds = qt_lds + BM * P;
@@ -331,8 +336,14 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     // 64 rows per load; a half past Lq repeats row Lq - 1
 #pragma unroll
     for (int hr = 0; hr < BM / 64; ++hr) {
-      if (w == 0) load_row_stat(&stat[n & 1][0][64 * hr], a.lse + qh, min(qbase + 64 * hr, Lq - 1), Lq, lane);
+      if (w == 0) lse_next[hr] = a.lse[qh + min(qbase + 64 * hr + lane, Lq - 1)];
       if (w == 4) load_row_stat(&stat[n & 1][1][64 * hr], a.delta + qh, min(qbase + 64 * hr, Lq - 1), Lq, lane);
+    }
+  };
+  auto publish_lse = [&](int n) {
+    if (w == 0) {
+#pragma unroll
+      for (int hr = 0; hr < BM / 64; ++hr) stat[n & 1][0][64 * hr + lane] = lse_next[hr] * -kLog2e;
     }
   };
   // K and V of this key tile, once (rows past Lk repeat the last key)
@@ -340,7 +351,10 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     const TileLoader<D> lkv(wl, lane, w < 4 ? a.k.sl : a.v.sl);
     lkv.template load<BN>(w < 4 ? sK : sV, w < 4 ? a.k.head(b, hk) : a.v.head(b, hk), k0, Lk, wl);
   }
-  if (niter > 0) issue(0);
+  if (niter > 0) {
+    issue(0);
+    publish_lse(0);
+  }
 
   TileReaderX<D> rq(lane);  // Q and dO tiles: offsets flip with the buffer
   TileReaderX<D> rk(lane);  // K and V tiles (resident)
@@ -354,6 +368,27 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
 
   wait_vmem();
   __syncthreads();
+  // V with its sign bits flipped (bf16 and half alike): the dP products,
+  // started from delta, then give delta - dP, and P times that is -dS in one
+  // multiply; dK takes the sign back with the scale at the end
+  {
+    constexpr int NCH = BN * P * 2 / 16;  // 16-byte chunks of the V tile
+    uint4* vv = reinterpret_cast<uint4*>(sV);
+#pragma unroll
+    for (int i = tid; i < NCH; i += 512) {
+      uint4 x = vv[i];
+      x.x ^= 0x80008000u;
+      x.y ^= 0x80008000u;
+      x.z ^= 0x80008000u;
+      x.w ^= 0x80008000u;
+      vv[i] = x;
+    }
+  }
+  __syncthreads();
+  // this wavefront's K operand fragments stay in registers (loop-invariant)
+  bf16x8 kf[NKD];
+#pragma unroll
+  for (int kd = 0; kd < NKD; ++kd) kf[kd] = rk.row16(sK, 32 * kb, kd);
   for (int n = 0; n < niter; ++n) {
     const int buf = n & 1;
     const int q0 = qtile_of(n) * BM;
@@ -372,11 +407,19 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
       if (!w_keys || (rb < nqb && a.mask[rb * a.nkb + wkb] == 0)) continue;
     }
 
-    f32x16 s = zero16(), dp = zero16();
+    // dp starts from each row's delta (C layout: register 4 i4 + e holds
+    // row 8 i4 + 4 lg + e); with V negated it ends as delta - dP
+    f32x16 s = zero16(), dp;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][r0 + 8 * i4 + 4 * lg]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = d4[e];
+    }
     prio_hi();
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
-      s = E::mma(rq.row16(Qs, r0, kd), rk.row16(sK, 32 * kb, kd), s);
+      s = E::mma(rq.row16(Qs, r0, kd), kf[kd], s);
       dp = E::mma(rq.row16(Ds, r0, kd), rk.row16(sV, 32 * kb, kd), dp);
     }
     // (no read-ahead pattern here: with eight wavefronts in step it only
@@ -384,9 +427,9 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     prio_lo();
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][r0 + 8 * i4 + 4 * lg]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][r0 + 8 * i4 + 4 * lg]);  // -LSE log2 e
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fast_exp2(fmaf(s[4 * i4 + e], c2, l4[e] * -kLog2e));
+      for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fast_exp2(fmaf(s[4 * i4 + e], c2, l4[e]));
     }
     // tiles that cross the diagonal or hold rows past Lq
     if ((CAUSAL && k0 + BN - 1 > q0 + off) || q0 + BM > Lq) {
@@ -398,12 +441,9 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = (crow(i, 0) >= thr && crow(i, 0) < rlim) ? s[i] : 0.f;
     }
+    // -dS = P (delta - dP)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][r0 + 8 * i4 + 4 * lg]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = s[4 * i4 + e] * (dp[4 * i4 + e] - d4[e]);
-    }
+    for (int i = 0; i < 16; ++i) dp[i] = s[i] * dp[i];
     const bf16x8 pf[2] = {E::pack8(s, 0), E::pack8(s, 1)};
     const bf16x8 ds[2] = {E::pack8(dp, 0), E::pack8(dp, 1)};
     prio_hi();
@@ -419,6 +459,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     }
 
     rq.flip(BUF);
+    if (n + 1 < niter) publish_lse(n + 1);
     wait_vmem();
     __syncthreads();
   }
@@ -449,7 +490,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   if (w < 4 && key_ok) {
     bf16_t* dkp = a.dk.head(b, hk) + (int64_t)krow * a.dk.sl;
     bf16_t* dvp = a.dv.head(b, hk) + (int64_t)krow * a.dv.sl;
-    const float sc = a.scale;
+    const float sc = -a.scale;  // the accumulators hold -dK / scale
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
