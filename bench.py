@@ -398,6 +398,86 @@ def gemm_canary(dev, n=4096, reps=10):
     return {"shape": f"{n}x{n}x{n} bf16", "ms": round(ms, 4), "TFLOP/s": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
 
 
+# The other configurations of the path, timed after the headline one: every
+# workload of the five configurations that is not the headline shape.
+SWEEP = ("dense4k_d64", "dense4k_d96", "d256_8192", "d256_4064x4096", "d256_8200", "long23k")
+
+
+def workload_sweep(dev, names=SWEEP, steps=10, warmup=3):
+    """For each workload: fa_fwd, fa_bwd_delta, fa_bwd_dq and fa_bwd_dkv on
+    resident inputs (the same seeded recipe as the headline), timed with HIP
+    events on the launch stream; medians over `steps` steps.  Model TFLOP/s
+    use the pages' FLOP model (the head-dim-256 shapes are a forward
+    workload: their forward figure is the one to read; the backward there is
+    timed as well)."""
+    import numpy as np
+    import torch
+
+    import causal_gqa_flashattention_amd as fa
+    from fa_synth import WORKLOADS, make_inputs
+
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name in names:
+        w = WORKLOADS[name]
+        bits = make_inputs(w, with_grad=True)
+        g = {n: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for n, b in bits.items()}
+        del bits
+        q, k, v, do = g["q"], g["k"], g["v"], g["do"]
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=dev)
+        delta = torch.empty_like(lse)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        sc, causal = w.softmax_scale, w.causal
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        resident = torch.cuda.memory_allocated()
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            fa.fa_fwd(q, k, v, o, lse, scale=sc, causal=causal, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            fa.fa_bwd_delta(o, do, delta, stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
+            fa.fa_bwd_dq(q, k, v, lse, delta, do, dq, scale=sc, causal=causal, stream=stream)
+            if ev is not None:
+                ev[3].record(stream)
+            fa.fa_bwd_dkv(q, k, v, lse, delta, do, dk, dv, scale=sc, causal=causal, stream=stream)
+            if ev is not None:
+                ev[4].record(stream)
+
+        for _ in range(warmup):
+            step()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        for e in evs:
+            step(e)
+        torch.cuda.synchronize()
+        med = {n: float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs]))
+               for j, n in enumerate(("fwd", "delta", "dq", "dkv"))}
+        step_ms = float(np.median([e[0].elapsed_time(e[4]) for e in evs]))
+        total, fwd_f = model_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal)
+        bwd_f = total - fwd_f
+        kind = "causal" if w.causal else "dense"
+        out[name] = {
+            "shape": f"{kind} GQA bf16, B={w.B} Hq={w.Hq} Hkv={w.Hkv} Lq={w.Lq} Lk={w.Lk} D={w.D}",
+            "kernels_median_ms": {n: round(t, 4) for n, t in med.items()},
+            "step_median_ms": round(step_ms, 4),
+            "fwd_TFLOP/s": round(fwd_f / (med["fwd"] * 1e-3) / 1e12, 1),
+            "bwd_TFLOP/s": round(bwd_f / ((med["delta"] + med["dq"] + med["dkv"]) * 1e-3) / 1e12, 1),
+            "fwd+bwd_TFLOP/s": round(total / (step_ms * 1e-3) / 1e12, 1),
+            "frac_of_peak": round(total / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "fwd_frac_of_peak": round(fwd_f / (med["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "peak_bytes": int(torch.cuda.max_memory_allocated()),
+            "resident_bytes": int(resident),
+        }
+        del g, q, k, v, do, o, lse, delta, dq, dk, dv
+        torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,6 +485,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="train8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip timing the other configurations (the 'workloads' key)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="copy kernels of known size plus one step, for counter runs")
     ap.add_argument("--summarize-inst", metavar="CSV",
@@ -565,6 +647,7 @@ def main(argv=None):
 
     names = ["fwd", "delta", "dq", "dkv"]
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    per_med = {n: float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
     step_ev = np.array([e[0].elapsed_time(e[4]) for e in evs])  # first launch to last, per step
     ms_step = wall * 1e3 / args.steps
     if mask_np is None:
@@ -579,9 +662,9 @@ def main(argv=None):
     kernels = {}
     for n in names:
         if n == "delta":
-            kernels[n] = {"ms": per[n], "GB/s": work[n] / (per[n] * 1e-3) / 1e9}
+            kernels[n] = {"ms": per[n], "median_ms": per_med[n], "GB/s": work[n] / (per[n] * 1e-3) / 1e9}
         else:
-            kernels[n] = {"ms": per[n], "TFLOP/s": work[n] / (per[n] * 1e-3) / 1e12}
+            kernels[n] = {"ms": per[n], "median_ms": per_med[n], "TFLOP/s": work[n] / (per[n] * 1e-3) / 1e12}
     dom = max(("fwd", "dq", "dkv"), key=lambda n: per[n])
     achieved = work[dom] / (per[dom] * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
@@ -650,6 +733,10 @@ def main(argv=None):
         out["mfma_ceiling"] = ceil
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, bits, mask=mask_np, pairs=pairs)
+    if w.name == "train8k" and not args.no_workloads:
+        del q, k, v, do, o, lse, delta, dq, dk, dv, g
+        torch.cuda.empty_cache()
+        out["workloads"] = workload_sweep(dev)
     print(json.dumps(out), flush=True)
     return 0
 
