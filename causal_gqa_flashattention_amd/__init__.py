@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     fa_bwd,
     fa_bwd_delta_ex,
     fa_bwd_ex,
+    fa_bwd_workspace_bytes,
     fa_bwd_short,
     fa_fwd_short,
     fa_fwd_short_noalloc,
@@ -37,6 +38,6 @@ from .binding import (  # noqa: F401
 __all__ = [
     "FAError", "MASK_BLOCK", "fa_fwd", "fa_bwd_delta", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkv",
     "fa_fwd_block_sparse", "fa_bwd_block_sparse", "fa_bwd_dq_block_sparse",
-    "fa_bwd_dkv_block_sparse", "fa_fwd_ex", "fa_bwd_delta_ex", "fa_bwd_ex", "FaTensor", "FA_BF16",
+    "fa_bwd_dkv_block_sparse", "fa_fwd_ex", "fa_bwd_delta_ex", "fa_bwd_ex", "fa_bwd_workspace_bytes", "FaTensor", "FA_BF16",
     "FA_F16", "fa_fwd_short", "fa_fwd_short_noalloc", "NOALLOC_SCRATCH_BYTES", "fa_bwd_short", "fa_short_workspace_bytes", "SHORT_MAX_LQ", "lib_path", "load_library", "status_str", "version",
 ]

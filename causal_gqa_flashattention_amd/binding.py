@@ -51,6 +51,9 @@ _SIGS = {
     "fa_bwd_ex": [_T] * 3 + [_vp, _vp] + [_T] * 4 + [_c_int] * 6
                  + [_c_float, _c_int, _c_int, _vp, ctypes.c_uint, _vp],
     "fa_short_workspace_bytes": [_c_int] * 6,
+    "fa_bwd_workspace_bytes": [_c_int] * 7,
+    "fa_bwd_ws": [_T] * 3 + [_vp, _vp] + [_T] * 4 + [_c_int] * 6
+                 + [_c_float, _c_int, _c_int, _vp, ctypes.c_uint, _vp, ctypes.c_size_t, _vp],
     "fa_fwd_short": [_T] * 4 + [_vp] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _vp, ctypes.c_size_t, _vp],
     "fa_fwd_short_noalloc": [_T] * 4 + [_vp] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _vp],
     "fa_bwd_short": [_T] * 3 + [_vp, _vp] + [_T] * 4 + [_c_int] * 6
@@ -89,7 +92,7 @@ def load_library() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = argtypes
             fn.restype = (ctypes.c_char_p if name in ("fa_status_str", "fa_version")
-                          else ctypes.c_size_t if name == "fa_short_workspace_bytes" else ctypes.c_int)
+                          else ctypes.c_size_t if name.endswith("_workspace_bytes") else ctypes.c_int)
         _lib = lib
     return _lib
 
@@ -392,9 +395,12 @@ def fa_bwd_delta_ex(o, do, delta=None, *, stream=None):
 
 
 def fa_bwd_ex(q, k, v, lse, delta, do, dq=None, dk=None, dv=None, *, scale: float, causal: bool,
-              block_mask=None, grads: str = "all", stream=None):
+              block_mask=None, grads: str = "all", stream=None, workspace=False):
     """fa_bwd for bf16 or fp16 strided views.  grads: "all", "dq" or "dkv";
-    returns (dq, dk, dv) with None for what was not asked for."""
+    returns (dq, dk, dv) with None for what was not asked for.  `workspace`:
+    False for fa_bwd_ex; a GPU byte tensor (at least fa_bwd_workspace_bytes)
+    or True (allocated here through torch) for fa_bwd_ws, whose dK/dV kernel
+    splits long query lists over several workgroups."""
     want = {"all": FA_GRAD_DQ | FA_GRAD_DKV, "dq": FA_GRAD_DQ, "dkv": FA_GRAD_DKV}[grads]
     qt = _view(q, "q")
     kt, vt, dot = _view(k, "k", q.dtype), _view(v, "v", q.dtype), _view(do, "do", q.dtype)
@@ -424,13 +430,27 @@ def fa_bwd_ex(q, k, v, lse, delta, do, dq=None, dk=None, dv=None, *, scale: floa
     if block_mask is not None:
         _require_mask(block_mask, Lq, Lk)
         mask = _ptr(block_mask)
-    st = load_library().fa_bwd_ex(qt, kt, vt, _ptr(lse), _ptr(delta), dot, dqt, dkt, dvt,
-                                  B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)),
-                                  _DTYPES[q.dtype], mask, want, _stream_ptr(stream))
-    _check(st, "fa_bwd_ex")
+    if workspace is False:
+        st = load_library().fa_bwd_ex(qt, kt, vt, _ptr(lse), _ptr(delta), dot, dqt, dkt, dvt,
+                                      B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)),
+                                      _DTYPES[q.dtype], mask, want, _stream_ptr(stream))
+        _check(st, "fa_bwd_ex")
+    else:
+        nbytes = fa_bwd_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, block_mask is not None)
+        ws = _workspace(None if workspace is True else workspace, nbytes, q.device) if nbytes else None
+        st = load_library().fa_bwd_ws(qt, kt, vt, _ptr(lse), _ptr(delta), dot, dqt, dkt, dvt,
+                                      B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)),
+                                      _DTYPES[q.dtype], mask, want, _ptr(ws), 0 if ws is None else ws.numel(),
+                                      _stream_ptr(stream))
+        _check(st, "fa_bwd_ws")
     return (dq if want & FA_GRAD_DQ else None,
             dk if want & FA_GRAD_DKV else None,
             dv if want & FA_GRAD_DKV else None)
+
+
+def fa_bwd_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, masked=False) -> int:
+    """Workspace bytes of fa_bwd_ws for this shape (0: no split planned)."""
+    return int(load_library().fa_bwd_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, int(bool(masked))))
 
 
 # ---------------------------------------------------------------- short queries

@@ -210,12 +210,52 @@ fa_status delta_common(const fa_tensor& o, const fa_tensor& dO, float* delta, in
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Query-range split of the dK/dV kernel (calls with a workspace).  A key
+// tile's work is its query-tile list times the group size.  Under a causal
+// mask the first key tile sees every query tile, the last almost none: with
+// at least two workgroups per CU the hardware's heaviest-first rounds pair
+// them up, with fewer the kernel lasts as long as the first tile.  A block
+// mask can hand one key tile every query tile (a global or sink column).
+// So: with a mask, lists longer than a quarter of the query tiles are split
+// four ways; without one, when there are fewer than 512 key-tile workgroups
+// (two per CU), every list is split until about 1024 workgroups (at most 8
+// chunks).  Lists that fit one chunk are written directly.
+struct DkvSplit {
+  int nsplit, cs;
+  size_t part_bytes, bytes;
+};
+
+DkvSplit dkv_split_plan(int B, int Hkv, int Lq, int Lk, int D, bool masked) {
+  DkvSplit p{1, 0, 0, 0};
+  if (B <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || !bwd_head_dim_ok(D)) return p;
+  const int bnk = cgqa::dkv_split_keys(D);
+  const int64_t nkt = ((int64_t)Lk + bnk - 1) / bnk;
+  const int64_t wgs = (int64_t)B * Hkv * nkt;
+  const int64_t nqt = ((int64_t)Lq + 63) / 64;
+  int64_t S = 1;
+  if (masked) {
+    S = 4;
+  } else if (wgs < 512) {
+    S = 2;
+    while (S < 8 && wgs * S < 1024) S *= 2;
+  }
+  S = std::min<int64_t>(S, nqt);
+  if (S <= 1 || wgs * S > INT32_MAX) return p;
+  p.nsplit = (int)S;
+  p.cs = (int)((nqt + S - 1) / S);
+  p.part_bytes = (size_t)(wgs * S) * 2 * bnk * D * sizeof(float);
+  p.bytes = p.part_bytes + (((size_t)wgs * sizeof(int) + 255) & ~(size_t)255);
+  return p;
+}
+
 // Shared body of every backward call.  which: FA_GRAD_DQ and/or FA_GRAD_DKV.
+// A workspace (may be NULL) lets the dK/dV kernel split long query lists.
 fa_status bwd_common(const fa_tensor& q, const fa_tensor& k, const fa_tensor& v, const float* lse,
                      const float* delta, const fa_tensor& dO, const fa_tensor& dq, const fa_tensor& dk,
                      const fa_tensor& dv, int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale,
                      int causal, fa_dtype dtype, const unsigned char* block_mask, unsigned which,
-                     void* stream) {
+                     void* stream, bool ws_call = false, void* workspace = nullptr,
+                     size_t workspace_bytes = 0) {
   if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
   if (!bwd_head_dim_ok(D)) return FA_ERR_HEAD_DIM;
   FA_TRY(check_sizes(B, Hq, Hkv, Lq, Lk, D, causal != 0));
@@ -249,7 +289,16 @@ fa_status bwd_common(const fa_tensor& q, const fa_tensor& k, const fa_tensor& v,
     FA_TRY(check_tensor(dv, B, Hkv, Lk, D, true));
   }
 
-  cgqa::BwdArgs a;
+  DkvSplit split{1, 0, 0, 0};
+  if (ws_call && (which & FA_GRAD_DKV)) {
+    split = dkv_split_plan(B, Hkv, Lq, Lk, D, block_mask != nullptr);
+    if (split.nsplit > 1) {
+      FA_TRY(check_ptr(workspace));
+      if (workspace_bytes < split.bytes) return FA_ERR_WORKSPACE;
+    }
+  }
+
+  cgqa::BwdArgs a{};
   a.q = to_kernel(q);
   a.k = to_kernel(k);
   a.v = to_kernel(v);
@@ -267,6 +316,13 @@ fa_status bwd_common(const fa_tensor& q, const fa_tensor& k, const fa_tensor& v,
   a.scale_log2 = scale * 1.4426950408889634f;
   a.mask = reinterpret_cast<const uint8_t*>(block_mask);
   a.nkb = (Lk + cgqa::kMaskBlock - 1) / cgqa::kMaskBlock;
+  a.nsplit = 1;
+  if (split.nsplit > 1) {
+    a.part = static_cast<float*>(workspace);
+    a.split_cnt = reinterpret_cast<int*>(static_cast<char*>(workspace) + split.part_bytes);
+    a.nsplit = split.nsplit;
+    a.cs = split.cs;
+  }
   const hipError_t e = cgqa::launch_bwd(a, D, causal != 0, (int)which, dtype == FA_F16,
                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -385,6 +441,20 @@ fa_status fa_bwd_ex(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, con
                     fa_dtype dtype, const unsigned char* block_mask, unsigned grads, void* stream) {
   return bwd_common(q, k, v, lse, delta, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal, dtype,
                     block_mask, grads, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D, int masked) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
+  return dkv_split_plan(B, Hkv, Lq, Lk, D, masked != 0).bytes;
+}
+
+fa_status fa_bwd_ws(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, const float* delta,
+                    fa_tensor dO, fa_tensor dq, fa_tensor dk, fa_tensor dv,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                    fa_dtype dtype, const unsigned char* block_mask, unsigned grads,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(q, k, v, lse, delta, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal, dtype,
+                    block_mask, grads, stream, true, workspace, workspace_bytes);
 }
 
 }  // extern "C"

@@ -228,6 +228,96 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
   }
 }
 
+// ---------------------------------------------------------------- dK / dV split
+// Query-range split (nsplit > 1, with a workspace): the workgroups of one key
+// tile are chunks 0 .. nsplit - 1 of its query-tile list (`len` entries).
+// The tile is shared by nc chunks, chunk c taking entries c, c + nc,
+// c + 2 nc, ... and writing fp32 partials; chunk 0 records nc for the
+// reduction kernel.  Strided, not consecutive, entries: the workgroups of one
+// chunk index then walk the query tiles in the same order, last first, and
+// those running at the same time share the tiles they load in L2 (with runs
+// of consecutive entries they read different tiles and the head-dim-256
+// kernel became bound by HBM).
+//  * Without a block mask (UNIFORM) every list is split nsplit ways
+//    (nc = min(nsplit, len)) and chunk c runs in slot c: workgroups are dealt
+//    round-robin to the XCDs by index, so one XCD runs one chunk index of
+//    many tiles in step.
+//  * Under a mask most lists may be short: a list that fits one chunk of
+//    `cs` entries is computed whole by chunk 0 and written directly (no
+//    partials), a longer one is shared by nc = ceil(len / cs) chunks.  Only
+//    chunk 0 always has work, so it is rotated to slot kt mod nsplit (see
+//    split_chunk).
+// Returns false for a workgroup with nothing to do (the caller exits before
+// its first barrier or after one every wavefront passes).
+struct SplitRange {
+  int lo, step, cnt;  // list entries lo, lo + step, ... (cnt of them)
+  bool partial;
+};
+template <bool UNIFORM>
+__device__ __forceinline__ bool split_range(const BwdArgs& a, int bh, int kt, int chunk, int len, int tid,
+                                            SplitRange& r) {
+  r = {0, 1, len, false};
+  if (a.nsplit <= 1) return true;
+  const int nc = UNIFORM ? min(a.nsplit, len) : (len + a.cs - 1) / a.cs;
+  if (chunk == 0 && tid == 0) a.split_cnt[bh * a.nkt + kt] = nc;
+  if (nc <= 1) return chunk == 0;
+  if (chunk >= nc) return false;
+  r = {chunk, nc, (len - chunk + nc - 1) / nc, true};
+  return true;
+}
+
+// Chunk of key tile kt that runs in slot `slot` of the tile's nsplit
+// consecutive workgroups.  Workgroups are dealt round-robin to the XCDs and,
+// within one, to its shader engines, so the slot decides where a chunk runs.
+// Under a mask chunk 0, the only one that always has work, is rotated to slot
+// kt mod nsplit so that busy workgroups spread over the whole chip (with the
+// chunk in the slot, every busy workgroup of a masked call whose lists are
+// short landed on one engine in four: measured three times slower).
+template <bool UNIFORM>
+__device__ __forceinline__ int split_chunk(int slot, int kt, int nsplit) {
+  return UNIFORM ? slot : (slot + nsplit - kt % nsplit) % nsplit;
+}
+
+// fp32 partials of chunk `chunk` of key tile kt: [2][BN][D] (dK accumulators,
+// then dV), key rows of the tile in order.
+template <int BN, int D>
+__device__ __forceinline__ float* split_part(const BwdArgs& a, int bh, int kt, int chunk) {
+  return a.part + ((int64_t)(bh * a.nkt + kt) * a.nsplit + chunk) * (2 * BN * D);
+}
+
+// Sum of the partials of every split key tile: one workgroup per (batch,
+// key/value head, key tile); tiles written directly are skipped.  dK takes
+// the factor ksc (the sign and scale the dK/dV kernel left out), dV none.
+template <class E, int D, int BN>
+__global__ __launch_bounds__(256) void fa_dkv_reduce_kernel(BwdArgs a) {
+  const int bh = blockIdx.x / a.nkt, kt = blockIdx.x - bh * a.nkt;
+  const int nc = a.split_cnt[bh * a.nkt + kt];
+  if (nc <= 1) return;
+  const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
+  const int k0 = kt * BN;
+  const float* base = split_part<BN, D>(a, bh, kt, 0);
+  constexpr int NV = BN * D / 4;  // float4 per array
+#pragma unroll 1
+  for (int which = 0; which < 2; ++which) {
+    const float f = which == 0 ? a.ksc : 1.f;
+    const Tensor& t = which == 0 ? a.dk : a.dv;
+    for (int e = threadIdx.x; e < NV; e += 256) {
+      const int key = (4 * e) / D, d = 4 * e - key * D;
+      if (k0 + key >= a.Lk) continue;
+      float4 acc = *reinterpret_cast<const float4*>(base + which * BN * D + 4 * e);
+      for (int c = 1; c < nc; ++c) {
+        const float4 x = *reinterpret_cast<const float4*>(base + (int64_t)c * 2 * BN * D + which * BN * D + 4 * e);
+        acc.x += x.x;
+        acc.y += x.y;
+        acc.z += x.z;
+        acc.w += x.w;
+      }
+      *reinterpret_cast<uint2*>(t.head(b, hk) + (int64_t)(k0 + key) * t.sl + d) =
+          E::pack4(acc.x * f, acc.y * f, acc.z * f, acc.w * f);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dK / dV
 // One workgroup = 8 wavefronts = 128 keys of one key/value head.  The keys
 // form four 32-key blocks; wavefront w owns block w % 4 for the query rows
@@ -267,9 +357,11 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = w & 3, qhalf = w >> 2;
   const int G = a.G;
-  const TileHead th = tile_major(blockIdx.x, a.B * a.Hkv);  // key tiles x (batch, key/value head)
+  // key tiles x chunks x (batch, key/value head); key tile 0 sees the most
+  // queries: heaviest first
+  const TileHead th = tile_major(blockIdx.x, a.B * a.Hkv);
   const int bh = th.h;
-  const int kt = th.t;  // key tile 0 sees the most queries: heaviest first
+  const int kt = th.t / a.nsplit, chunk = split_chunk<!MASKED>(th.t - kt * a.nsplit, kt, a.nsplit);
   const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
@@ -305,8 +397,13 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     __syncthreads();
     nql = __builtin_amdgcn_readfirstlane(qlist[nq]);
   }
-  const int niter = G * nql;
-  auto qtile_of = [&](int n) { return MASKED ? __builtin_amdgcn_readfirstlane(qlist[n / G]) : nqt - 1 - n / G; };
+  SplitRange sr;
+  if (!split_range<!MASKED>(a, bh, kt, chunk, nql, tid, sr)) return;  // (uniform: nql is)
+  const int niter = G * sr.cnt;
+  auto qtile_of = [&](int n) {
+    const int i = sr.lo + sr.step * (n / G);
+    return MASKED ? __builtin_amdgcn_readfirstlane(qlist[i]) : nqt - 1 - i;
+  };
   const int wkb = (k0 + 32 * kb) / kMaskBlock;  // mask column of this wavefront's keys
   const bool w_keys = k0 + 32 * kb < Lk;
   const int nqb = (Lq + kMaskBlock - 1) / kMaskBlock;  // mask rows
@@ -487,7 +584,22 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  if (w < 4 && key_ok) {
+  if (sr.partial) {
+    if (w < 4) {
+      float* pk = split_part<BN, D>(a, bh, kt, chunk) + (32 * kb + lr) * D;
+      float* pv = pk + BN * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16 &ck = dk[db], &cv = dv[db];
+          *reinterpret_cast<float4*>(pk + 32 * db + 8 * q4 + 4 * lg) =
+              make_float4(ck[4 * q4], ck[4 * q4 + 1], ck[4 * q4 + 2], ck[4 * q4 + 3]);
+          *reinterpret_cast<float4*>(pv + 32 * db + 8 * q4 + 4 * lg) =
+              make_float4(cv[4 * q4], cv[4 * q4 + 1], cv[4 * q4 + 2], cv[4 * q4 + 3]);
+        }
+    }
+  } else if (w < 4 && key_ok) {
     bf16_t* dkp = a.dk.head(b, hk) + (int64_t)krow * a.dk.sl;
     bf16_t* dvp = a.dv.head(b, hk) + (int64_t)krow * a.dv.sl;
     const float sc = -a.scale;  // the accumulators hold -dK / scale
@@ -532,9 +644,11 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   const int kb = w & 1, qhalf = w >> 1;
   const int r0 = 32 * qhalf;  // this wavefront's rows within a tile
   const int G = a.G;
-  const TileHead th = tile_major(blockIdx.x, a.B * a.Hkv);  // key tiles x (batch, key/value head)
+  // key tiles x chunks x (batch, key/value head); key tile 0 sees the most
+  // queries: heaviest first
+  const TileHead th = tile_major(blockIdx.x, a.B * a.Hkv);
   const int bh = th.h;
-  const int kt = th.t;  // key tile 0 sees the most queries: heaviest first
+  const int kt = th.t / a.nsplit, chunk = split_chunk<!MASKED>(th.t - kt * a.nsplit, kt, a.nsplit);
   const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
@@ -567,8 +681,13 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     __syncthreads();
     nql = __builtin_amdgcn_readfirstlane(qlist[nq]);
   }
-  const int niter = G * nql;
-  auto qtile_of = [&](int n) { return MASKED ? __builtin_amdgcn_readfirstlane(qlist[n / G]) : nqt - 1 - n / G; };
+  SplitRange sr;
+  if (!split_range<!MASKED>(a, bh, kt, chunk, nql, tid, sr)) return;  // (uniform: nql is)
+  const int niter = G * sr.cnt;
+  auto qtile_of = [&](int n) {
+    const int i = sr.lo + sr.step * (n / G);
+    return MASKED ? __builtin_amdgcn_readfirstlane(qlist[i]) : nqt - 1 - i;
+  };
 
   const TileLoader<D> ldq(w, lane, a.q.sl), ldo(w, lane, a.dO.sl);
   const bf16_t* const qsrc = a.q.head(b, hk * G);
@@ -680,7 +799,22 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  if (qhalf == 0 && key_ok) {
+  if (sr.partial) {
+    if (qhalf == 0) {
+      float* pk = split_part<BN, D>(a, bh, kt, chunk) + (32 * kb + lr) * D;
+      float* pv = pk + BN * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16 &ck = dk[db], &cv = dv[db];
+          *reinterpret_cast<float4*>(pk + 32 * db + 8 * q4 + 4 * lg) =
+              make_float4(ck[4 * q4], ck[4 * q4 + 1], ck[4 * q4 + 2], ck[4 * q4 + 3]);
+          *reinterpret_cast<float4*>(pv + 32 * db + 8 * q4 + 4 * lg) =
+              make_float4(cv[4 * q4], cv[4 * q4 + 1], cv[4 * q4 + 2], cv[4 * q4 + 3]);
+        }
+    }
+  } else if (qhalf == 0 && key_ok) {
     bf16_t* dkp = a.dk.head(b, hk) + (int64_t)krow * a.dk.sl;
     bf16_t* dvp = a.dv.head(b, hk) + (int64_t)krow * a.dv.sl;
     const float sc = a.scale;
@@ -978,16 +1112,26 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
   BwdArgs a = a0;
   // keys per dK/dV workgroup: 128 up to D = 128; at D = 256, 64, or 32 when
   // 64-key workgroups would make fewer than two per CU (measured: 32-key
-  // workgroups are faster at 128-258 64-key ones, slower from 512)
-  const bool k32 = D > 128 && (int64_t)a.B * a.Hkv * ((a.Lk + 63) / 64) < 512;
+  // workgroups are faster at 128-258 64-key ones, slower from 512).  With a
+  // query-range split (a.part, from a workspace) the 64-key kernel runs: the
+  // split balances the causal triangle instead.
+  const bool split = a.part != nullptr && a.nsplit > 1;
+  if (!split) {
+    a.nsplit = 1;
+    a.part = nullptr;
+    a.split_cnt = nullptr;
+  }
+  const bool k32 = D > 128 && !split && (int64_t)a.B * a.Hkv * ((a.Lk + 63) / 64) < 512;
   const int bnk = D > 128 ? (k32 ? 32 : 64) : 128;
   a.nkt = (a.Lk + bnk - 1) / bnk;
+  // the dK accumulators hold dK / scale, negated in fa_dkv_kernel (V negated)
+  a.ksc = D > 128 ? a.scale : -a.scale;
   const bool masked = a.mask != nullptr;
   // dynamic LDS under a block mask: each workgroup's tile list and its count
   const size_t dq_list = masked ? ((size_t)(a.Lk + BN_Q - 1) / BN_Q + 1) * sizeof(int) : 0;
   const size_t dkv_list = masked ? ((size_t)(a.Lq + 63) / 64 + 1) * sizeof(int) : 0;
   const int ndq = (which & 1) ? a.B * a.Hq * a.nqt : 0;
-  const int ndkv = (which & 2) ? a.B * a.Hkv * a.nkt : 0;
+  const int ndkv = (which & 2) ? a.B * a.Hkv * a.nkt * a.nsplit : 0;
   auto dq = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(ndq), dim3(256), dq_list, stream, a); };
   auto dkv = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(ndkv), dim3(D > 128 ? 256 : 512), dkv_list, stream, a);
@@ -1015,6 +1159,9 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
       else
         masked ? dkv(fa_dkv_kernel<E, D, false, true>) : dkv(fa_dkv_kernel<E, D, false, false>);
     }
+    if (split)
+      hipLaunchKernelGGL((fa_dkv_reduce_kernel<E, D, dkv_split_keys(D)>), dim3(a.B * a.Hkv * a.nkt), dim3(256), 0,
+                         stream, a);
   }
   return hipGetLastError();
 }

@@ -48,6 +48,17 @@ struct BwdArgs {
   float scale_log2;
   const uint8_t* mask;  // block mask [ceil(Lq/64)][nkb], nonzero = kept; null: dense
   int nkb;              // ceil(Lk / 64)
+  // Query-range split of the dK/dV kernels (nsplit > 1; needs a workspace):
+  // a key tile's query-tile list is shared by up to nsplit workgroups (all of
+  // them without a mask; under a mask only lists longer than `cs` entries,
+  // by ceil(len / cs)), each taking every nc-th entry and writing its fp32
+  // dK / dV accumulators to part; the tile's first workgroup writes nc to
+  // split_cnt (0 or 1: written directly, nothing to reduce), and
+  // fa_dkv_reduce_kernel adds the partials up.
+  float* part;          // [B * Hkv][nkt][nsplit][2][BN][D] fp32, or null
+  int* split_cnt;       // [B * Hkv][nkt]
+  int nsplit, cs;       // 1 and unused without a workspace
+  float ksc;            // factor from a dK accumulator to dK (the dV one is 1)
 };
 
 // Short-query path (Lq <= kShortMaxLq): the G * Lq (query head, query row)
@@ -74,8 +85,12 @@ struct SplitArgs {
 // the elements are IEEE half instead of bfloat16.
 hipError_t launch_fwd(const FwdArgs& a, int D, bool causal, bool f16, hipStream_t stream);
 hipError_t launch_delta(const DeltaArgs& a, int D, bool f16, hipStream_t stream);
-// which: 1 = dQ kernel, 2 = dK/dV kernel, 3 = both (dQ first).
+// which: 1 = dQ kernel, 2 = dK/dV kernel, 3 = both (dQ first).  With
+// a.part set, the dK/dV kernel splits long query lists (a.nsplit, a.cs) and a
+// reduction kernel follows it.
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, bool f16, hipStream_t stream);
+// keys per dK/dV workgroup of the split path (64 at head dim 256, else 128)
+constexpr int dkv_split_keys(int D) { return D > 128 ? 64 : 128; }
 // short path: split forward + combine; split dQ + reduce
 hipError_t launch_fwd_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream);
 hipError_t launch_dq_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream);

@@ -228,6 +228,40 @@ fa_status fa_bwd_ex(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, con
                     fa_dtype dtype, const unsigned char* block_mask, unsigned grads, void* stream);
 
 /*
+ * fa_bwd_ex with a workspace for the dK/dV kernel's load balance.  The
+ * dK/dV kernel gives each workgroup one key tile (128 keys; 64 at D = 256)
+ * and loops over the query tiles that see it (page "feat(attention):
+ * complete Flash Attention VJP implementation", Architecture / Two-Kernel
+ * Design).  Under a causal mask the first key tile is seen by every query
+ * tile and the last by almost none; with few key/value heads (fewer than two
+ * workgroups per CU) the kernel then lasts as long as its first tile, and a
+ * block mask can give one key tile every query tile (a sink or global
+ * column, same page, "Sparse Block Masks").  With a workspace, a key tile
+ * whose list of query tiles is long is shared by several workgroups, each
+ * taking a run of the list and writing fp32 partial dK and dV to the
+ * workspace; a second kernel adds them up (no atomics).  dk and dv equal
+ * those of fa_bwd_ex up to the order of fp32 additions.
+ *
+ * fa_bwd_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, masked) is the workspace
+ * these calls use for that shape, with (masked != 0) or without a block
+ * mask; 0 means no split is planned and the workspace may be NULL.  The
+ * workspace is a DEVICE buffer of at least that many bytes, 16-byte aligned,
+ * whose contents on entry do not matter; it must not be shared by calls that
+ * may run at the same time.  It grows linearly with Lk (B * Hkv * Lk * D * 8
+ * bytes times the number of chunks, at most 8).  Other arguments, checks and
+ * errors are those of fa_bwd_ex; FA_ERR_NULL / FA_ERR_ALIGN /
+ * FA_ERR_WORKSPACE for the workspace when dk/dv are asked for and a split is
+ * planned.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D, int masked);
+
+fa_status fa_bwd_ws(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, const float* delta,
+                    fa_tensor dO, fa_tensor dq, fa_tensor dk, fa_tensor dv,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                    fa_dtype dtype, const unsigned char* block_mask, unsigned grads,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Short queries (Lq <= FA_SHORT_MAX_LQ; decode-style shapes).  Page
  * "feat(attention): complete Flash Attention VJP implementation" sends query
  * lengths of at most 8 to separate vector kernels with fp32 accumulators

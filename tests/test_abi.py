@@ -249,3 +249,24 @@ def test_short_noalloc_validation(vlib):
     ws.restype = ctypes.c_size_t
     assert ws(128, 32, 8, 8, 4096, 256) > (64 << 20)
     assert f(big_q, big_kv, big_kv, big_q, P, 128, 32, 8, 8, 4096, 256, 0.1, 1, 0, None) == 11
+
+
+def test_bwd_workspace_plan(lib):
+    f = lib.fa_bwd_workspace_bytes
+    f.restype = ctypes.c_size_t
+    assert f(1, 32, 8, 8192, 8192, 128, 0) == 0        # two rounds of key-tile workgroups: no split
+    assert f(1, 32, 8, 8192, 8192, 128, 1) > 0         # a mask may hold a sink column
+    assert f(1, 16, 2, 8192, 8192, 256, 0) > 0         # one round at head dim 256: split
+    assert f(1, 16, 2, 8192, 8192, 256, 0) % 16 == 0
+    assert f(1, 4, 1, 60, 60, 128, 0) == 0             # one query tile: nothing to split
+    assert f(1, 6, 4, 100, 100, 128, 0) == 0           # Hq % Hkv
+
+
+def test_bwd_ws_validation(vlib):
+    q = _dense(vlib, 16, 8192, 256)
+    kv = _dense(vlib, 2, 8192, 256)
+    f = vlib.fa_bwd_ws
+    args = (q, kv, kv, P, P, q, q, kv, kv, 1, 16, 2, 8192, 8192, 256, 0.1, 1, 0, None, 3)
+    assert f(*args, None, 0, None) == 1                 # split planned, no workspace
+    assert f(*args, P, 1024, None) == 11                # too small
+    assert f(*args, P + 8, 1 << 30, None) == 2          # misaligned
