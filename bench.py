@@ -403,7 +403,7 @@ def gemm_canary(dev, n=4096, reps=10):
 SWEEP = ("dense4k_d64", "dense4k_d96", "d256_8192", "d256_4064x4096", "d256_8200", "long23k")
 
 
-def workload_sweep(dev, names=SWEEP, steps=10, warmup=3):
+def workload_sweep(dev, names=SWEEP, steps=20, warmup=5):
     """For each workload: fa_fwd, fa_bwd_delta, fa_bwd_dq and fa_bwd_dkv on
     resident inputs (the same seeded recipe as the headline), timed with HIP
     events on the launch stream; medians over `steps` steps.  Model TFLOP/s
@@ -429,9 +429,20 @@ def workload_sweep(dev, names=SWEEP, steps=10, warmup=3):
         delta = torch.empty_like(lse)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         sc, causal = w.softmax_scale, w.causal
+        # dK/dV with the load-balancing workspace where the library plans a
+        # split for this shape (allocated here, outside the timed steps)
+        ws_bytes = fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
         torch.cuda.synchronize()
         torch.cuda.reset_peak_memory_stats()
         resident = torch.cuda.memory_allocated()
+
+        def dkv_call():
+            if ws is None:
+                fa.fa_bwd_dkv(q, k, v, lse, delta, do, dk, dv, scale=sc, causal=causal, stream=stream)
+            else:
+                fa.fa_bwd_ex(q, k, v, lse, delta, do, None, dk, dv, scale=sc, causal=causal, grads="dkv",
+                             workspace=ws, stream=stream)
 
         def step(ev=None):
             if ev is not None:
@@ -445,7 +456,7 @@ def workload_sweep(dev, names=SWEEP, steps=10, warmup=3):
             fa.fa_bwd_dq(q, k, v, lse, delta, do, dq, scale=sc, causal=causal, stream=stream)
             if ev is not None:
                 ev[3].record(stream)
-            fa.fa_bwd_dkv(q, k, v, lse, delta, do, dk, dv, scale=sc, causal=causal, stream=stream)
+            dkv_call()
             if ev is not None:
                 ev[4].record(stream)
 
@@ -472,8 +483,9 @@ def workload_sweep(dev, names=SWEEP, steps=10, warmup=3):
             "fwd_frac_of_peak": round(fwd_f / (med["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "peak_bytes": int(torch.cuda.max_memory_allocated()),
             "resident_bytes": int(resident),
+            "dkv_call": "fa_bwd_dkv" if ws is None else f"fa_bwd_ws ({ws_bytes} bytes of workspace)",
         }
-        del g, q, k, v, do, o, lse, delta, dq, dk, dv
+        del g, q, k, v, do, o, lse, delta, dq, dk, dv, ws
         torch.cuda.empty_cache()
     return out
 
@@ -545,6 +557,12 @@ def main(argv=None):
         ws = torch.empty(fa.fa_short_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D), dtype=torch.uint8,
                          device=dev)
 
+    # dK/dV through fa_bwd_ws where the library plans a load-balancing split
+    # for this shape (never for the 8192-token headline shape); the workspace
+    # is allocated before the timed steps and counted as resident
+    ws_bytes = 0 if short else fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, mask is not None)
+    dkv_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+
     def step_short(ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -577,7 +595,7 @@ def main(argv=None):
         if ev is not None:
             ev[3].record(stream)
         fa.fa_bwd_ex(q, k, v, lse, delta, do, None, dk, dv, scale=sc, causal=causal, block_mask=mask,
-                     grads="dkv", stream=stream)
+                     grads="dkv", stream=stream, workspace=False if dkv_ws is None else dkv_ws)
         if ev is not None:
             ev[4].record(stream)
 
@@ -604,7 +622,10 @@ def main(argv=None):
                                       stream=stream)
         if ev is not None:
             ev[3].record(stream)
-        if mask is None:
+        if dkv_ws is not None:
+            fa.fa_bwd_ex(q, k, v, lse, delta, do, None, dk, dv, scale=sc, causal=causal, block_mask=mask,
+                         grads="dkv", workspace=dkv_ws, stream=stream)
+        elif mask is None:
             fa.fa_bwd_dkv(q, k, v, lse, delta, do, dk, dv, scale=sc, causal=causal, stream=stream)
         else:
             fa.fa_bwd_dkv_block_sparse(q, k, v, lse, delta, do, mask, dk, dv, scale=sc, causal=causal,
@@ -714,7 +735,8 @@ def main(argv=None):
         "config": {"workload": f"{w.name}: {kind} GQA fwd+bwd, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
                                f"Lq={w.Lq} Lk={w.Lk} D={w.D}{mask_desc}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Lq": w.Lq, "Lk": w.Lk, "D": w.D, "causal": w.causal,
-                   "visible_pairs_per_head": int(pairs)},
+                   "visible_pairs_per_head": int(pairs),
+                   "dkv_workspace_bytes": int(ws_bytes)},
         "frac_of_peak": round(value / (PEAK_HBM_GBS if short else PEAK_BF16_TFLOPS), 4),
         "model_tflop_per_step": round(total_flops / 1e12, 4),
         "kernels": {n: {kk: round(vv, 4) for kk, vv in d.items()} for n, d in kernels.items()},

@@ -214,36 +214,45 @@ fa_status delta_common(const fa_tensor& o, const fa_tensor& dO, float* delta, in
 // tile's work is its query-tile list times the group size.  Under a causal
 // mask the first key tile sees every query tile, the last almost none: with
 // at least two workgroups per CU the hardware's heaviest-first rounds pair
-// them up, with fewer the kernel lasts as long as the first tile.  A block
-// mask can hand one key tile every query tile (a global or sink column).
-// So: with a mask, lists longer than a quarter of the query tiles are split
-// four ways; without one, when there are fewer than 512 key-tile workgroups
-// (two per CU), every list is split until about 1024 workgroups (at most 8
-// chunks).  Lists that fit one chunk are written directly.
+// them up, with fewer the kernel lasts as long as the first tile.  So without
+// a mask, when there are fewer than 512 key-tile workgroups (two per CU),
+// every list is split until there are about 1024 workgroups (at most 8
+// chunks).  A block mask can hand one key tile every query tile (a sink or
+// global column) while the others see few: then a planning kernel measures
+// the lists on the device and splits only the long ones, with at most
+// jmax = max(16, nkt / 4) extra chunks per head.
 struct DkvSplit {
-  int nsplit, cs;
+  int nsplit, jmax;
   size_t part_bytes, bytes;
 };
 
 DkvSplit dkv_split_plan(int B, int Hkv, int Lq, int Lk, int D, bool masked) {
   DkvSplit p{1, 0, 0, 0};
   if (B <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || !bwd_head_dim_ok(D)) return p;
+  if (masked && (Lq > FA_MASK_MAX_LEN || Lk > FA_MASK_MAX_LEN)) return p;
   const int bnk = cgqa::dkv_split_keys(D);
   const int64_t nkt = ((int64_t)Lk + bnk - 1) / bnk;
-  const int64_t wgs = (int64_t)B * Hkv * nkt;
+  const int64_t nh = (int64_t)B * Hkv;
+  const int64_t wgs = nh * nkt;
   const int64_t nqt = ((int64_t)Lq + 63) / 64;
-  int64_t S = 1;
+  const size_t slot_bytes = (size_t)2 * bnk * D * sizeof(float);
   if (masked) {
-    S = 4;
-  } else if (wgs < 512) {
-    S = 2;
-    while (S < 8 && wgs * S < 1024) S *= 2;
+    if (nqt < 2 || nkt > cgqa::kMaxPlanTiles) return p;
+    const int64_t jmax = std::max<int64_t>(16, (nkt + 3) / 4);
+    if (wgs + nh * jmax > INT32_MAX || nh * jmax * 8 > INT32_MAX) return p;
+    p.nsplit = 8;
+    p.jmax = (int)jmax;
+    p.part_bytes = (size_t)(nh * 2 * jmax) * slot_bytes;
+    p.bytes = p.part_bytes + (((size_t)cgqa::dkv_plan_ints(nkt, jmax) * sizeof(int) + 255) & ~(size_t)255);
+    return p;
   }
+  if (wgs >= 512 || wgs * 8 > INT32_MAX) return p;
+  int64_t S = 2;
+  while (S < 8 && wgs * S < 1024) S *= 2;
   S = std::min<int64_t>(S, nqt);
-  if (S <= 1 || wgs * S > INT32_MAX) return p;
+  if (S <= 1) return p;
   p.nsplit = (int)S;
-  p.cs = (int)((nqt + S - 1) / S);
-  p.part_bytes = (size_t)(wgs * S) * 2 * bnk * D * sizeof(float);
+  p.part_bytes = (size_t)(wgs * S) * slot_bytes;
   p.bytes = p.part_bytes + (((size_t)wgs * sizeof(int) + 255) & ~(size_t)255);
   return p;
 }
@@ -319,9 +328,16 @@ fa_status bwd_common(const fa_tensor& q, const fa_tensor& k, const fa_tensor& v,
   a.nsplit = 1;
   if (split.nsplit > 1) {
     a.part = static_cast<float*>(workspace);
-    a.split_cnt = reinterpret_cast<int*>(static_cast<char*>(workspace) + split.part_bytes);
+    int* tail = reinterpret_cast<int*>(static_cast<char*>(workspace) + split.part_bytes);
     a.nsplit = split.nsplit;
-    a.cs = split.cs;
+    if (block_mask != nullptr) {
+      a.plan = tail;
+      a.jmax = split.jmax;
+      a.slots = 2 * split.jmax;
+      a.nextra = B * Hkv * split.jmax;
+    } else {
+      a.split_cnt = tail;
+    }
   }
   const hipError_t e = cgqa::launch_bwd(a, D, causal != 0, (int)which, dtype == FA_F16,
                                         static_cast<hipStream_t>(stream));

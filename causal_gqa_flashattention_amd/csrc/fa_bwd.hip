@@ -229,92 +229,255 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
 }
 
 // ---------------------------------------------------------------- dK / dV split
-// Query-range split (nsplit > 1, with a workspace): the workgroups of one key
-// tile are chunks 0 .. nsplit - 1 of its query-tile list (`len` entries).
-// The tile is shared by nc chunks, chunk c taking entries c, c + nc,
-// c + 2 nc, ... and writing fp32 partials; chunk 0 records nc for the
-// reduction kernel.  Strided, not consecutive, entries: the workgroups of one
-// chunk index then walk the query tiles in the same order, last first, and
-// those running at the same time share the tiles they load in L2 (with runs
-// of consecutive entries they read different tiles and the head-dim-256
-// kernel became bound by HBM).
-//  * Without a block mask (UNIFORM) every list is split nsplit ways
-//    (nc = min(nsplit, len)) and chunk c runs in slot c: workgroups are dealt
-//    round-robin to the XCDs by index, so one XCD runs one chunk index of
-//    many tiles in step.
-//  * Under a mask most lists may be short: a list that fits one chunk of
-//    `cs` entries is computed whole by chunk 0 and written directly (no
-//    partials), a longer one is shared by nc = ceil(len / cs) chunks.  Only
-//    chunk 0 always has work, so it is rotated to slot kt mod nsplit (see
-//    split_chunk).
-// Returns false for a workgroup with nothing to do (the caller exits before
-// its first barrier or after one every wavefront passes).
+// Query-range split (nsplit > 1, with a workspace): the workgroups that share
+// a key tile are chunks 0 .. nc - 1 of its query-tile list (`len` entries),
+// chunk c taking entries c, c + nc, c + 2 nc, ... and writing fp32 partials
+// that fa_dkv_reduce_kernel adds up.  Strided, not consecutive, entries: the
+// workgroups of one chunk index walk the query tiles in the same order, last
+// first, and those running at the same time share the tiles they load in L2
+// (with runs of consecutive entries they read different tiles and the
+// head-dim-256 kernel became bound by HBM).
+//  * Without a mask every list is split min(nsplit, len) ways and chunk c runs
+//    in slot c of the tile's nsplit consecutive workgroups: workgroups are
+//    dealt round-robin to the XCDs by index, so one XCD runs one chunk index
+//    of many tiles in step.  (Only chunk 0 then records nc.)
+//  * Under a mask most lists may be short and a few long (a sink column).
+//    fa_dkv_plan_kernel has measured every list and chosen nc per tile; the
+//    grid starts with one workgroup per extra chunk (c >= 1) of the long
+//    lists, then one per key tile for chunk 0.
+struct DkvWork {
+  int bh, kt, chunk;
+};
+
+// at most this many chunks per key tile under a mask (the extra-chunk table
+// keeps kt * kMaxChunks + c)
+constexpr int kMaxChunks = 32;
+
+// Which (head, key tile, chunk) this workgroup takes; false: nothing (an
+// unused extra-chunk workgroup, which exits at once).
+template <bool MASKED>
+__device__ __forceinline__ bool dkv_work(const BwdArgs& a, DkvWork& wk) {
+  const int nh = a.B * a.Hkv;
+  if (a.nsplit <= 1) {
+    const TileHead th = tile_major(blockIdx.x, nh);  // key tiles x heads, tile 0 (heaviest) first
+    wk = {th.h, th.t, 0};
+    return true;
+  }
+  if constexpr (!MASKED) {
+    const TileHead th = tile_major(blockIdx.x, nh);
+    const int kt = th.t / a.nsplit;
+    wk = {th.h, kt, th.t - kt * a.nsplit};
+    return true;
+  } else {
+    if ((int)blockIdx.x < a.nextra) {
+      const TileHead th = tile_major(blockIdx.x, nh);  // extra chunks x heads
+      if (th.t >= a.plan[0]) return false;
+      const int e = a.plan[3 + 2 * a.nkt + th.t];
+      wk = {th.h, e / kMaxChunks, e % kMaxChunks};
+      return true;
+    }
+    const TileHead th = tile_major(blockIdx.x - a.nextra, nh);
+    wk = {th.h, th.t, 0};
+    return true;
+  }
+}
+
 struct SplitRange {
   int lo, step, cnt;  // list entries lo, lo + step, ... (cnt of them)
-  bool partial;
+  float* part;        // this chunk's partials, or null: write dK / dV directly
 };
-template <bool UNIFORM>
-__device__ __forceinline__ bool split_range(const BwdArgs& a, int bh, int kt, int chunk, int len, int tid,
-                                            SplitRange& r) {
-  r = {0, 1, len, false};
+
+// This workgroup's share of its key tile's list of `len` entries; false when
+// it has none (the caller exits before its first barrier or after one every
+// wavefront passes).
+template <bool MASKED, int BN, int D>
+__device__ __forceinline__ bool split_range(const BwdArgs& a, const DkvWork& wk, int len, int tid, SplitRange& r) {
+  r = {0, 1, len, nullptr};
   if (a.nsplit <= 1) return true;
-  const int nc = UNIFORM ? min(a.nsplit, len) : (len + a.cs - 1) / a.cs;
-  if (chunk == 0 && tid == 0) a.split_cnt[bh * a.nkt + kt] = nc;
-  if (nc <= 1) return chunk == 0;
-  if (chunk >= nc) return false;
-  r = {chunk, nc, (len - chunk + nc - 1) / nc, true};
+  int nc;
+  float* slot0;
+  if constexpr (!MASKED) {
+    nc = min(a.nsplit, len);
+    if (wk.chunk == 0 && tid == 0) a.split_cnt[wk.bh * a.nkt + wk.kt] = nc;
+    slot0 = a.part + ((int64_t)(wk.bh * a.nkt + wk.kt) * a.nsplit) * (2 * BN * D);
+  } else {
+    nc = a.plan[3 + wk.kt];
+    slot0 = a.part + ((int64_t)wk.bh * a.slots + a.plan[3 + a.nkt + wk.kt]) * (2 * BN * D);
+  }
+  if (nc <= 1) return wk.chunk == 0;
+  if (wk.chunk >= nc) return false;
+  r = {wk.chunk, nc, (len - wk.chunk + nc - 1) / nc, slot0 + (int64_t)wk.chunk * (2 * BN * D)};
   return true;
 }
 
-// Chunk of key tile kt that runs in slot `slot` of the tile's nsplit
-// consecutive workgroups.  Workgroups are dealt round-robin to the XCDs and,
-// within one, to its shader engines, so the slot decides where a chunk runs.
-// Under a mask chunk 0, the only one that always has work, is rotated to slot
-// kt mod nsplit so that busy workgroups spread over the whole chip (with the
-// chunk in the slot, every busy workgroup of a masked call whose lists are
-// short landed on one engine in four: measured three times slower).
-template <bool UNIFORM>
-__device__ __forceinline__ int split_chunk(int slot, int kt, int nsplit) {
-  return UNIFORM ? slot : (slot + nsplit - kt % nsplit) % nsplit;
-}
-
-// fp32 partials of chunk `chunk` of key tile kt: [2][BN][D] (dK accumulators,
-// then dV), key rows of the tile in order.
-template <int BN, int D>
-__device__ __forceinline__ float* split_part(const BwdArgs& a, int bh, int kt, int chunk) {
-  return a.part + ((int64_t)(bh * a.nkt + kt) * a.nsplit + chunk) * (2 * BN * D);
-}
-
-// Sum of the partials of every split key tile: one workgroup per (batch,
-// key/value head, key tile); tiles written directly are skipped.  dK takes
-// the factor ksc (the sign and scale the dK/dV kernel left out), dV none.
+// The partials of every split key tile added up.  kReduceSlices workgroups
+// per (batch, key/value head, split tile), each over a slice of the tile's
+// dK and dV elements, with the chunks' loads issued four at a time (a tile's
+// partials are a few MB: one workgroup per tile was bound by load latency).
+// Without a mask every tile is a candidate (tiles written directly exit);
+// under one the plan lists the split tiles.  dK takes the factor ksc (the
+// sign and scale the dK/dV kernel left out), dV none.
+constexpr int kReduceSlices = 8;
 template <class E, int D, int BN>
 __global__ __launch_bounds__(256) void fa_dkv_reduce_kernel(BwdArgs a) {
-  const int bh = blockIdx.x / a.nkt, kt = blockIdx.x - bh * a.nkt;
-  const int nc = a.split_cnt[bh * a.nkt + kt];
+  const bool planned = a.plan != nullptr;
+  const int per_head = (planned ? a.jmax : a.nkt) * kReduceSlices;
+  const int bh = blockIdx.x / per_head;
+  const int rest = blockIdx.x - bh * per_head;
+  const int ti = rest / kReduceSlices, slice = rest - ti * kReduceSlices;
+  int kt, nc;
+  const float* base;
+  if (planned) {
+    if (ti >= a.plan[2]) return;
+    kt = a.plan[3 + 2 * a.nkt + a.jmax + ti];
+    nc = a.plan[3 + kt];
+    base = a.part + ((int64_t)bh * a.slots + a.plan[3 + a.nkt + kt]) * (2 * BN * D);
+  } else {
+    kt = ti;
+    nc = a.split_cnt[bh * a.nkt + kt];
+    base = a.part + ((int64_t)(bh * a.nkt + kt) * a.nsplit) * (2 * BN * D);
+  }
   if (nc <= 1) return;
   const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
   const int k0 = kt * BN;
-  const float* base = split_part<BN, D>(a, bh, kt, 0);
-  constexpr int NV = BN * D / 4;  // float4 per array
-#pragma unroll 1
-  for (int which = 0; which < 2; ++which) {
-    const float f = which == 0 ? a.ksc : 1.f;
-    const Tensor& t = which == 0 ? a.dk : a.dv;
-    for (int e = threadIdx.x; e < NV; e += 256) {
-      const int key = (4 * e) / D, d = 4 * e - key * D;
-      if (k0 + key >= a.Lk) continue;
-      float4 acc = *reinterpret_cast<const float4*>(base + which * BN * D + 4 * e);
-      for (int c = 1; c < nc; ++c) {
-        const float4 x = *reinterpret_cast<const float4*>(base + (int64_t)c * 2 * BN * D + which * BN * D + 4 * e);
-        acc.x += x.x;
-        acc.y += x.y;
-        acc.z += x.z;
-        acc.w += x.w;
+  constexpr int NV = 2 * BN * D / 4;  // float4 of dK then dV
+  constexpr int PER = NV / kReduceSlices;
+  static_assert(NV % kReduceSlices == 0 && PER % 256 == 0, "reduction slices");
+  for (int e = slice * PER + threadIdx.x; e < (slice + 1) * PER; e += 256) {
+    const int which = e >= NV / 2;
+    const int el = 4 * e - which * BN * D;
+    const int key = el / D, d = el - key * D;
+    if (k0 + key >= a.Lk) continue;
+    const float* p = base + 4 * e;
+    float4 acc = *reinterpret_cast<const float4*>(p);
+    int c = 1;
+    for (; c + 4 <= nc; c += 4) {
+      float4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const float4*>(p + (int64_t)(c + u) * 2 * BN * D);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc.x += x[u].x;
+        acc.y += x[u].y;
+        acc.z += x[u].z;
+        acc.w += x[u].w;
       }
-      *reinterpret_cast<uint2*>(t.head(b, hk) + (int64_t)(k0 + key) * t.sl + d) =
-          E::pack4(acc.x * f, acc.y * f, acc.z * f, acc.w * f);
     }
+    for (; c < nc; ++c) {
+      const float4 x = *reinterpret_cast<const float4*>(p + (int64_t)c * 2 * BN * D);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    const float f = which ? 1.f : a.ksc;
+    const Tensor& t = which ? a.dv : a.dk;
+    *reinterpret_cast<uint2*>(t.head(b, hk) + (int64_t)(k0 + key) * t.sl + d) =
+        E::pack4(acc.x * f, acc.y * f, acc.z * f, acc.w * f);
+  }
+}
+
+// List length of every key tile under a block mask: one wavefront per key
+// tile counts the BM-row query tiles that some key of the BN-key tile sees
+// (the lists the dK/dV kernel builds), 64 candidates per step.  The mask is
+// the same for every head, so are the lengths.
+template <int BM, int BN, bool CAUSAL>
+__global__ __launch_bounds__(64) void fa_dkv_count_kernel(BwdArgs a) {
+  const int kt = blockIdx.x, lane = threadIdx.x;
+  const int nqt = (a.Lq + BM - 1) / BM, nqb = (a.Lq + kMaskBlock - 1) / kMaskBlock;
+  const int k0 = kt * BN;
+  const int qt_first = (CAUSAL ? max(0, k0 - a.off) : 0) / BM;
+  const int kb0 = k0 / kMaskBlock, kb1 = (min(k0 + BN, a.Lk) - 1) / kMaskBlock;
+  int cnt = 0;
+  for (int q0 = qt_first; q0 < nqt; q0 += 64) {
+    const int qt = q0 + lane;
+    bool any = false;
+    if (qt < nqt) {
+      const int rb_end = min((qt + 1) * (BM / kMaskBlock), nqb);
+      for (int rb = qt * (BM / kMaskBlock); rb < rb_end; ++rb)
+        for (int kbk = kb0; kbk <= kb1; ++kbk) any |= a.mask[rb * a.nkb + kbk] != 0;
+    }
+    cnt += __popcll(__ballot(any));
+  }
+  if (lane == 0) a.plan[3 + 2 * a.nkt + 2 * a.jmax + kt] = cnt;
+}
+
+// The split plan under a block mask (one workgroup, after
+// fa_dkv_count_kernel): lists up to 1.25x the mean length are computed whole;
+// a longer one is cut into chunks of cs = max(ceil(mean / 2),
+// ceil(max / kMaxChunks)) entries, cs doubled until the extra chunks fit
+// jmax; tile kt gets nc chunks, its first slot, and its chunks c >= 1 a place
+// in the extra-chunk table.  (Half-mean chunks keep a long list's extra work
+// in pieces small enough to fill the gaps the short lists leave: with chunks
+// of 1.25 means, the 8192-token shape with a 1024-key window and one sink
+// block took 0.48 ms for dK/dV, with half-mean chunks 0.43 ms.)
+__global__ __launch_bounds__(1024) void fa_dkv_plan_kernel(BwdArgs a) {
+  __shared__ int len_s[kMaxPlanTiles];
+  __shared__ int red[2][16];
+  __shared__ int cs_s, thr_s;
+  const int tid = threadIdx.x, nkt = a.nkt;
+  const int* lens = a.plan + 3 + 2 * nkt + 2 * a.jmax;
+  int sum = 0, mx = 0;
+  for (int kt = tid; kt < nkt; kt += 1024) {
+    const int l = lens[kt];
+    len_s[kt] = l;
+    sum += l;
+    mx = max(mx, l);
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    sum += __shfl_xor(sum, o, 64);
+    mx = max(mx, __shfl_xor(mx, o, 64));
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = sum;
+    red[1][tid >> 6] = mx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int s = 0, m = 0;
+    for (int i = 0; i < 16; ++i) {
+      s += red[0][i];
+      m = max(m, red[1][i]);
+    }
+    thr_s = (5 * s + 4 * nkt - 1) / (4 * nkt);
+    cs_s = max(1, max((s + 2 * nkt - 1) / (2 * nkt), (m + kMaxChunks - 1) / kMaxChunks));
+  }
+  __syncthreads();
+  const int thr = thr_s;
+  // double cs until the extra chunks fit (every thread counts its tiles)
+  for (;;) {
+    const int cs = cs_s;
+    int extra = 0;
+    for (int kt = tid; kt < nkt; kt += 1024)
+      if (len_s[kt] > thr) extra += (len_s[kt] + cs - 1) / cs - 1;
+    for (int o = 32; o >= 1; o >>= 1) extra += __shfl_xor(extra, o, 64);
+    __syncthreads();
+    if ((tid & 63) == 0) red[0][tid >> 6] = extra;
+    __syncthreads();
+    int tot = 0;
+    for (int i = 0; i < 16; ++i) tot += red[0][i];
+    if (tot <= a.jmax) break;  // (the same decision in every thread)
+    __syncthreads();
+    if (tid == 0) cs_s = 2 * cs;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int cs = cs_s;
+    int* plan = a.plan;
+    int slot = 0, j = 0, ns = 0;
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int nc = len_s[kt] > thr ? max(1, (len_s[kt] + cs - 1) / cs) : 1;
+      plan[3 + kt] = nc;
+      plan[3 + nkt + kt] = nc > 1 ? slot : 0;
+      if (nc > 1) {
+        slot += nc;
+        plan[3 + 2 * nkt + a.jmax + ns++] = kt;
+        for (int c = 1; c < nc; ++c) plan[3 + 2 * nkt + j++] = kt * kMaxChunks + c;
+      }
+    }
+    plan[0] = j;
+    plan[1] = cs;
+    plan[2] = ns;
   }
 }
 
@@ -357,11 +520,11 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = w & 3, qhalf = w >> 2;
   const int G = a.G;
-  // key tiles x chunks x (batch, key/value head); key tile 0 sees the most
+  // key tiles (x chunks) x (batch, key/value head); key tile 0 sees the most
   // queries: heaviest first
-  const TileHead th = tile_major(blockIdx.x, a.B * a.Hkv);
-  const int bh = th.h;
-  const int kt = th.t / a.nsplit, chunk = split_chunk<!MASKED>(th.t - kt * a.nsplit, kt, a.nsplit);
+  DkvWork wk;
+  if (!dkv_work<MASKED>(a, wk)) return;
+  const int bh = wk.bh, kt = wk.kt;
   const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
@@ -398,7 +561,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     nql = __builtin_amdgcn_readfirstlane(qlist[nq]);
   }
   SplitRange sr;
-  if (!split_range<!MASKED>(a, bh, kt, chunk, nql, tid, sr)) return;  // (uniform: nql is)
+  if (!split_range<MASKED, BN, D>(a, wk, nql, tid, sr)) return;  // (uniform: nql is)
   const int niter = G * sr.cnt;
   auto qtile_of = [&](int n) {
     const int i = sr.lo + sr.step * (n / G);
@@ -584,9 +747,9 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  if (sr.partial) {
+  if (sr.part != nullptr) {
     if (w < 4) {
-      float* pk = split_part<BN, D>(a, bh, kt, chunk) + (32 * kb + lr) * D;
+      float* pk = sr.part + (32 * kb + lr) * D;
       float* pv = pk + BN * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -644,11 +807,11 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   const int kb = w & 1, qhalf = w >> 1;
   const int r0 = 32 * qhalf;  // this wavefront's rows within a tile
   const int G = a.G;
-  // key tiles x chunks x (batch, key/value head); key tile 0 sees the most
+  // key tiles (x chunks) x (batch, key/value head); key tile 0 sees the most
   // queries: heaviest first
-  const TileHead th = tile_major(blockIdx.x, a.B * a.Hkv);
-  const int bh = th.h;
-  const int kt = th.t / a.nsplit, chunk = split_chunk<!MASKED>(th.t - kt * a.nsplit, kt, a.nsplit);
+  DkvWork wk;
+  if (!dkv_work<MASKED>(a, wk)) return;
+  const int bh = wk.bh, kt = wk.kt;
   const int b = bh / a.Hkv, hk = bh - (bh / a.Hkv) * a.Hkv;
   const int Lq = a.Lq, Lk = a.Lk, off = a.off;
 
@@ -682,7 +845,7 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     nql = __builtin_amdgcn_readfirstlane(qlist[nq]);
   }
   SplitRange sr;
-  if (!split_range<!MASKED>(a, bh, kt, chunk, nql, tid, sr)) return;  // (uniform: nql is)
+  if (!split_range<MASKED, BN, D>(a, wk, nql, tid, sr)) return;  // (uniform: nql is)
   const int niter = G * sr.cnt;
   auto qtile_of = [&](int n) {
     const int i = sr.lo + sr.step * (n / G);
@@ -799,9 +962,9 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  if (sr.partial) {
+  if (sr.part != nullptr) {
     if (qhalf == 0) {
-      float* pk = split_part<BN, D>(a, bh, kt, chunk) + (32 * kb + lr) * D;
+      float* pk = sr.part + (32 * kb + lr) * D;
       float* pv = pk + BN * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -1120,6 +1283,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
     a.nsplit = 1;
     a.part = nullptr;
     a.split_cnt = nullptr;
+    a.plan = nullptr;
   }
   const bool k32 = D > 128 && !split && (int64_t)a.B * a.Hkv * ((a.Lk + 63) / 64) < 512;
   const int bnk = D > 128 ? (k32 ? 32 : 64) : 128;
@@ -1130,12 +1294,23 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
   // dynamic LDS under a block mask: each workgroup's tile list and its count
   const size_t dq_list = masked ? ((size_t)(a.Lk + BN_Q - 1) / BN_Q + 1) * sizeof(int) : 0;
   const size_t dkv_list = masked ? ((size_t)(a.Lq + 63) / 64 + 1) * sizeof(int) : 0;
+  const int nh = a.B * a.Hkv;
   const int ndq = (which & 1) ? a.B * a.Hq * a.nqt : 0;
-  const int ndkv = (which & 2) ? a.B * a.Hkv * a.nkt * a.nsplit : 0;
+  // dK/dV workgroups: key tiles (x chunks without a mask; extra chunks first
+  // under one)
+  const int ndkv = !(which & 2) ? 0 : !split ? nh * a.nkt : masked ? a.nextra + nh * a.nkt : nh * a.nkt * a.nsplit;
   auto dq = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(ndq), dim3(256), dq_list, stream, a); };
   auto dkv = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(ndkv), dim3(D > 128 ? 256 : 512), dkv_list, stream, a);
   };
+  if (split && masked && ndkv > 0) {
+    constexpr int BMK = D == 64 ? 128 : 64;  // the dK/dV kernel's query tile
+    if (causal)
+      hipLaunchKernelGGL((fa_dkv_count_kernel<BMK, dkv_split_keys(D), true>), dim3(a.nkt), dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fa_dkv_count_kernel<BMK, dkv_split_keys(D), false>), dim3(a.nkt), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(fa_dkv_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+  }
   if (ndq > 0) {
     if (causal)
       masked ? dq(fa_dq_kernel<E, D, BN_Q, true, true>) : dq(fa_dq_kernel<E, D, BN_Q, true, false>);
@@ -1160,8 +1335,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
         masked ? dkv(fa_dkv_kernel<E, D, false, true>) : dkv(fa_dkv_kernel<E, D, false, false>);
     }
     if (split)
-      hipLaunchKernelGGL((fa_dkv_reduce_kernel<E, D, dkv_split_keys(D)>), dim3(a.B * a.Hkv * a.nkt), dim3(256), 0,
-                         stream, a);
+      hipLaunchKernelGGL((fa_dkv_reduce_kernel<E, D, dkv_split_keys(D)>),
+                         dim3(nh * (masked ? a.jmax : a.nkt) * kReduceSlices), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }

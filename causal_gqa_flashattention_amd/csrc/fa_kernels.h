@@ -48,16 +48,28 @@ struct BwdArgs {
   float scale_log2;
   const uint8_t* mask;  // block mask [ceil(Lq/64)][nkb], nonzero = kept; null: dense
   int nkb;              // ceil(Lk / 64)
-  // Query-range split of the dK/dV kernels (nsplit > 1; needs a workspace):
-  // a key tile's query-tile list is shared by up to nsplit workgroups (all of
-  // them without a mask; under a mask only lists longer than `cs` entries,
-  // by ceil(len / cs)), each taking every nc-th entry and writing its fp32
-  // dK / dV accumulators to part; the tile's first workgroup writes nc to
-  // split_cnt (0 or 1: written directly, nothing to reduce), and
-  // fa_dkv_reduce_kernel adds the partials up.
-  float* part;          // [B * Hkv][nkt][nsplit][2][BN][D] fp32, or null
-  int* split_cnt;       // [B * Hkv][nkt]
-  int nsplit, cs;       // 1 and unused without a workspace
+  // Query-range split of the dK/dV kernels (nsplit > 1; needs a workspace).
+  // A key tile's query-tile list is shared by nc workgroups, chunk c taking
+  // every nc-th entry from entry c and writing its fp32 dK / dV accumulators
+  // to a slot of `part`; fa_dkv_reduce_kernel adds a tile's slots up.
+  //  * Without a mask (plan == null): every list is split min(nsplit, len)
+  //    ways; the grid is key tiles x nsplit; slots [B * Hkv][nkt][nsplit];
+  //    chunk 0 writes nc to split_cnt.
+  //  * Under a mask (plan != null): fa_dkv_count_kernel measures every key
+  //    tile's list and fa_dkv_plan_kernel writes plan (int32): [0] the
+  //    number of extra chunks J, [1] the chunk length cs, [2] the number of
+  //    split tiles, [3 + kt] nc of tile kt (1: written directly),
+  //    [3 + nkt + kt] its first slot, [3 + 2 nkt + j] extra chunk j as
+  //    kt * kMaxChunks + c (c >= 1), [3 + 2 nkt + jmax + i] split tile i,
+  //    [3 + 2 nkt + 2 jmax + kt] the list length of tile kt.  The grid is
+  //    nextra = B * Hkv * jmax extra-chunk workgroups (first, so that long
+  //    lists start early), then one workgroup per key tile for chunk 0;
+  //    slots [B * Hkv][slots].
+  float* part;          // fp32 partials [.][2][BN][D] (dK accumulators, then dV), or null
+  int* split_cnt;       // [B * Hkv][nkt] (no mask)
+  int* plan;            // (mask) see above
+  int nsplit, cs;       // chunks per key tile (at most), entries per chunk
+  int nextra, jmax, slots;
   float ksc;            // factor from a dK accumulator to dK (the dV one is 1)
 };
 
@@ -91,6 +103,10 @@ hipError_t launch_delta(const DeltaArgs& a, int D, bool f16, hipStream_t stream)
 hipError_t launch_bwd(const BwdArgs& a, int D, bool causal, int which, bool f16, hipStream_t stream);
 // keys per dK/dV workgroup of the split path (64 at head dim 256, else 128)
 constexpr int dkv_split_keys(int D) { return D > 128 ? 64 : 128; }
+// key tiles a masked call's split plan can hold (Lk <= 262144, 64-key tiles)
+constexpr int kMaxPlanTiles = 4096;
+// int32 entries of a masked call's split plan
+constexpr int64_t dkv_plan_ints(int64_t nkt, int64_t jmax) { return 3 + 3 * nkt + 2 * jmax; }
 // short path: split forward + combine; split dQ + reduce
 hipError_t launch_fwd_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream);
 hipError_t launch_dq_short(const SplitArgs& a, int D, bool causal, bool f16, hipStream_t stream);

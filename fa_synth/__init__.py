@@ -146,6 +146,10 @@ WORKLOADS = {
     "decode32k_d128": AttnShape("decode32k_d128", 1, 32, 8, 1, 32768, 128, True, seed=7200),
     "train8k_window": AttnShape("train8k_window", 1, 32, 8, 8192, 8192, 128, True, seed=2100,
                                 mask=("window", 1024, 0)),
+    # the same window plus the first key block kept for every query block (a
+    # "sink" column: one key tile seen by every query tile)
+    "train8k_sink": AttnShape("train8k_sink", 1, 32, 8, 8192, 8192, 128, True, seed=2100,
+                              mask=("window", 1024, 1)),
 }
 
 

@@ -239,16 +239,21 @@ fa_status fa_bwd_ex(fa_tensor q, fa_tensor k, fa_tensor v, const float* lse, con
  * column, same page, "Sparse Block Masks").  With a workspace, a key tile
  * whose list of query tiles is long is shared by several workgroups, each
  * taking a run of the list and writing fp32 partial dK and dV to the
- * workspace; a second kernel adds them up (no atomics).  dk and dv equal
- * those of fa_bwd_ex up to the order of fp32 additions.
+ * workspace; a second kernel adds them up (no atomics).  Without a mask, when
+ * there are fewer than two key-tile workgroups per CU, every list is split
+ * the same number of ways (at most 8); under a mask a planning kernel reads
+ * the mask on the device and splits only the lists longer than 1.25x the
+ * mean, into chunks of about half the mean.  dk and dv equal those of
+ * fa_bwd_ex up to the order of fp32 additions.
  *
  * fa_bwd_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, masked) is the workspace
  * these calls use for that shape, with (masked != 0) or without a block
  * mask; 0 means no split is planned and the workspace may be NULL.  The
  * workspace is a DEVICE buffer of at least that many bytes, 16-byte aligned,
  * whose contents on entry do not matter; it must not be shared by calls that
- * may run at the same time.  It grows linearly with Lk (B * Hkv * Lk * D * 8
- * bytes times the number of chunks, at most 8).  Other arguments, checks and
+ * may run at the same time.  It grows linearly with Lk: about
+ * B * Hkv * Lk * D * 8 bytes times the number of chunks without a mask, and
+ * about B * Hkv * Lk * D * 4 bytes under one.  Other arguments, checks and
  * errors are those of fa_bwd_ex; FA_ERR_NULL / FA_ERR_ALIGN /
  * FA_ERR_WORKSPACE for the workspace when dk/dv are asked for and a split is
  * planned.
