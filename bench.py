@@ -171,8 +171,9 @@ def summarize_pmc(fetch_csv, write_csv, workload):
             # every kernel variant of a stage (e.g. fa_fwd_kernel, fa_fwd_pp_kernel)
             for key, tag in (("fwd", "cgqa::fa_fwd_"), ("delta", "cgqa::fa_delta_"),
                              ("dq", "cgqa::fa_dq_"), ("dkv", "cgqa::fa_dkv_")):
-                if tag in n:
-                    vals.setdefault(key, {})[counter] = v * factor * 1024
+                if tag in n:  # a stage's kernels add up (dK/dV: its split reduction too)
+                    d = vals.setdefault(key, {})
+                    d[counter] = d.get(counter, 0.0) + v * factor * 1024
     for key, d in vals.items():
         out["kernels"][key] = {"fetch_bytes": round(d.get("FETCH_SIZE", 0.0)),
                                "write_bytes": round(d.get("WRITE_SIZE", 0.0)),
@@ -233,12 +234,15 @@ def cpu_baseline(w, bits, budget_s=30.0, mask=None, pairs=None):
             "full_workload_s_extrapolated": round(dt * full / total, 1)}
 
 
-def executed_mfma(w):
+def executed_mfma(w, split=None):
     """Matrix work the kernels issue for workload w, following their tilings
     (diagonal tiles run whole, waves past Lq idle), in units of one
     32x32x16 instruction (32768 FLOP; a 16x16x32 one counts half).  Where
     only 32x32x16 instructions run (D <= 128) it is the count SQ_INSTS_MFMA
-    should read."""
+    should read.  `split`: whether dK/dV runs with a load-balancing
+    workspace (bench.py uses one whenever the library plans a split; at head
+    dim 256 that is the 64-key kernel; a split shares the same iterations
+    between workgroups and changes no count)."""
     cdiv = lambda a, b: -(-a // b)
     D, B, Hq, Hkv, Lq, Lk = w.D, w.B, w.Hq, w.Hkv, w.Lq, w.Lk
     G, off, causal = Hq // Hkv, Lk - Lq, w.causal
@@ -264,9 +268,11 @@ def executed_mfma(w):
         dq += 4 * (4 * NKD + NDB * 4) * cdiv(kv_end(qt * 128 + 128), 64)
     # dK/dV, query tiles of 64: 8 waves x 128 keys up to D = 128; at D = 256
     # 4 waves x 64 keys, or x 32 keys (16 rows each) below 512 64-key workgroups
+    if split is None:
+        split = split_planned(w)
     if D != 256:
         bnk, per_iter = 128, 8 * (2 * NKD + 4 * NDB)
-    elif B * Hkv * cdiv(Lk, 64) >= 512:
+    elif split or B * Hkv * cdiv(Lk, 64) >= 512:
         bnk, per_iter = 64, 4 * (2 * NKD + 4 * NDB)
     else:
         bnk, per_iter = 32, 4 * (2 * (D // 32) + 2 * NDB)
@@ -276,6 +282,20 @@ def executed_mfma(w):
         nq = max(0, cdiv(Lq, 64) - qfirst // 64)
         dkv += G * nq * per_iter
     return {"fwd": fwd * B * Hq, "dq": dq * B * Hq, "dkv": dkv * B * Hkv}
+
+
+def split_planned(w):
+    """Whether bench.py runs this workload's dK/dV with a split workspace: the
+    library's own plan (fa_bwd_workspace_bytes), mirrored here for the
+    counter summaries, which run without a GPU."""
+    cdiv = lambda a, b: -(-a // b)
+    if w.Lq <= 8:
+        return False
+    bnk = 64 if w.D > 128 else 128
+    wgs = w.B * w.Hkv * cdiv(w.Lk, bnk)
+    if w.mask is not None:
+        return cdiv(w.Lq, 64) >= 2
+    return wgs < 512 and cdiv(w.Lq, 64) >= 2
 
 
 def summarize_inst(csv_path, workload):
@@ -292,9 +312,13 @@ def summarize_inst(csv_path, workload):
                     if t in n), None)
         if key is None:
             continue
-        d = rows.setdefault(key, {})
-        d[r["Counter_Name"]] = float(r["Counter_Value"])
-        d["dur_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        # a stage's dispatches add up (dK/dV: its split reduction too); each
+        # dispatch's duration counted once
+        d = rows.setdefault(key, {"dispatches": set()})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if r["Dispatch_Id"] not in d["dispatches"]:
+            d["dispatches"].add(r["Dispatch_Id"])
+            d["dur_ns"] = d.get("dur_ns", 0) + int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     out = {"workload": workload, "kernels": {}}
     for k, d in rows.items():
         e = {"counted_mfma": int(d.get("SQ_INSTS_MFMA", 0)), "analytic_mfma": want[k]}
@@ -377,6 +401,91 @@ def mfma_ceiling(dev, cus):
                           "wave 0 of each workgroup, median over workgroups, in the last of 10 timed launches",
             }
     return res
+
+
+def power_sample(dev, w, secs=3.0):
+    """Board power and shader clock (amd-smi, sampled from a thread) while
+    each attention kernel of workload w runs back to back for `secs`
+    seconds, and while the matrix-core probe's random- and constant-operand
+    loops do: whether a kernel runs at the power limit, and at what clock."""
+    import ctypes
+    import subprocess
+    import threading
+    import numpy as np
+    import torch
+    import causal_gqa_flashattention_amd as fa
+    from causal_gqa_flashattention_amd.build import PKG_DIR, PROBE_LIB_NAME
+    from fa_synth import make_inputs, normal_bf16_bits
+
+    def smi(stop, recs):
+        while not stop.is_set():
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True, text=True)
+            try:
+                gd = json.loads(r.stdout)["gpu_data"][0]
+                recs.append((gd["power"]["socket_power"]["value"],
+                             float(np.mean([v["clk"]["value"] for k, v in gd["clock"].items() if k.startswith("gfx_")]))))
+            except Exception:  # pragma: no cover - a sample the tool could not give
+                pass
+            time.sleep(0.05)
+
+    bits = make_inputs(w, with_grad=True)
+    g = {n: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for n, b in bits.items()}
+    q, k, v, do = g["q"], g["k"], g["v"], g["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    sc, causal = w.softmax_scale, w.causal
+    fa.fa_fwd(q, k, v, o, lse, scale=sc, causal=causal)
+    fa.fa_bwd_delta(o, do, delta)
+    plib = ctypes.CDLL(os.path.join(PKG_DIR, PROBE_LIB_NAME))
+    loop = plib.cgqa_mfma_loop
+    loop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    loop.restype = ctypes.c_double
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    pb = torch.from_numpy(normal_bf16_bits((8192 * 8,), seed=7, sigma=1.0).view("int16")).to(dev)
+    pout = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    calls = {
+        "fwd": lambda: fa.fa_fwd(q, k, v, o, lse, scale=sc, causal=causal),
+        "dq": lambda: fa.fa_bwd_dq(q, k, v, lse, delta, do, dq, scale=sc, causal=causal),
+        "dkv": lambda: fa.fa_bwd_dkv(q, k, v, lse, delta, do, dk, dv, scale=sc, causal=causal),
+    }
+    flops = kernel_work(w, visible_pairs(w.Lq, w.Lk, w.causal))
+    out = {}
+    for mode in ("idle", "fwd", "dq", "dkv", "mfma_random", "mfma_constant"):
+        torch.cuda.synchronize()
+        recs, stop = [], threading.Event()
+        th = threading.Thread(target=smi, args=(stop, recs))
+        th.start()
+        time.sleep(0.3)
+        t0, ms = time.time(), []
+        while time.time() - t0 < secs:
+            if mode == "idle":
+                time.sleep(0.05)
+            elif mode.startswith("mfma"):
+                ms.append(loop(pb.data_ptr(), pout.data_ptr(), cus, 2048, 5, int(mode == "mfma_random")) / 5)
+            else:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(20):
+                    calls[mode]()
+                e1.record()
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1) / 20)
+        stop.set()
+        th.join()
+        rec = {"samples": len(recs)}
+        if recs:
+            W, C = np.array([r[0] for r in recs], dtype=float), np.array([r[1] for r in recs])
+            rec.update({"power_w_median": float(np.median(W)), "power_w_max": float(W.max()),
+                        "gfx_mhz_median": float(np.median(C))})
+        if ms:
+            t = float(np.median(ms))
+            rec["ms"] = round(t, 4)
+            f = 2.0 * 32 * 32 * 16 * 32 * 2048 * cus * 8 if mode.startswith("mfma") else flops[mode]
+            rec["TFLOP/s"] = round(f / (t * 1e-3) / 1e12, 1)
+        out[mode] = rec
+    return out
 
 
 def gemm_canary(dev, n=4096, reps=10):
@@ -506,6 +615,9 @@ def main(argv=None):
                          "counter run against the kernels' analytic MFMA counts")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only run the matrix-core throughput probe and print its JSON")
+    ap.add_argument("--power", action="store_true",
+                    help="only sample board power and clock (amd-smi) while each kernel, and the "
+                         "matrix-core probe, runs back to back; print its JSON")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --profile-pass run into profiles/traffic_<workload>.json")
@@ -533,6 +645,10 @@ def main(argv=None):
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     if args.mfma_ceiling:
         print(json.dumps({"mfma_ceiling": mfma_ceiling(dev, cus)}), flush=True)
+        return 0
+    if args.power:
+        fa.load_library()
+        print(json.dumps({"workload": w.name, "power": power_sample(dev, w)}), flush=True)
         return 0
     fa.load_library()
     bits = make_inputs(w, with_grad=True)

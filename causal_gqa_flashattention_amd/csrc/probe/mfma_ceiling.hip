@@ -184,3 +184,27 @@ extern "C" int cgqa_mfma_clock(const void* bits, float* out, uint64_t* stamps, u
   if (rc == 0) rc = run(mfma_loop<true>, tflops_random, ghz_random);
   return rc;
 }
+
+// One variant of the loops above, `reps` launches back to back (constant
+// operands when random == 0): a sustained load for reading the board's power
+// and clock from outside.  Returns the elapsed milliseconds (HIP events), or
+// a negative HIP error code.
+extern "C" double cgqa_mfma_loop(const void* bits, float* out, int cus, int iters, int reps, int random) {
+  const uint4* src = static_cast<const uint4*>(bits);
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -1.0;
+  (void)hipEventRecord(e0, 0);
+  for (int r = 0; r < reps; ++r) {
+    if (random)
+      hipLaunchKernelGGL(mfma_loop<true>, dim3(cus), dim3(512), 0, 0, src, out, iters, (uint64_t*)nullptr);
+    else
+      hipLaunchKernelGGL(mfma_loop<false>, dim3(cus), dim3(512), 0, 0, src, out, iters, (uint64_t*)nullptr);
+  }
+  (void)hipEventRecord(e1, 0);
+  const hipError_t e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  (void)hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return e == hipSuccess ? (double)ms : -(double)e;
+}
