@@ -15,6 +15,7 @@
 // looping over the group, then over query blocks).  The scale of dS is
 // applied once to the finished dQ and dK.
 #include <climits>
+#include <type_traits>
 
 #include "fa_device.h"
 #include "fa_kernels.h"
@@ -482,10 +483,14 @@ __global__ __launch_bounds__(1024) void fa_dkv_plan_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK / dV
-// One workgroup = 8 wavefronts = 128 keys of one key/value head.  The keys
-// form four 32-key blocks; wavefront w owns block w % 4 for the query rows
-// 32*(w / 4) .. +31 of every query tile, so two wavefronts accumulate partial
+// One workgroup = 2 KB wavefronts = 32 KB keys of one key/value head.  The
+// keys form KB 32-key blocks; wavefront w owns block w % KB for the query rows
+// 32*(w / KB) .. +31 of every query tile, so two wavefronts accumulate partial
 // dK/dV for the same keys over different rows and add them once at the end.
+// KB = 4 (8 wavefronts, one workgroup per CU) by default; KB = 2 at head dim
+// 64, where two 4-wavefront workgroups share a CU: their barriers are
+// independent, so one workgroup's vector work overlaps the other's matrix
+// products (at D = 64 the two take about the same time per tile).
 // K and V sit in LDS for the whole kernel; query tiles of 64 rows of Q and dO
 // stream through LDS (double buffered, direct loads one tile ahead) with
 // their LSE and delta, for every query head of the group in turn.
@@ -495,13 +500,16 @@ __global__ __launch_bounds__(1024) void fa_dkv_plan_kernel(BwdArgs a) {
 //   dS = P * (dP - delta)
 //   dV^T += dO^T P      (A = dO^T by transposed LDS reads, B = P)
 //   dK^T += Q^T dS      (A = Q^T by transposed LDS reads, B = dS)
-template <class E, int D, bool CAUSAL, bool MASKED>
-__global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
-  constexpr int BN = 128;   // keys per workgroup
-  // query rows per tile: 64 (two halves of 32), or 128 at head dim 64, where a
-  // 64-row tile is too little matrix work per barrier; each wave then takes
-  // two 32-row units per tile (under a block mask, one per 64-row mask block)
-  constexpr int BM = D == 64 ? 128 : 64;
+template <class E, int D, bool CAUSAL, bool MASKED, int KB = 4>
+__global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdArgs a) {
+  static_assert(KB == 4 || KB == 2, "four or two key blocks");
+  constexpr int NW = 2 * KB;  // wavefronts
+  constexpr int BN = 32 * KB;  // keys per workgroup
+  // query rows per tile: 64 (two halves of 32), or 128 at head dim 64 with
+  // eight wavefronts, where a 64-row tile is too little matrix work per
+  // barrier; each wave then takes two 32-row units per tile (under a block
+  // mask, one per 64-row mask block)
+  constexpr int BM = D == 64 && KB == 4 ? 128 : 64;
   static_assert(BM % kMaskBlock == 0, "query tiles are whole mask blocks");
   constexpr int P = Tile<D>::P;
   constexpr int NKD = D / 16;
@@ -518,7 +526,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kb = w & 3, qhalf = w >> 2;
+  const int kb = w & (KB - 1), qhalf = w / KB;
   const int G = a.G;
   // key tiles (x chunks) x (batch, key/value head); key tile 0 sees the most
   // queries: heaviest first
@@ -571,9 +579,11 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   const bool w_keys = k0 + 32 * kb < Lk;
   const int nqb = (Lq + kMaskBlock - 1) / kMaskBlock;  // mask rows
 
-  // the 8 waves load as two groups of four: waves 0-3 fill Q, waves 4-7 fill dO
+  // eight waves load as two groups of four: waves 0-3 fill Q, waves 4-7 fill
+  // dO; four waves fill both
   const int wl = w & 3;
-  const TileLoader<D> ld(wl, lane, w < 4 ? a.q.sl : a.dO.sl);
+  const TileLoader<D> ld(wl, lane, NW == 4 || w < 4 ? a.q.sl : a.dO.sl);
+  constexpr int WDELTA = NW == 8 ? 4 : 1;  // the wave that loads the rows' delta
   const bf16_t* const qsrc = a.q.head(b, hk * G);
   const bf16_t* const osrc = a.dO.head(b, hk * G);
   // Q and dO are direct global->LDS loads, and so are the rows' delta
@@ -589,15 +599,20 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     const int hi = n % G, qtile = qtile_of(n);
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;  // LSE and delta rows
     const int qbase = qtile * BM;
-    if (w < 4)
+    if constexpr (NW == 8) {
+      if (w < 4)
+        ld.template load<BM>(qt_lds, qsrc + hi * a.q.sh, qbase, Lq, wl);
+      else
+        ld.template load<BM>(dt_lds, osrc + hi * a.dO.sh, qbase, Lq, wl);
+    } else {
       ld.template load<BM>(qt_lds, qsrc + hi * a.q.sh, qbase, Lq, wl);
-    else
-      ld.template load<BM>(dt_lds, osrc + hi * a.dO.sh, qbase, Lq, wl);
+      TileLoader<D>(wl, lane, a.dO.sl).template load<BM>(dt_lds, osrc + hi * a.dO.sh, qbase, Lq, wl);
+    }
     // 64 rows per load; a half past Lq repeats row Lq - 1
 #pragma unroll
     for (int hr = 0; hr < BM / 64; ++hr) {
       if (w == 0) lse_next[hr] = a.lse[qh + min(qbase + 64 * hr + lane, Lq - 1)];
-      if (w == 4) load_row_stat(&stat[n & 1][1][64 * hr], a.delta + qh, min(qbase + 64 * hr, Lq - 1), Lq, lane);
+      if (w == WDELTA) load_row_stat(&stat[n & 1][1][64 * hr], a.delta + qh, min(qbase + 64 * hr, Lq - 1), Lq, lane);
     }
   };
   auto publish_lse = [&](int n) {
@@ -607,9 +622,12 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     }
   };
   // K and V of this key tile, once (rows past Lk repeat the last key)
-  {
+  if constexpr (NW == 8) {
     const TileLoader<D> lkv(wl, lane, w < 4 ? a.k.sl : a.v.sl);
     lkv.template load<BN>(w < 4 ? sK : sV, w < 4 ? a.k.head(b, hk) : a.v.head(b, hk), k0, Lk, wl);
+  } else {
+    TileLoader<D>(wl, lane, a.k.sl).template load<BN>(sK, a.k.head(b, hk), k0, Lk, wl);
+    TileLoader<D>(wl, lane, a.v.sl).template load<BN>(sV, a.v.head(b, hk), k0, Lk, wl);
   }
   if (niter > 0) {
     issue(0);
@@ -635,7 +653,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     constexpr int NCH = BN * P * 2 / 16;  // 16-byte chunks of the V tile
     uint4* vv = reinterpret_cast<uint4*>(sV);
 #pragma unroll
-    for (int i = tid; i < NCH; i += 512) {
+    for (int i = tid; i < NCH; i += 64 * NW) {
       uint4 x = vv[i];
       x.x ^= 0x80008000u;
       x.y ^= 0x80008000u;
@@ -724,21 +742,22 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  // ---- add the two row halves: waves 4-7 hand their partials to waves 0-3
-  // through LDS (the tile buffers are free now), lane-contiguous per register
+  // ---- add the two row halves: waves KB.. hand their partials to waves
+  // 0..KB-1 through LDS (the tile buffers are free now), lane-contiguous per
+  // register
   float* red = reinterpret_cast<float*>(smem);
-  static_assert((2 * BUF + 2 * BN * P) * 2 >= 4 * NDB * 16 * 64 * 4, "reduction buffer too small");
+  static_assert((2 * BUF + 2 * BN * P) * 2 >= KB * NDB * 16 * 64 * 4, "reduction buffer too small");
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     f32x16* acc = pass == 0 ? dk : dv;
-    if (w >= 4) {
+    if (w >= KB) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) red[((kb * NDB + db) * 16 + i) * 64 + lane] = acc[db][i];
     }
     __syncthreads();
-    if (w < 4) {
+    if (w < KB) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -748,7 +767,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
   }
 
   if (sr.part != nullptr) {
-    if (w < 4) {
+    if (w < KB) {
       float* pk = sr.part + (32 * kb + lr) * D;
       float* pv = pk + BN * D;
 #pragma unroll
@@ -762,7 +781,7 @@ __global__ __launch_bounds__(512, 1) void fa_dkv_kernel(BwdArgs a) {
               make_float4(cv[4 * q4], cv[4 * q4 + 1], cv[4 * q4 + 2], cv[4 * q4 + 3]);
         }
     }
-  } else if (w < 4 && key_ok) {
+  } else if (w < KB && key_ok) {
     bf16_t* dkp = a.dk.head(b, hk) + (int64_t)krow * a.dk.sl;
     bf16_t* dvp = a.dv.head(b, hk) + (int64_t)krow * a.dv.sl;
     const float sc = -a.scale;  // the accumulators hold -dK / scale
@@ -1286,7 +1305,9 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
     a.plan = nullptr;
   }
   const bool k32 = D > 128 && !split && (int64_t)a.B * a.Hkv * ((a.Lk + 63) / 64) < 512;
-  const int bnk = D > 128 ? (k32 ? 32 : 64) : 128;
+  // head dim 64 without a split: 64-key workgroups of four wavefronts, two per CU
+  const bool kb2 = D == 64 && !split;
+  const int bnk = D > 128 ? (k32 ? 32 : 64) : kb2 ? 64 : 128;
   a.nkt = (a.Lk + bnk - 1) / bnk;
   // the dK accumulators hold dK / scale, negated in fa_dkv_kernel (V negated)
   a.ksc = D > 128 ? a.scale : -a.scale;
@@ -1301,7 +1322,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
   const int ndkv = !(which & 2) ? 0 : !split ? nh * a.nkt : masked ? a.nextra + nh * a.nkt : nh * a.nkt * a.nsplit;
   auto dq = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(ndq), dim3(256), dq_list, stream, a); };
   auto dkv = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(ndkv), dim3(D > 128 ? 256 : 512), dkv_list, stream, a);
+    hipLaunchKernelGGL(kern, dim3(ndkv), dim3(D > 128 || kb2 ? 256 : 512), dkv_list, stream, a);
   };
   if (split && masked && ndkv > 0) {
     constexpr int BMK = D == 64 ? 128 : 64;  // the dK/dV kernel's query tile
@@ -1329,10 +1350,19 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
       else
         masked ? dkv(fa_dkv_reg_kernel<E, D, false, true>) : dkv(fa_dkv_reg_kernel<E, D, false, false>);
     } else {
-      if (causal)
-        masked ? dkv(fa_dkv_kernel<E, D, true, true>) : dkv(fa_dkv_kernel<E, D, true, false>);
-      else
-        masked ? dkv(fa_dkv_kernel<E, D, false, true>) : dkv(fa_dkv_kernel<E, D, false, false>);
+      auto go = [&](auto kb) {
+        constexpr int KB = decltype(kb)::value;
+        if (causal)
+          masked ? dkv(fa_dkv_kernel<E, D, true, true, KB>) : dkv(fa_dkv_kernel<E, D, true, false, KB>);
+        else
+          masked ? dkv(fa_dkv_kernel<E, D, false, true, KB>) : dkv(fa_dkv_kernel<E, D, false, false, KB>);
+      };
+      if constexpr (D == 64) {
+        if (kb2) go(std::integral_constant<int, 2>{});
+        else go(std::integral_constant<int, 4>{});
+      } else {
+        go(std::integral_constant<int, 4>{});
+      }
     }
     if (split)
       hipLaunchKernelGGL((fa_dkv_reduce_kernel<E, D, dkv_split_keys(D)>),
