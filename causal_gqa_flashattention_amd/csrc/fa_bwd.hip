@@ -571,10 +571,6 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
   SplitRange sr;
   if (!split_range<MASKED, BN, D>(a, wk, nql, tid, sr)) return;  // (uniform: nql is)
   const int niter = G * sr.cnt;
-  auto qtile_of = [&](int n) {
-    const int i = sr.lo + sr.step * (n / G);
-    return MASKED ? __builtin_amdgcn_readfirstlane(qlist[i]) : nqt - 1 - i;
-  };
   const int wkb = (k0 + 32 * kb) / kMaskBlock;  // mask column of this wavefront's keys
   const bool w_keys = k0 + 32 * kb < Lk;
   const int nqb = (Lq + kMaskBlock - 1) / kMaskBlock;  // mask rows
@@ -583,36 +579,62 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
   // dO; four waves fill both
   const int wl = w & 3;
   const TileLoader<D> ld(wl, lane, NW == 4 || w < 4 ? a.q.sl : a.dO.sl);
+  const TileLoader<D> ldo(wl, lane, a.dO.sl);  // (four waves: their dO)
   constexpr int WDELTA = NW == 8 ? 4 : 1;  // the wave that loads the rows' delta
-  const bf16_t* const qsrc = a.q.head(b, hk * G);
-  const bf16_t* const osrc = a.dO.head(b, hk * G);
   // Q and dO are direct global->LDS loads, and so are the rows' delta
-  // (wave 4), rows past Lq repeating the last row.  The rows' LSE goes to
-  // LDS already multiplied by -log2 e, so that a score's probability is one
-  // fma and one exp2: wave 0 loads it into a register with the tile and
+  // (wave WDELTA), rows past Lq repeating the last row.  The rows' LSE goes
+  // to LDS already multiplied by -log2 e, so that a score's probability is
+  // one fma and one exp2: wave 0 loads it into a register with the tile and
   // writes it scaled before the barrier that ends the iteration
   // (publish_lse), when the buffer's previous readers are done.
+  // The next tile to load is kept as running state (query head nx_hi of the
+  // group, list entry nx_i, the head's Q / dO / LSE / delta bases), advanced
+  // by additions: no division by the group size and no 64-bit products per
+  // tile, and LDS destinations as plain byte addresses.
   float lse_next[BM / 64];
-  auto issue = [&](int n) {
-    bf16_t* qt_lds = smem + (n & 1) * BUF;
-    bf16_t* dt_lds = qt_lds + BM * P;
-    const int hi = n % G, qtile = qtile_of(n);
-    const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;  // LSE and delta rows
+  const uint32_t smem_a = lds_addr(smem), stat_a = lds_addr(&stat[0][0][0]);
+  const int64_t srow0 = (int64_t)(b * a.Hq + hk * G) * Lq;  // LSE / delta row of the group's first head
+  const bf16_t* nx_q = a.q.head(b, hk * G);
+  const bf16_t* nx_o = a.dO.head(b, hk * G);
+  const float* nx_l = a.lse + srow0;
+  const float* nx_d = a.delta + srow0;
+  int nx_hi = 0, nx_i = sr.lo, q0_nx = 0;
+  auto issue = [&](int n) {  // tile n (the next in order)
+    const uint32_t qt_a = smem_a + (uint32_t)(n & 1) * (BUF * 2);
+    const uint32_t dt_a = qt_a + BM * P * 2;
+    const int qtile = MASKED ? __builtin_amdgcn_readfirstlane(qlist[nx_i]) : nqt - 1 - nx_i;
     const int qbase = qtile * BM;
+    q0_nx = qbase;
     if constexpr (NW == 8) {
       if (w < 4)
-        ld.template load<BM>(qt_lds, qsrc + hi * a.q.sh, qbase, Lq, wl);
+        ld.template load_at<BM>(qt_a, nx_q, qbase, Lq, wl);
       else
-        ld.template load<BM>(dt_lds, osrc + hi * a.dO.sh, qbase, Lq, wl);
+        ld.template load_at<BM>(dt_a, nx_o, qbase, Lq, wl);
     } else {
-      ld.template load<BM>(qt_lds, qsrc + hi * a.q.sh, qbase, Lq, wl);
-      TileLoader<D>(wl, lane, a.dO.sl).template load<BM>(dt_lds, osrc + hi * a.dO.sh, qbase, Lq, wl);
+      ld.template load_at<BM>(qt_a, nx_q, qbase, Lq, wl);
+      ldo.template load_at<BM>(dt_a, nx_o, qbase, Lq, wl);
     }
     // 64 rows per load; a half past Lq repeats row Lq - 1
 #pragma unroll
     for (int hr = 0; hr < BM / 64; ++hr) {
-      if (w == 0) lse_next[hr] = a.lse[qh + min(qbase + 64 * hr + lane, Lq - 1)];
-      if (w == WDELTA) load_row_stat(&stat[n & 1][1][64 * hr], a.delta + qh, min(qbase + 64 * hr, Lq - 1), Lq, lane);
+      if (w == 0) lse_next[hr] = nx_l[min(qbase + 64 * hr + lane, Lq - 1)];
+      if (w == WDELTA)
+        load_row_stat_at(stat_a + (uint32_t)(((n & 1) * 2 + 1) * BM + 64 * hr) * 4u, nx_d, min(qbase + 64 * hr, Lq - 1),
+                         Lq, lane);
+    }
+    // advance: heads innermost, then the list
+    if (++nx_hi < G) {
+      nx_q += a.q.sh;
+      nx_o += a.dO.sh;
+      nx_l += Lq;
+      nx_d += Lq;
+    } else {
+      nx_hi = 0;
+      nx_i += sr.step;
+      nx_q -= (int64_t)(G - 1) * a.q.sh;
+      nx_o -= (int64_t)(G - 1) * a.dO.sh;
+      nx_l -= (int64_t)(G - 1) * Lq;
+      nx_d -= (int64_t)(G - 1) * Lq;
     }
   };
   auto publish_lse = [&](int n) {
@@ -629,9 +651,11 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
     TileLoader<D>(wl, lane, a.k.sl).template load<BN>(sK, a.k.head(b, hk), k0, Lk, wl);
     TileLoader<D>(wl, lane, a.v.sl).template load<BN>(sV, a.v.head(b, hk), k0, Lk, wl);
   }
+  int q0_cur = 0;
   if (niter > 0) {
     issue(0);
     publish_lse(0);
+    q0_cur = q0_nx;
   }
 
   TileReaderX<D> rq(lane);  // Q and dO tiles: offsets flip with the buffer
@@ -669,7 +693,7 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
   for (int kd = 0; kd < NKD; ++kd) kf[kd] = rk.row16(sK, 32 * kb, kd);
   for (int n = 0; n < niter; ++n) {
     const int buf = n & 1;
-    const int q0 = qtile_of(n) * BM;
+    const int q0 = q0_cur;
     if (n + 1 < niter) issue(n + 1);
     const bf16_t* Qs = smem;            // + buf * BUF through rq's flipped offsets
     const bf16_t* Ds = smem + BM * P;
@@ -738,6 +762,7 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
 
     rq.flip(BUF);
     if (n + 1 < niter) publish_lse(n + 1);
+    q0_cur = q0_nx;
     wait_vmem();
     __syncthreads();
   }

@@ -410,6 +410,29 @@ struct TileLoader {
     }
   }
 
+  // The same as load() with the tile given by its LDS byte address (from
+  // lds_addr): no generic-pointer conversion per load, which the compiler
+  // otherwise rebuilds from the shared aperture with a null check each time.
+  template <int ROWS>
+  __device__ __forceinline__ void load_at(uint32_t tile, const bf16_t* g, int row0, int nrows, int w) const {
+    constexpr int ROUNDS = ROWS * PC / 256;
+    static_assert(ROWS * PC % 256 == 0, "tile must split evenly over four waves");
+    const bf16_t* const g0 = g + (int64_t)row0 * rs;  // wave-uniform
+    const uint32_t t0 = tile + (uint32_t)w * 1024u;
+    if (row0 + ROWS <= nrows) {
+#pragma unroll
+      for (int i = 0; i < ROUNDS; ++i)
+        lds_dma16_at(t0 + 4096u * i, g0 + i * rstep, (uint32_t)(lro + src_off(4 * RW * i + rl)) * 2u);
+    } else {
+      const int last = nrows - 1 - row0;  // last tile row that exists
+#pragma unroll
+      for (int i = 0; i < ROUNDS; ++i) {
+        const int r = 4 * RW * i + rl;
+        lds_dma16_at(t0 + 4096u * i, g0, (uint32_t)(min(r, last) * rs + src_off(r)) * 2u);
+      }
+    }
+  }
+
   // One global_load_lds_dwordx4: lane l's 16 bytes at sbase + voff go to LDS
   // address dst + 16*l (dst and sbase wave-uniform).  Issued as inline
   // assembly so that the compiler does not treat the load as a write to LDS
@@ -421,7 +444,18 @@ struct TileLoader {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :: "s"(m0v), "v"(voff), "s"(sbase) : "memory");
   }
+  // the same with the LDS byte address itself (wave-uniform)
+  __device__ __forceinline__ static void lds_dma16_at(uint32_t dst, const bf16_t* sbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(dst), "v"(voff), "s"(sbase) : "memory");
+  }
 };
+
+// LDS byte address of a pointer into a __shared__ array (the value an LDS
+// instruction or the DMA's m0 takes).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const LDS_AS void*)(p));
+}
 
 // Direct global->LDS copy of a ROWS x D tile by ONE wavefront, into the
 // layout TileLoader<D> produces with four: 1 KiB block b holds tile rows
@@ -482,6 +516,11 @@ __device__ __forceinline__ void lds_dma4(void* dst, const void* sbase, uint32_t 
 // last row (row0 < nrows).  Waited for like the tile loads.
 __device__ __forceinline__ void load_row_stat(float* dst, const float* src, int row0, int nrows, int lane) {
   lds_dma4(dst, src + row0, (uint32_t)min(lane, nrows - 1 - row0) * 4u);
+}
+// the same with dst given by its LDS byte address
+__device__ __forceinline__ void load_row_stat_at(uint32_t dst, const float* src, int row0, int nrows, int lane) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(dst), "v"((uint32_t)min(lane, nrows - 1 - row0) * 4u), "s"(src + row0) : "memory");
 }
 
 // Scheduling pattern for a block of NM MFMAs that each consume RPM LDS reads:
