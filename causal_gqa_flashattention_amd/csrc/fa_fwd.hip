@@ -323,6 +323,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
   // buffer x & 3 to (x + 1) & 3 is an XOR of the offsets with
   // (x odd ? 3 : 1) * TILE
   TileReaderX<D> rd(lane);
+  rd.shift_tr(4 * TILE * 2);  // the transposed reads (V) are given smem, not sV
   const float c2 = a.scale_log2;
   float m_run = -INFINITY;
   float l_run = 0.f;
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db] = E::mma(rd.trA(sV, 16 * ks, db), pf[ks], acc[db]);
+        for (int db = 0; db < NDB; ++db) acc[db] = E::mma(rd.trA(smem, 16 * ks, db), pf[ks], acc[db]);
       // the transposed reads run kLookahead ahead of the products (the K
       // fragments' registers are free by now)
       constexpr int NM = NKS * NDB, NR = 2 * NM, LA = kLookahead < NR ? kLookahead : NR;
