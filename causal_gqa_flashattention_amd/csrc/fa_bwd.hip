@@ -659,6 +659,12 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
   }
 
   TileReaderX<D> rq(lane);  // Q and dO tiles: offsets flip with the buffer
+  // ... and, at head dim >= 96 without a mask, carry this wave's row half, so
+  // that every read's row offset is a constant (the instruction's immediate,
+  // not a vector add per address).  (Elsewhere the extra live offsets cost
+  // occupancy or a spill.)
+  constexpr bool FOLD_ROWS = !MASKED && D >= 96;
+  if constexpr (FOLD_ROWS) rq.shift(2 * 32 * qhalf * P);
   TileReaderX<D> rk(lane);  // K and V tiles (resident)
   const float c2 = a.scale_log2;
   f32x16 dk[NDB], dv[NDB];
@@ -701,6 +707,7 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
 #pragma unroll
     for (int u = 0; u < BM / 64; ++u) {
     const int r0 = 32 * qhalf + 64 * u;  // this wave's rows within the tile
+    const int rr = FOLD_ROWS ? 64 * u : r0;  // the same as the reads take it
     // under a block mask, a unit whose 64-row block this wavefront's keys do
     // not see is skipped (blocks past the mask's last row are computed, to
     // zero contributions, as without a mask)
@@ -721,8 +728,8 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
     prio_hi();
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
-      s = E::mma(rq.row16(Qs, r0, kd), kf[kd], s);
-      dp = E::mma(rq.row16(Ds, r0, kd), rk.row16(sV, 32 * kb, kd), dp);
+      s = E::mma(rq.row16(Qs, rr, kd), kf[kd], s);
+      dp = E::mma(rq.row16(Ds, rr, kd), rk.row16(sV, 32 * kb, kd), dp);
     }
     // (no read-ahead pattern here: with eight wavefronts in step it only
     // bunches the LDS reads, measured slower)
@@ -753,8 +760,8 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        dv[db] = E::mma(rq.trA(Ds, r0 + 16 * h, db), pf[h], dv[db]);
-        dk[db] = E::mma(rq.trA(Qs, r0 + 16 * h, db), ds[h], dk[db]);
+        dv[db] = E::mma(rq.trA(Ds, rr + 16 * h, db), pf[h], dv[db]);
+        dk[db] = E::mma(rq.trA(Qs, rr + 16 * h, db), ds[h], dk[db]);
       }
     prio_lo();
     }

@@ -288,6 +288,10 @@ struct TileReaderX {
   // 64 KB or more into LDS the compiler otherwise adds the base to every
   // read's address.
   __device__ __forceinline__ void shift_tr(int bytes) { tr0 += bytes; }
+  __device__ __forceinline__ void shift(int bytes) {
+    ra0 += bytes;
+    tr0 += bytes;
+  }
   __device__ __forceinline__ bf16x8 row16(const bf16_t* tile, int r0, int kd) const {
     const char* p = reinterpret_cast<const char*>(tile + r0 * P + 128 * (kd / NRA)) + (ra0 ^ (32 * (kd % NRA)));
     return lds_read16(reinterpret_cast<const bf16_t*>(p));
