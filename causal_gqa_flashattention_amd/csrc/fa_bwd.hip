@@ -906,20 +906,28 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   const TileLoader<D> ldq(w, lane, a.q.sl), ldo(w, lane, a.dO.sl);
   const bf16_t* const qsrc = a.q.head(b, hk * G);
   const bf16_t* const osrc = a.dO.head(b, hk * G);
-  // Q, dO and the rows' LSE (wave 0) and delta (wave 1) by direct loads
+  // Q, dO and the rows' delta (wave 1) by direct loads.  The rows' LSE goes
+  // to LDS already multiplied by -log2 e (one fma and one exp2 per score):
+  // wave 0 loads it into a register with the tile and writes it scaled before
+  // the barrier that ends the iteration (publish_lse).
+  float lse_next = 0.f;
   auto issue = [&](int n) {
     bf16_t* qt_lds = smem + (n & 1) * BUF;
     const int hi = n % G, qtile = qtile_of(n);
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
     const int qbase = qtile * BM;
-    // stats first: anything the compiler reloads for them then waits on
-    // nothing but its own load
-    if (w == 0) load_row_stat(&stat[n & 1][0][0], a.lse + qh, qbase, Lq, lane);
     if (w == 1) load_row_stat(&stat[n & 1][1][0], a.delta + qh, qbase, Lq, lane);
     ldq.template load<BM>(qt_lds, qsrc + hi * a.q.sh, qbase, Lq, w);
     ldo.template load<BM>(qt_lds + BM * P, osrc + hi * a.dO.sh, qbase, Lq, w);
+    if (w == 0) lse_next = a.lse[qh + min(qbase + lane, Lq - 1)];
   };
-  if (niter > 0) issue(0);
+  auto publish_lse = [&](int n) {
+    if (w == 0) stat[n & 1][0][lane] = lse_next * -kLog2e;
+  };
+  if (niter > 0) {
+    issue(0);
+    publish_lse(0);
+  }
 
   bf16x8 kf[NKD], vf[NKD];
   {
@@ -927,11 +935,21 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
       kf[kd] = as_bf16x8(ldg16(a.k.head(b, hk) + (int64_t)kr * a.k.sl + 16 * kd + 8 * lg));
-      vf[kd] = as_bf16x8(ldg16(a.v.head(b, hk) + (int64_t)kr * a.v.sl + 16 * kd + 8 * lg));
+      // V with its sign bits flipped (bf16 and half alike): the dP products,
+      // started from delta, then give delta - dP, and P times that is -dS in
+      // one multiply; dK takes the sign back with the scale at the end
+      uint4 x = ldg16(a.v.head(b, hk) + (int64_t)kr * a.v.sl + 16 * kd + 8 * lg);
+      x.x ^= 0x80008000u;
+      x.y ^= 0x80008000u;
+      x.z ^= 0x80008000u;
+      x.w ^= 0x80008000u;
+      vf[kd] = as_bf16x8(x);
     }
   }
 
   TileReader<D> rd(lane);
+  // the reads' offsets carry this wave's row half: row offsets are immediates
+  rd.shift(2 * r0 * P);
   const float c2 = a.scale_log2;
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -949,17 +967,25 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
     const bf16_t* Qs = smem;  // + buf * BUF through the reader's flipped offsets
     const bf16_t* Ds = smem + BM * P;
 
-    f32x16 s = zero16(), dp = zero16();
+    // dp starts from each row's delta (C layout: register 4 i4 + e holds
+    // row 8 i4 + 4 lg + e); with V negated it ends as delta - dP
+    f32x16 s = zero16(), dp;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][r0 + 8 * i4 + 4 * lg]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = d4[e];
+    }
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
-      s = E::mma(rd.row16(Qs, r0, kd), kf[kd], s);
-      dp = E::mma(rd.row16(Ds, r0, kd), vf[kd], dp);
+      s = E::mma(rd.row16(Qs, 0, kd), kf[kd], s);
+      dp = E::mma(rd.row16(Ds, 0, kd), vf[kd], dp);
     }
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][r0 + 8 * i4 + 4 * lg]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[buf][0][r0 + 8 * i4 + 4 * lg]);  // -LSE log2 e
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fast_exp2(fmaf(s[4 * i4 + e], c2, l4[e] * -kLog2e));
+      for (int e = 0; e < 4; ++e) s[4 * i4 + e] = fast_exp2(fmaf(s[4 * i4 + e], c2, l4[e]));
     }
     // tiles that cross the diagonal or hold rows past Lq
     if ((CAUSAL && k0 + BN - 1 > q0 + off) || q0 + BM > Lq) {
@@ -969,23 +995,21 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = (crow(i, 0) >= thr && crow(i, 0) < rlim) ? s[i] : 0.f;
     }
+    // -dS = P (delta - dP)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[buf][1][r0 + 8 * i4 + 4 * lg]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = s[4 * i4 + e] * (dp[4 * i4 + e] - d4[e]);
-    }
+    for (int i = 0; i < 16; ++i) dp[i] = s[i] * dp[i];
     const bf16x8 pf0 = E::pack8(s, 0), pf1 = E::pack8(s, 1);
     const bf16x8 ds0 = E::pack8(dp, 0), ds1 = E::pack8(dp, 1);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      dv[db] = E::mma(rd.trA(Ds, r0, db), pf0, dv[db]);
-      dv[db] = E::mma(rd.trA(Ds, r0 + 16, db), pf1, dv[db]);
-      dk[db] = E::mma(rd.trA(Qs, r0, db), ds0, dk[db]);
-      dk[db] = E::mma(rd.trA(Qs, r0 + 16, db), ds1, dk[db]);
+      dv[db] = E::mma(rd.trA(Ds, 0, db), pf0, dv[db]);
+      dv[db] = E::mma(rd.trA(Ds, 16, db), pf1, dv[db]);
+      dk[db] = E::mma(rd.trA(Qs, 0, db), ds0, dk[db]);
+      dk[db] = E::mma(rd.trA(Qs, 16, db), ds1, dk[db]);
     }
 
     rd.flip(BUF);
+    if (n + 1 < niter) publish_lse(n + 1);
     wait_vmem();
     __syncthreads();
   }
@@ -1031,7 +1055,7 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   } else if (qhalf == 0 && key_ok) {
     bf16_t* dkp = a.dk.head(b, hk) + (int64_t)krow * a.dk.sl;
     bf16_t* dvp = a.dv.head(b, hk) + (int64_t)krow * a.dv.sl;
-    const float sc = a.scale;
+    const float sc = -a.scale;  // the accumulators hold -dK / scale
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1341,8 +1365,9 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
   const bool kb2 = D == 64 && !split;
   const int bnk = D > 128 ? (k32 ? 32 : 64) : kb2 ? 64 : 128;
   a.nkt = (a.Lk + bnk - 1) / bnk;
-  // the dK accumulators hold dK / scale, negated in fa_dkv_kernel (V negated)
-  a.ksc = D > 128 ? a.scale : -a.scale;
+  // the dK accumulators of the kernels that write partials hold -dK / scale
+  // (V negated)
+  a.ksc = -a.scale;
   const bool masked = a.mask != nullptr;
   // dynamic LDS under a block mask: each workgroup's tile list and its count
   const size_t dq_list = masked ? ((size_t)(a.Lk + BN_Q - 1) / BN_Q + 1) * sizeof(int) : 0;

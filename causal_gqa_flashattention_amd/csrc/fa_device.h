@@ -244,6 +244,17 @@ struct TileReader {
 #pragma unroll
       for (int dm = 0; dm < NTR; ++dm) tr[h][dm] ^= 2 * half;
   }
+  // Carry a fixed row offset (bytes, a multiple of 32 P, below the flip's
+  // half) in every offset, so that reads take a constant row offset: an
+  // instruction immediate instead of a vector add per address.
+  __device__ __forceinline__ void shift(int bytes) {
+#pragma unroll
+    for (int j = 0; j < NRA; ++j) ra[j] += bytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dm = 0; dm < NTR; ++dm) tr[h][dm] += bytes;
+  }
   __device__ __forceinline__ bf16x8 row16(const bf16_t* tile, int r0, int kd) const {
     const char* p = reinterpret_cast<const char*>(tile + r0 * P + 128 * (kd / NRA)) + ra[kd % NRA];
     return lds_read16(reinterpret_cast<const bf16_t*>(p));
