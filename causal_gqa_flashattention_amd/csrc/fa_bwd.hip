@@ -126,11 +126,12 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_dq_kernel(BwdArgs 
   const bool w_rows = q0 + 32 * w < Lq;
 
   const TileLoader<D> ldk(w, lane, ks), ldv(w, lane, vs);
+  const uint32_t smem_a = lds_addr(smem);  // (byte addresses: no pointer conversion per load)
   auto issue = [&](int ti) {
     const int j = tile(ti);
-    bf16_t* buf = smem + (ti & 1) * BUF;
-    ldk.template load<BN>(buf, kp, j * BN, Lk, w);
-    ldv.template load<BN>(buf + BN * P, vp, j * BN, Lk, w);
+    const uint32_t buf = smem_a + (uint32_t)(ti & 1) * (BUF * 2);
+    ldk.template load_at<BN>(buf, kp, j * BN, Lk, w);
+    ldv.template load_at<BN>(buf + BN * P * 2, vp, j * BN, Lk, w);
   };
   if (nt > 0) issue(0);
 
@@ -911,14 +912,15 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_reg_kernel(BwdArgs a) {
   // wave 0 loads it into a register with the tile and writes it scaled before
   // the barrier that ends the iteration (publish_lse).
   float lse_next = 0.f;
+  const uint32_t smem_a = lds_addr(smem);  // (byte addresses: no pointer conversion per load)
   auto issue = [&](int n) {
-    bf16_t* qt_lds = smem + (n & 1) * BUF;
+    const uint32_t qt_a = smem_a + (uint32_t)(n & 1) * (BUF * 2);
     const int hi = n % G, qtile = qtile_of(n);
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
     const int qbase = qtile * BM;
     if (w == 1) load_row_stat(&stat[n & 1][1][0], a.delta + qh, qbase, Lq, lane);
-    ldq.template load<BM>(qt_lds, qsrc + hi * a.q.sh, qbase, Lq, w);
-    ldo.template load<BM>(qt_lds + BM * P, osrc + hi * a.dO.sh, qbase, Lq, w);
+    ldq.template load_at<BM>(qt_a, qsrc + hi * a.q.sh, qbase, Lq, w);
+    ldo.template load_at<BM>(qt_a + BM * P * 2, osrc + hi * a.dO.sh, qbase, Lq, w);
     if (w == 0) lse_next = a.lse[qh + min(qbase + lane, Lq - 1)];
   };
   auto publish_lse = [&](int n) {
@@ -1141,15 +1143,16 @@ __global__ __launch_bounds__(256, 1) void fa_dkv_k32_kernel(BwdArgs a) {
   const TileLoader<D> ldq(w, lane, a.q.sl), ldo(w, lane, a.dO.sl);
   const bf16_t* const qsrc = a.q.head(b, hk * G);
   const bf16_t* const osrc = a.dO.head(b, hk * G);
+  const uint32_t smem_a = lds_addr(smem);  // (byte addresses: no pointer conversion per load)
   auto issue = [&](int n) {
-    bf16_t* qt_lds = smem + (n & 1) * BUF;
+    const uint32_t qt_a = smem_a + (uint32_t)(n & 1) * (BUF * 2);
     const int hi = n % G, qtile = qtile_of(n);
     const int64_t qh = (int64_t)(b * a.Hq + hk * G + hi) * Lq;
     const int qbase = qtile * BM;
     if (w == 0) load_row_stat(&stat[n & 1][0][0], a.lse + qh, qbase, Lq, lane);
     if (w == 1) load_row_stat(&stat[n & 1][1][0], a.delta + qh, qbase, Lq, lane);
-    ldq.template load<BM>(qt_lds, qsrc + hi * a.q.sh, qbase, Lq, w);
-    ldo.template load<BM>(qt_lds + BM * P, osrc + hi * a.dO.sh, qbase, Lq, w);
+    ldq.template load_at<BM>(qt_a, qsrc + hi * a.q.sh, qbase, Lq, w);
+    ldo.template load_at<BM>(qt_a + BM * P * 2, osrc + hi * a.dO.sh, qbase, Lq, w);
   };
   if (niter > 0) issue(0);
 

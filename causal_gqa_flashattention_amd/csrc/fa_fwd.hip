@@ -100,11 +100,12 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
   const bool w_rows = q0 + 32 * w < Lq;
 
   const TileLoader<D> ldk(w, lane, ks), ldv(w, lane, vs);
+  const uint32_t smem_a = lds_addr(smem);  // (byte addresses: no pointer conversion per load)
   auto issue = [&](int ti) {
     const int j = tile(ti);
-    bf16_t* buf = smem + (ti & 1) * BUF;
-    ldk.template load<BN>(buf, kp, j * BN, Lk, w);
-    ldv.template load<BN>(buf + BN * P, vp, j * BN, Lk, w);
+    const uint32_t buf = smem_a + (uint32_t)(ti & 1) * (BUF * 2);
+    ldk.template load_at<BN>(buf, kp, j * BN, Lk, w);
+    ldv.template load_at<BN>(buf + BN * P * 2, vp, j * BN, Lk, w);
   };
   if (nt > 0) issue(0);
 
@@ -337,13 +338,15 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(FwdArgs a) {
 
   // loads issued by matrix step x: K of tile x + 2 (waves 0-3) or V of
   // tile x + 1 (waves 4-7); returns whether this wavefront issued any
+  // (LDS destinations as byte addresses: no generic-pointer conversion per load)
+  const uint32_t sK_a = lds_addr(sK), sV_a = lds_addr(sV);
   auto loads = [&](int x) -> bool {
     if (w < 4) {
       if (x + 2 >= nt) return false;
-      ld.template load<BN>(sK + ((x + 2) & 3) * TILE, kp, (x + 2) * BN, Lk, w);
+      ld.template load_at<BN>(sK_a + (uint32_t)((x + 2) & 3) * (TILE * 2), kp, (x + 2) * BN, Lk, w);
     } else {
       if (x + 1 >= nt) return false;
-      ld.template load<BN>(sV + ((x + 1) & 3) * TILE, vp, (x + 1) * BN, Lk, w & 3);
+      ld.template load_at<BN>(sV_a + (uint32_t)((x + 1) & 3) * (TILE * 2), vp, (x + 1) * BN, Lk, w & 3);
     }
     return true;
   };
