@@ -489,18 +489,19 @@ __global__ __launch_bounds__(1024) void fa_dkv_plan_kernel(BwdArgs a) {
 // 32*(w / KB) .. +31 of every query tile, so two wavefronts accumulate partial
 // dK/dV for the same keys over different rows and add them once at the end.
 // KB = 4 (8 wavefronts, one workgroup per CU) by default; KB = 2 at head dim
-// 64, where two 4-wavefront workgroups share a CU: their barriers are
-// independent, so one workgroup's vector work overlaps the other's matrix
-// products (at D = 64 the two take about the same time per tile).
-// K and V sit in LDS for the whole kernel; query tiles of 64 rows of Q and dO
-// stream through LDS (double buffered, direct loads one tile ahead) with
-// their LSE and delta, for every query head of the group in turn.
+// 64 without a split, where three 4-wavefront workgroups share a CU: their
+// barriers are independent, so one workgroup's vector work can overlap
+// another's matrix products.
+// K and V sit in LDS for the whole kernel (each wave's K operand fragments
+// also in registers); query tiles of Q and dO stream through LDS (double
+// buffered, direct loads one tile ahead) with their LSE and delta, for every
+// query head of the group in turn.
 // Per query tile and wavefront (32 rows x 32 keys):
-//   S  = Q K^T          (A = Q rows, B = K rows, both from LDS)
-//   dP = dO V^T         (A = dO rows, B = V rows)
-//   dS = P * (dP - delta)
+//   S  = Q K^T          (A = Q rows from LDS, B = K rows in registers)
+//   dP = dO V^T         (A = dO rows, B = V rows, from LDS)
+//   dS = P * (dP - delta), formed as -dS = P * (delta - dP) (V negated)
 //   dV^T += dO^T P      (A = dO^T by transposed LDS reads, B = P)
-//   dK^T += Q^T dS      (A = Q^T by transposed LDS reads, B = dS)
+//   dK^T += Q^T dS      (A = Q^T by transposed LDS reads, B = -dS)
 template <class E, int D, bool CAUSAL, bool MASKED, int KB = 4>
 __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdArgs a) {
   static_assert(KB == 4 || KB == 2, "four or two key blocks");
