@@ -26,6 +26,8 @@
 // max grows by more than 2^8 (in exp2 units) over the max it was last scaled
 // with.  O = acc / l and L = m + log2 l do not depend on which m is used, and
 // with the slack every p = exp2(s - m) stays <= 256, far from overflow.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -101,13 +103,22 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
 
   const TileLoader<D> ldk(w, lane, ks), ldv(w, lane, vs);
   const uint32_t smem_a = lds_addr(smem);  // (byte addresses: no pointer conversion per load)
-  auto issue = [&](int ti) {
-    const int j = tile(ti);
-    const uint32_t buf = smem_a + (uint32_t)(ti & 1) * (BUF * 2);
-    ldk.template load_at<BN>(buf, kp, j * BN, Lk, w);
-    ldv.template load_at<BN>(buf + BN * P * 2, vp, j * BN, Lk, w);
+  // K (and V) of tile ti into buffer ti & 1
+  auto issue_k = [&](int ti) {
+    ldk.template load_at<BN>(smem_a + (uint32_t)(ti & 1) * (BUF * 2), kp, tile(ti) * BN, Lk, w);
   };
-  if (nt > 0) issue(0);
+  auto issue_v = [&](int ti) {
+    ldv.template load_at<BN>(smem_a + (uint32_t)(ti & 1) * (BUF * 2) + BN * P * 2, vp, tile(ti) * BN, Lk, w);
+  };
+  // One wavefront per SIMD (head dim 256) without a block mask: K runs one
+  // tile ahead of V, so that the scores of tile ti + 1 go to the matrix cores
+  // while tile ti is exponentiated (the second loop below).
+  constexpr bool LEAD = D > 128 && !MASKED;
+  if (nt > 0) {
+    issue_k(0);
+    issue_v(0);
+  }
+  if (LEAD && nt > 1) issue_k(1);
 
   // ---- Q^T operand (B): lane holds query qrow, head-dim slots 16*kd + 8*lg + s
   bf16x8 qf[NKD];
@@ -125,11 +136,15 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = zero16();
 
+  if constexpr (!LEAD) {
   wait_vmem();
   __syncthreads();
   for (int ti = 0; ti < nt; ++ti) {
     const int j = tile(ti);
-    if (ti + 1 < nt) issue(ti + 1);
+    if (ti + 1 < nt) {
+      issue_k(ti + 1);
+      issue_v(ti + 1);
+    }
     const bf16_t* Ks = smem;           // + (ti & 1) * BUF through the reader's offsets
     const bf16_t* Vs = smem + BN * P;
     bool skip = false;  // this wavefront's rows do not see tile j
@@ -210,6 +225,131 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void fa_fwd_kernel(FwdArgs
     rd.flip(BUF);
     wait_vmem();
     __syncthreads();
+  }
+  } else {
+    // Iteration ti holds S(ti) (computed in the iteration before) and issues
+    // K(ti + 2) and V(ti + 1); it forms S(ti + 1) = K(ti + 1) Q^T with the
+    // softmax of S(ti) laid between those products (they do not depend on
+    // each other), then O += P(ti) V(ti).  K(ti + 1) and V(ti) are resident:
+    // the key-read offsets run one buffer ahead of the transposed ones.
+    const bf16_t* Ks = smem;
+    const bf16_t* Vs = smem + BN * P;
+    auto scores = [&](f32x16 (&t)[NNB]) {
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb) {
+        t[nb] = zero16();
+#pragma unroll
+        for (int kd = 0; kd < NKD; ++kd) t[nb] = E::mma(rd.row16(Ks, nb * 32, kd), qf[kd], t[nb]);
+      }
+    };
+    // hide keys past the diagonal or past Lk (tile j; every tile from
+    // n_full on), without a branch
+    auto mask_tile = [&](f32x16 (&t)[NNB], int j) {
+      const int last = CAUSAL ? min(qrow + off, Lk - 1) : Lk - 1;
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb) {
+        const int thr = last - (j * BN + nb * 32 + 4 * lg);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t[nb][i] = (crow(i, 0) <= thr) ? t[nb][i] : -INFINITY;
+      }
+    };
+    // running max of S (exp2 units): a candidate for m_run
+    auto tile_max = [&](const f32x16 (&t)[NNB]) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, t[nb][i]);
+      return max_xor32(mx) * c2;
+    };
+    f32x16 sc[NNB];
+    wait_vmem();
+    __syncthreads();
+    if (nt > 0) {
+      scores(sc);
+      if (n_full == 0) mask_tile(sc, 0);
+      m_run = tile_max(sc);  // (the accumulator is still zero)
+    }
+    rd.flip_ra(BUF);
+    __syncthreads();  // K(0) read by every wavefront before K(2) goes to its buffer
+    // Iteration ti, one basic block up to the rare rescale: S(ti + 1) on the
+    // matrix cores with the exponentials of S(ti) between the products, then
+    // O += P(ti) V(ti) with the mask and running max of S(ti + 1) between
+    // those.  If that max grew past the slack, the accumulator is rescaled
+    // after the products (it then holds tiles up to ti, all at the old max).
+    // The exponentials need only m_run from the iteration before; the loop is
+    // split where the next tile starts to need the mask, so that no branch
+    // sits between them and the products they hide under.
+    auto step = [&](int ti, auto has_next, auto mask_next) {
+      constexpr bool NXT = decltype(has_next)::value;
+      constexpr bool MSK = decltype(mask_next)::value;
+      if constexpr (NXT) {
+        if (ti + 2 < nt) issue_k(ti + 2);
+        issue_v(ti + 1);
+      }
+      f32x16 sn[NNB];
+      if constexpr (NXT) scores(sn);
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float rs = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(fmaf(sc[nb][i], c2, -m_use));
+          sc[nb][i] = p;
+          rs += p;
+        }
+      bf16x8 pf[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) pf[ks] = E::pack8(sc[ks / 2], ks % 2);
+      l_run += rs;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) acc[db] = E::mma(rd.trA(Vs, 16 * ks, db), pf[ks], acc[db]);
+      if constexpr (NXT) {
+        if constexpr (MSK) mask_tile(sn, ti + 1);
+        const float m_cand = tile_max(sn);
+        // score products: K reads kLookahead ahead, exponentials between
+        __builtin_amdgcn_sched_group_barrier(0x100, kLookahead, 0);
+#pragma unroll
+        for (int t = 0; t < NNB * NKD - kLookahead; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kLookahead, 0);
+        // P V products: V reads four products ahead, mask and max between
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int t = 0; t < NDB * NKS - 4; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        const bool resc = __any(m_cand > m_run + kSlack);
+        if (resc) {
+          __asm__ volatile("");  // a real branch: the rescale is rare
+          const float m_new = fmaxf(m_run, m_cand);
+          const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) scale_agpr(acc[db], alpha);
+          m_run = m_new;
+        }
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb) sc[nb] = sn[nb];
+        rd.flip(BUF);
+        wait_vmem();
+        __syncthreads();
+      }
+    };
+    // (without a block mask tile(ti) = ti: tile ti + 1 needs the mask from n_full on)
+    int ti = 0;
+    for (; ti + 1 < min(nt, n_full); ++ti) step(ti, std::true_type{}, std::false_type{});
+    for (; ti + 1 < nt; ++ti) step(ti, std::true_type{}, std::true_type{});
+    if (nt > 0) step(nt - 1, std::false_type{}, std::false_type{});
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; a row that saw no
