@@ -18,6 +18,11 @@ seeded generator; ``window_block_mask`` keeps, for every query block, the
 key blocks that overlap a band of ``window`` keys ending at the block's last
 query row (bottom-right aligned, as the causal diagonal), plus the first
 ``sink_blocks`` key blocks.
+
+``ramp_bits`` builds inputs whose scores rise steadily along the keys
+(a shared direction u in Q and K, K's component along it growing with the
+key index), so that a row's running maximum keeps growing from key block to
+key block.
 """
 from __future__ import annotations
 
@@ -39,6 +44,7 @@ __all__ = [
     "random_block_mask",
     "window_block_mask",
     "block_mask_of",
+    "ramp_bits",
 ]
 
 MASK_BLOCK = 64
@@ -86,6 +92,31 @@ def normal_bf16_bits(shape, seed: int, sigma: float = 1.0) -> np.ndarray:
     if sigma != 1.0:
         x = x * np.float32(sigma)
     return bf16_bits_from_f32(x)
+
+
+def ramp_bits(B: int, Hq: int, Hkv: int, Lq: int, Lk: int, D: int, seed: int, rise: float,
+              scale: float, dtype: str = "bf16") -> dict:
+    """Q, K, V, dO bits whose scores q_i . k_j * scale are about rise * j / Lk
+    plus noise of standard deviation about 0.25.
+
+    u is the unit vector (1, ..., 1) / sqrt(D).  q_i = 4 u + 0.5 n with n a
+    normal draw made orthogonal to u; k_j = b_j u + 0.5 n' likewise, with
+    b_j = rise * (j / Lk) / (4 * scale).  V and dO are plain normal draws.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    u = np.full(D, 1.0 / math.sqrt(D), dtype=np.float64)
+
+    def noise(shape):
+        n = rng.standard_normal(size=shape)
+        return n - (n @ u)[..., None] * u
+
+    q = 4.0 * u + 0.5 * noise((B, Hq, Lq, D))
+    b = rise * (np.arange(Lk) / Lk) / (4.0 * scale)
+    k = b[None, None, :, None] * u + 0.5 * noise((B, Hkv, Lk, D))
+    v = rng.standard_normal(size=(B, Hkv, Lk, D))
+    do = rng.standard_normal(size=(B, Hq, Lq, D))
+    conv = bf16_bits_from_f32 if dtype == "bf16" else f16_bits_from_f32
+    return {n: conv(x.astype(np.float32)) for n, x in (("q", q), ("k", k), ("v", v), ("do", do))}
 
 
 @dataclass(frozen=True)

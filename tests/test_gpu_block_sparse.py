@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import oracle
-from fa_synth import (WORKLOADS, block_mask_of, make_inputs, normal_bf16_bits, random_block_mask,
+from fa_synth import (WORKLOADS, block_mask_of, make_inputs, normal_bf16_bits, ramp_bits, random_block_mask,
                       window_block_mask)
 from parity_util import check_masked, oracle_full, run_library, to_f64, to_gpu
 
@@ -40,17 +40,20 @@ def mask_gpu(m):
     return torch.from_numpy(np.ascontiguousarray(m, dtype=np.uint8)).cuda()
 
 
-def run_masked_case(B, Hq, Hkv, Lq, Lk, D, causal, mask, seed, label=""):
+def run_masked_case(B, Hq, Hkv, Lq, Lk, D, causal, mask, seed, label="", ramp=None,
+                    names=("o", "lse", "dq", "dk", "dv")):
     label = f"{label} B{B} Hq{Hq} Hkv{Hkv} Lq{Lq} Lk{Lk} D{D} causal={causal} seed={seed}"
     print(f"[case] {label} kept={int(mask.sum())}/{mask.size}", flush=True)
-    bits = make_bits(B, Hq, Hkv, Lq, Lk, D, seed)
     scale = float(np.float32(1.0 / math.sqrt(D)))
+    # ramp: scores rising by that much along each row (ramp_bits)
+    bits = (make_bits(B, Hq, Hkv, Lq, Lk, D, seed) if ramp is None
+            else ramp_bits(B, Hq, Hkv, Lq, Lk, D, seed, rise=ramp, scale=scale))
     g = {n: to_gpu(b) for n, b in bits.items()}
     out = run_library(g["q"], g["k"], g["v"], g["do"], scale, causal, block_mask=mask_gpu(mask))
     ref = oracle_full(bits, scale, causal, block_mask=mask)
     vis = oracle.visible_mask(Lq, Lk, causal, block_mask=mask)
     rows_empty, keys_empty = ~vis.any(axis=1), ~vis.any(axis=0)
-    for n in ("o", "lse", "dq", "dk", "dv"):
+    for n in names:
         check_masked(n, to_f64(out[n]), ref[n], label, keys_empty if n in ("dk", "dv") else rows_empty)
     return out, ref
 
@@ -83,6 +86,17 @@ def test_all_ones_mask_is_bitwise_dense(D, causal, Lq, Lk):
 def test_random_mask(D, causal, Lq, Lk):
     mask = random_block_mask(Lq, Lk, 0.5, seed=8200 + D + Lq)
     run_masked_case(1, 4, 2, Lq, Lk, D, causal, mask, seed=8300 + D + Lk, label="random")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("causal", [True, False])
+def test_random_mask_rising_scores(D, causal):
+    # the masked kernels' accumulator rescale, run several times per row
+    # (scores rising by 48 along each row; see test_gpu_parity)
+    mask = random_block_mask(600, 600, 0.7, seed=8400 + D)
+    # (dQ is not compared on these inputs: test_gpu_parity.RAMP_CHECKED)
+    run_masked_case(1, 4, 2, 600, 600, D, causal, mask, seed=8500 + D + int(causal), label="ramp",
+                    ramp=48.0, names=("o", "lse", "dk", "dv"))
 
 
 @pytest.mark.parametrize("density", [0.2, 0.8])

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from fa_synth import normal_bits
+from fa_synth import normal_bits, ramp_bits
 from parity_util import check, oracle_full, to_f64, to_gpu
 
 pytestmark = pytest.mark.gpu
@@ -36,18 +36,23 @@ def run_short(g, scale, causal, workspace=None):
     return {"o": o, "lse": lse, "delta": delta, "dq": dq, "dk": dk, "dv": dv}
 
 
-def short_case(B, Hq, Hkv, Lq, Lk, D, causal, seed, dtype="bf16"):
+def short_case(B, Hq, Hkv, Lq, Lk, D, causal, seed, dtype="bf16", ramp=None,
+               names=("o", "lse", "dq", "dk", "dv")):
     label = f"short {dtype} B{B} Hq{Hq} Hkv{Hkv} Lq{Lq} Lk{Lk} D{D} causal={causal}"
+    if ramp is not None:
+        label += f" ramp={ramp}"
     print(f"[case] {label}", flush=True)
-    bits = make_bits(B, Hq, Hkv, Lq, Lk, D, seed, dtype)
     scale = float(np.float32(1.0 / math.sqrt(D)))
+    # ramp: scores rising by that much along each row (ramp_bits)
+    bits = (make_bits(B, Hq, Hkv, Lq, Lk, D, seed, dtype) if ramp is None
+            else ramp_bits(B, Hq, Hkv, Lq, Lk, D, seed, rise=ramp, scale=scale, dtype=dtype))
     g = {n: to_gpu(b, dtype) for n, b in bits.items()}
     out = run_short(g, scale, causal)
     ref = oracle_full(bits, scale, causal, dtype=dtype)
     # Lk = 1: every row sees one key, P = 1 and dS = dP - delta is exactly 0;
     # the GPU's two fp32 dot products dO.V and dO.O differ by rounding only
     atol = {"dq": 1e-4, "dk": 1e-4} if Lk == 1 else {}
-    for n in ("o", "lse", "dq", "dk", "dv"):
+    for n in names:
         check(n, to_f64(out[n]), ref[n], label, atol=atol.get(n, 0.0))
     return g, out
 
@@ -57,6 +62,17 @@ def short_case(B, Hq, Hkv, Lq, Lk, D, causal, seed, dtype="bf16"):
 @pytest.mark.parametrize("causal", [True, False])
 def test_short_parity(D, Lq, Lk, causal):
     short_case(1, 8, 2, Lq, Lk, D, causal, seed=10000 + D + 10 * Lq + Lk)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("causal", [True, False])
+def test_short_rising_scores(D, causal):
+    # scores rising by 120 along 4100 keys: a row's running max passes the
+    # slack every few key tiles, in the chunk kernels and in the merge
+    # (chunks far apart along the row differ by many orders of magnitude)
+    # (dQ is not compared on these inputs: test_gpu_parity.RAMP_CHECKED)
+    short_case(1, 8, 2, 5, 4100, D, causal, seed=10300 + D + int(causal), ramp=120.0,
+               names=("o", "lse", "dk", "dv"))
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 1), (32, 4)])
