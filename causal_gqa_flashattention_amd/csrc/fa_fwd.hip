@@ -20,7 +20,10 @@
 //   transposed LDS read.
 // K and V tiles are double buffered in LDS and filled by direct global->LDS
 // loads issued one tile ahead.  Tiles that need no mask (fully below the
-// diagonal and inside Lk) run a mask-free body.
+// diagonal and inside Lk) run a mask-free body.  At head dim 256 (one
+// wavefront per SIMD, nothing to hide one wavefront's softmax behind) and
+// without a block mask, K runs a tile ahead of V instead: the scores of the
+// next tile go to the matrix cores between the current tile's exponentials.
 //
 // Running max with slack: the accumulator is rescaled only when some row's
 // max grows by more than 2^8 (in exp2 units) over the max it was last scaled
