@@ -512,13 +512,16 @@ def gemm_canary(dev, n=4096, reps=10):
 SWEEP = ("dense4k_d64", "dense4k_d96", "d256_8192", "d256_4064x4096", "d256_8200", "long23k")
 
 
-def workload_sweep(dev, names=SWEEP, steps=20, warmup=5):
+def workload_sweep(dev, names=SWEEP, min_steps=20, warm_s=0.15, timed_s=0.25):
     """For each workload: fa_fwd, fa_bwd_delta, fa_bwd_dq and fa_bwd_dkv on
     resident inputs (the same seeded recipe as the headline), timed with HIP
-    events on the launch stream; medians over `steps` steps.  Model TFLOP/s
-    use the pages' FLOP model (the head-dim-256 shapes are a forward
-    workload: their forward figure is the one to read; the backward there is
-    timed as well)."""
+    events on the launch stream; medians over the timed steps.  Each
+    workload first runs for at least `warm_s` seconds (the clock takes tens
+    of milliseconds to settle after the load changes: 25 steps of a 0.7 ms
+    workload measured 8% slow), then times at least `min_steps` steps and
+    `timed_s` seconds.  Model TFLOP/s use the pages' FLOP model (the
+    head-dim-256 shapes are a forward workload: their forward figure is the
+    one to read; the backward there is timed as well)."""
     import numpy as np
     import torch
 
@@ -569,8 +572,16 @@ def workload_sweep(dev, names=SWEEP, steps=20, warmup=5):
             if ev is not None:
                 ev[4].record(stream)
 
-        for _ in range(warmup):
+        t0 = time.perf_counter()
+        warmup = 0
+        while True:
             step()
+            warmup += 1
+            if warmup % 4 == 0:
+                torch.cuda.synchronize()
+                if time.perf_counter() - t0 >= warm_s:
+                    break
+        steps = max(min_steps, int(math.ceil(timed_s / ((time.perf_counter() - t0) / warmup))))
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
         for e in evs:
             step(e)
@@ -593,6 +604,8 @@ def workload_sweep(dev, names=SWEEP, steps=20, warmup=5):
             "peak_bytes": int(torch.cuda.max_memory_allocated()),
             "resident_bytes": int(resident),
             "dkv_call": "fa_bwd_dkv" if ws is None else f"fa_bwd_ws ({ws_bytes} bytes of workspace)",
+            "warmup_steps": warmup,
+            "timed_steps": steps,
         }
         del g, q, k, v, do, o, lse, delta, dq, dk, dv, ws
         torch.cuda.empty_cache()
