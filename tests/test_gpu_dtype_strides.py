@@ -63,6 +63,24 @@ def test_f16_parity(D, causal, Lq, Lk):
         check(n, to_f64(out[n]), ref[n], label)
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_f16_rising_scores(D):
+    # the accumulator rescale in half precision: scores rising by 48 along
+    # each row (fa_synth.ramp_bits; dQ is not compared on these inputs, see
+    # test_gpu_parity.RAMP_CHECKED)
+    from fa_synth import ramp_bits
+    L = 600
+    label = f"f16 ramp D{D} L{L} causal"
+    print(f"[case] {label}", flush=True)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    bits = ramp_bits(1, 4, 2, L, L, D, 9500 + D, rise=48.0, scale=scale, dtype="f16")
+    g = {n: to_gpu(b, "f16") for n, b in bits.items()}
+    out = run_ex(g["q"], g["k"], g["v"], g["do"], scale, True)
+    ref = oracle_full(bits, scale, True, dtype="f16")
+    for n in ("o", "lse", "dk", "dv"):
+        check(n, to_f64(out[n]), ref[n], label)
+
+
 def test_f16_gqa_batches_and_mask():
     import oracle
     B, Hq, Hkv, L, D = 2, 8, 2, 520, 128
