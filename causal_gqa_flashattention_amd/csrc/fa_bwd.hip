@@ -496,23 +496,34 @@ __global__ __launch_bounds__(1024) void fa_dkv_plan_kernel(BwdArgs a) {
 // also in registers); query tiles of Q and dO stream through LDS (double
 // buffered, direct loads one tile ahead) with their LSE and delta, for every
 // query head of the group in turn.
+// H1 (head dims 96 and 128 without a causal mask or a split): KB = 4
+// wavefronts of 32 keys each over 32-row query tiles, one row half, so that
+// two 4-wavefront workgroups share a CU with independent barriers, as at
+// head dim 64.  (With a causal mask the key tiles' work is unequal and two
+// heavy ones would share a CU; one workgroup per CU in heaviest-first order
+// balances them.)  The K tile is read into registers through the query-tile
+// buffers before the first query tile arrives: the LDS of two workgroups
+// holds no more.
 // Per query tile and wavefront (32 rows x 32 keys):
 //   S  = Q K^T          (A = Q rows from LDS, B = K rows in registers)
 //   dP = dO V^T         (A = dO rows, B = V rows, from LDS)
 //   dS = P * (dP - delta), formed as -dS = P * (delta - dP) (V negated)
 //   dV^T += dO^T P      (A = dO^T by transposed LDS reads, B = P)
 //   dK^T += Q^T dS      (A = Q^T by transposed LDS reads, B = -dS)
-template <class E, int D, bool CAUSAL, bool MASKED, int KB = 4>
-__global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdArgs a) {
+template <class E, int D, bool CAUSAL, bool MASKED, int KB = 4, bool H1 = false>
+__global__ __launch_bounds__(H1 ? 64 * KB : 128 * KB, KB == 4 && !H1 ? 1 : 2) void fa_dkv_kernel(BwdArgs a) {
   static_assert(KB == 4 || KB == 2, "four or two key blocks");
-  constexpr int NW = 2 * KB;  // wavefronts
+  static_assert(!H1 || (KB == 4 && D >= 96), "one row half: 128-key workgroups");
+  constexpr int NW = H1 ? KB : 2 * KB;  // wavefronts
   constexpr int BN = 32 * KB;  // keys per workgroup
   // query rows per tile: 64 (two halves of 32), or 128 at head dim 64 with
   // eight wavefronts, where a 64-row tile is too little matrix work per
   // barrier; each wave then takes two 32-row units per tile (under a block
   // mask, one per 64-row mask block)
-  constexpr int BM = D == 64 && KB == 4 ? 128 : 64;
-  static_assert(BM % kMaskBlock == 0, "query tiles are whole mask blocks");
+  constexpr int BM = H1 ? 32 : D == 64 && KB == 4 ? 128 : 64;
+  static_assert(BM % kMaskBlock == 0 || kMaskBlock % BM == 0, "query tiles tile the mask blocks");
+  constexpr int NU = BM < 64 ? 1 : BM / 64;  // 32-row units of this wave per tile (64 rows each apart)
+  constexpr int SR = BM < 64 ? 64 : BM;      // rows of a stat buffer (64-row loads)
   constexpr int P = Tile<D>::P;
   constexpr int NKD = D / 16;
   constexpr int NDB = D / 32;
@@ -521,14 +532,15 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
   // then the K and V tiles of this workgroup
   constexpr int BUF = 2 * BM * P;
   static_assert((BUF & (BUF - 1)) == 0, "buffer size must be a power of two");
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF + 2 * BN * P];
-  bf16_t* const sK = smem + 2 * BUF;
-  bf16_t* const sV = sK + BN * P;
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buf][lse / delta][row]
+  static_assert(!H1 || 2 * BUF == BN * P, "H1: the K tile fills the two query-tile buffers");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * BUF + (H1 ? 1 : 2) * BN * P];
+  bf16_t* const sK = H1 ? smem : smem + 2 * BUF;
+  bf16_t* const sV = smem + 2 * BUF + (H1 ? 0 : BN * P);
+  __shared__ __attribute__((aligned(16))) float stat[2][2][SR];  // [buf][lse / delta][row]
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kb = w & (KB - 1), qhalf = w / KB;
+  const int kb = w & (KB - 1), qhalf = H1 ? 0 : w / KB;
   const int G = a.G;
   // key tiles (x chunks) x (batch, key/value head); key tile 0 sees the most
   // queries: heaviest first
@@ -560,8 +572,8 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
     if (w == 0) {
       const int cnt = build_list(qlist, nq, lane, [&](int i) { return nqt - 1 - i; }, [&](int qtl) {
         bool any = false;
-        const int rb_end = min((qtl + 1) * (BM / kMaskBlock), (Lq + kMaskBlock - 1) / kMaskBlock);
-        for (int rb = qtl * (BM / kMaskBlock); rb < rb_end; ++rb)
+        const int rb_end = min(((qtl + 1) * BM - 1) / kMaskBlock + 1, (Lq + kMaskBlock - 1) / kMaskBlock);
+        for (int rb = qtl * BM / kMaskBlock; rb < rb_end; ++rb)
           for (int kbk = kb0; kbk <= kb1; ++kbk) any |= a.mask[rb * a.nkb + kbk] != 0;
         return any;
       });
@@ -593,7 +605,7 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
   // group, list entry nx_i, the head's Q / dO / LSE / delta bases), advanced
   // by additions: no division by the group size and no 64-bit products per
   // tile, and LDS destinations as plain byte addresses.
-  float lse_next[BM / 64];
+  float lse_next[NU];
   const uint32_t smem_a = lds_addr(smem), stat_a = lds_addr(&stat[0][0][0]);
   const int64_t srow0 = (int64_t)(b * a.Hq + hk * G) * Lq;  // LSE / delta row of the group's first head
   const bf16_t* nx_q = a.q.head(b, hk * G);
@@ -616,12 +628,13 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
       ld.template load_at<BM>(qt_a, nx_q, qbase, Lq, wl);
       ldo.template load_at<BM>(dt_a, nx_o, qbase, Lq, wl);
     }
-    // 64 rows per load; a half past Lq repeats row Lq - 1
+    // 64 rows per load; a half past Lq repeats row Lq - 1 (with 32-row
+    // tiles the second 32 rows are loaded and not read)
 #pragma unroll
-    for (int hr = 0; hr < BM / 64; ++hr) {
+    for (int hr = 0; hr < NU; ++hr) {
       if (w == 0) lse_next[hr] = nx_l[min(qbase + 64 * hr + lane, Lq - 1)];
       if (w == WDELTA)
-        load_row_stat_at(stat_a + (uint32_t)(((n & 1) * 2 + 1) * BM + 64 * hr) * 4u, nx_d, min(qbase + 64 * hr, Lq - 1),
+        load_row_stat_at(stat_a + (uint32_t)(((n & 1) * 2 + 1) * SR + 64 * hr) * 4u, nx_d, min(qbase + 64 * hr, Lq - 1),
                          Lq, lane);
     }
     // advance: heads innermost, then the list
@@ -642,7 +655,7 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
   auto publish_lse = [&](int n) {
     if (w == 0) {
 #pragma unroll
-      for (int hr = 0; hr < BM / 64; ++hr) stat[n & 1][0][64 * hr + lane] = lse_next[hr] * -kLog2e;
+      for (int hr = 0; hr < NU; ++hr) stat[n & 1][0][64 * hr + lane] = lse_next[hr] * -kLog2e;
     }
   };
   // K and V of this key tile, once (rows past Lk repeat the last key)
@@ -654,7 +667,7 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
     TileLoader<D>(wl, lane, a.v.sl).template load<BN>(sV, a.v.head(b, hk), k0, Lk, wl);
   }
   int q0_cur = 0;
-  if (niter > 0) {
+  if (!H1 && niter > 0) {
     issue(0);
     publish_lse(0);
     q0_cur = q0_nx;
@@ -699,6 +712,18 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
   bf16x8 kf[NKD];
 #pragma unroll
   for (int kd = 0; kd < NKD; ++kd) kf[kd] = rk.row16(sK, 32 * kb, kd);
+  if constexpr (H1) {
+    // the K tile's LDS is the query-tile buffers: every wave has read its
+    // fragments before the first query tile goes there
+    __syncthreads();
+    if (niter > 0) {
+      issue(0);
+      publish_lse(0);
+      q0_cur = q0_nx;
+    }
+    wait_vmem();
+    __syncthreads();
+  }
   for (int n = 0; n < niter; ++n) {
     const int buf = n & 1;
     const int q0 = q0_cur;
@@ -707,7 +732,7 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
     const bf16_t* Ds = smem + BM * P;
     {
 #pragma unroll
-    for (int u = 0; u < BM / 64; ++u) {
+    for (int u = 0; u < NU; ++u) {
     const int r0 = 32 * qhalf + 64 * u;  // this wave's rows within the tile
     const int rr = FOLD_ROWS ? 64 * u : r0;  // the same as the reads take it
     // under a block mask, a unit whose 64-row block this wavefront's keys do
@@ -780,9 +805,9 @@ __global__ __launch_bounds__(128 * KB, KB == 4 ? 1 : 2) void fa_dkv_kernel(BwdAr
   // 0..KB-1 through LDS (the tile buffers are free now), lane-contiguous per
   // register
   float* red = reinterpret_cast<float*>(smem);
-  static_assert((2 * BUF + 2 * BN * P) * 2 >= KB * NDB * 16 * 64 * 4, "reduction buffer too small");
+  static_assert(H1 || (2 * BUF + 2 * BN * P) * 2 >= KB * NDB * 16 * 64 * 4, "reduction buffer too small");
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < (H1 ? 0 : 2); ++pass) {
     f32x16* acc = pass == 0 ? dk : dv;
     if (w >= KB) {
 #pragma unroll
@@ -1367,6 +1392,9 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
   const bool k32 = D > 128 && !split && (int64_t)a.B * a.Hkv * ((a.Lk + 63) / 64) < 512;
   // head dim 64 without a split: 64-key workgroups of four wavefronts, two per CU
   const bool kb2 = D == 64 && !split;
+  // head dims 96 and 128 without a causal mask or a split: four wavefronts of
+  // the same 128 keys over 32-row query tiles, two workgroups per CU
+  const bool h1 = (D == 96 || D == 128) && !split && !causal;
   const int bnk = D > 128 ? (k32 ? 32 : 64) : kb2 ? 64 : 128;
   a.nkt = (a.Lk + bnk - 1) / bnk;
   // the dK accumulators of the kernels that write partials hold -dK / scale
@@ -1375,7 +1403,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
   const bool masked = a.mask != nullptr;
   // dynamic LDS under a block mask: each workgroup's tile list and its count
   const size_t dq_list = masked ? ((size_t)(a.Lk + BN_Q - 1) / BN_Q + 1) * sizeof(int) : 0;
-  const size_t dkv_list = masked ? ((size_t)(a.Lq + 63) / 64 + 1) * sizeof(int) : 0;
+  const size_t dkv_list = masked ? ((size_t)(a.Lq + (h1 ? 31 : 63)) / (h1 ? 32 : 64) + 1) * sizeof(int) : 0;
   const int nh = a.B * a.Hkv;
   const int ndq = (which & 1) ? a.B * a.Hq * a.nqt : 0;
   // dK/dV workgroups: key tiles (x chunks without a mask; extra chunks first
@@ -1383,7 +1411,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
   const int ndkv = !(which & 2) ? 0 : !split ? nh * a.nkt : masked ? a.nextra + nh * a.nkt : nh * a.nkt * a.nsplit;
   auto dq = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(ndq), dim3(256), dq_list, stream, a); };
   auto dkv = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(ndkv), dim3(D > 128 || kb2 ? 256 : 512), dkv_list, stream, a);
+    hipLaunchKernelGGL(kern, dim3(ndkv), dim3(D > 128 || kb2 || h1 ? 256 : 512), dkv_list, stream, a);
   };
   if (split && masked && ndkv > 0) {
     constexpr int BMK = D == 64 ? 128 : 64;  // the dK/dV kernel's query tile
@@ -1422,7 +1450,10 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, bool causal, int which, hipStr
         if (kb2) go(std::integral_constant<int, 2>{});
         else go(std::integral_constant<int, 4>{});
       } else {
-        go(std::integral_constant<int, 4>{});
+        if (h1)
+          masked ? dkv(fa_dkv_kernel<E, D, false, true, 4, true>) : dkv(fa_dkv_kernel<E, D, false, false, 4, true>);
+        else
+          go(std::integral_constant<int, 4>{});
       }
     }
     if (split)
